@@ -1,0 +1,153 @@
+/*
+ * nvfp4.h -- C ABI of the MI355X (gfx950) NVFP4 W4A4 linear layer.
+ *
+ * The layer, as the pages describe it: activations and weights are NVFP4
+ * tensors -- 4-bit E2M1 element codes, one E4M3 scale per 16-element block set
+ * from the block maximum divided by 6, and one FP32 scale per tensor
+ * (Summary page "Summary of 'Why Gated DeltaNet Survives 4-Bit Quantization'",
+ * Background, item 1).  Activations are quantized on the fly at every call
+ * ("W4A4", paper abstract).  Weights come from modules calibrated one by one,
+ * each with its own FP32 scale; when several modules are fused into one GEMM,
+ * each module's output columns must be rescaled with that module's own scale
+ * -- the pages' repair of the global-scale mismatch (paper abstract; Glonce
+ * article, "Who it affects" and "Risks and caveats"; aiany page,
+ * "Mechanistic notes").  The segment table below is that per-module scale map.
+ *
+ * Conventions for every call:
+ *  - Buffer pointers are DEVICE pointers unless marked "host".  The caller
+ *    allocates and owns every buffer; the library never allocates, frees or
+ *    retains device memory and keeps no mutable global state.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *    Work is enqueued on it and the call returns without synchronizing;
+ *    device-side faults surface at the caller's next synchronization.
+ *  - Arguments are validated on the host before anything is launched; a
+ *    non-OK status means nothing was enqueued.  The library never prints and
+ *    never aborts.  NVFP4_EHIP reports a failed launch (hipGetLastError).
+ *  - Element codes are packed two per byte, the even k in the low nibble:
+ *    byte j of a row = code[2j] | code[2j+1] << 4; code = sign << 3 | mag,
+ *    mag 0..7 = 0, 0.5, 1, 1.5, 2, 3, 4, 6.  Scales are E4M3FN bytes
+ *    (0x00..0x7E).  Blocks of 16 run along K.
+ *  - Every pointer must be 16-byte aligned; K must be a multiple of 16.
+ */
+#ifndef NVFP4_W4A4_H
+#define NVFP4_W4A4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define NVFP4_ABI_VERSION 1
+#define NVFP4_MAX_SEGMENTS 16
+
+typedef enum {
+  NVFP4_OK = 0,
+  NVFP4_EINVAL = 1,     /* null pointer, negative size, overlapping input/output buffers */
+  NVFP4_ESHAPE = 2,     /* K % 16 != 0, leading dimension too small, size overflow */
+  NVFP4_EALIGN = 3,     /* pointer not 16-byte aligned, or bf16 leading dimension not a multiple of 8 */
+  NVFP4_ESEGMENTS = 4,  /* segments do not tile [0, N) in order, or nseg not in [1, 16] */
+  NVFP4_EWORKSPACE = 5, /* workspace missing or smaller than the *_workspace_bytes query */
+  NVFP4_EHIP = 6        /* a kernel launch failed */
+} nvfp4_status;
+
+/* One fused module: output columns [n_begin, n_end) of the GEMM (rows of the weight). */
+typedef struct {
+  int32_t n_begin;
+  int32_t n_end;
+} nvfp4_segment;
+
+/* Version of this ABI (NVFP4_ABI_VERSION).  Needs no GPU. */
+int nvfp4_abi_version(void);
+
+/* Static text for a status code.  Needs no GPU. */
+const char* nvfp4_status_str(int status);
+
+/* ---------------------------------------------------------------------------
+ * Activation quantization (the "A4" of W4A4).
+ *
+ * Encodes bf16 activations x[M][K] (row stride ldx elements) to NVFP4 in the
+ * canonical layout: codes[M][K/2] and scales[M][K/16], both row-major and
+ * dense.  The per-tensor scale maps the tensor's absolute maximum amax onto
+ * 6 * 448 = 2688 (the largest E2M1 magnitude times the largest E4M3 scale):
+ *   g_enc = fl(2688 / amax), g_dec = fl(amax / 2688);
+ *   per block: t = fl(bmax / 6), s = fl(t * g_enc), scale = E4M3(s)
+ *              (round to nearest even, saturate at 448; t == 0 gives 0);
+ *   per element: y = fl(|x| * fl(g_enc / s_dec)), mag = E2M1(y)
+ *              (round to nearest even, saturate at 6; x == 0 or s_dec == 0
+ *              gives 0); the sign bit is copied from x, -0.0 included.
+ * amax == 0 gives g_dec = 0, scales 0 and sign-only codes.  Results are
+ * bit-exact to that definition (binary32, no fused multiply-add).
+ *
+ *   amax_in   NULL: dynamic mode, amax = max|x| over the whole tensor.
+ *             Otherwise a device pointer to one finite float >= 0 holding a
+ *             calibrated amax (static mode); values of |x| above it saturate.
+ *   g_dec_out device pointer to one float: receives g_dec.
+ *   workspace device scratch of nvfp4_quantize_act_workspace_bytes(M, K)
+ *             bytes (may be NULL when that is 0); contents need no setup.
+ * Non-finite x are outside the contract (no fault; codes unspecified).
+ * ------------------------------------------------------------------------- */
+size_t nvfp4_quantize_act_workspace_bytes(int64_t M, int64_t K);
+
+nvfp4_status nvfp4_quantize_act(const void* x_bf16, int64_t M, int64_t K, int64_t ldx,
+                                const float* amax_in,
+                                uint8_t* codes, uint8_t* scales, float* g_dec_out,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Weight packing (offline, post-training; the aiany page, "Who it's for",
+ * describes the recipe as calibration-only post-training quantization).
+ *
+ * Encodes fp32 weights w[N][K] (row stride ldw elements) with the same rule
+ * as the activations, module by module: each segment's rows get their own
+ * amax and g_dec (w_g_dec[i], device, nseg floats).  Output is the tiled
+ * weight layout the GEMM reads, with N padded to a multiple of 16 and K to a
+ * multiple of 128 with zero codes and zero scales (sizes from
+ * nvfp4_packed_weight_bytes).  The layout: chunks of 16 rows x 128 k, strip
+ * major (chunk = (n / 16) * (Kp / 128) + k / 128); each code chunk is
+ * 16 x 64 bytes and each scale chunk 16 x 8 bytes, both row-major in the
+ * canonical encoding.  `segs` is a HOST array.
+ * ------------------------------------------------------------------------- */
+nvfp4_status nvfp4_packed_weight_bytes(int64_t N, int64_t K, size_t* codes_bytes, size_t* scales_bytes);
+
+size_t nvfp4_pack_weight_workspace_bytes(int64_t N, int64_t K, int32_t nseg);
+
+nvfp4_status nvfp4_pack_weight(const float* w, int64_t N, int64_t K, int64_t ldw,
+                               const nvfp4_segment* segs, int32_t nseg,
+                               uint8_t* w_codes, uint8_t* w_scales, float* w_g_dec,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+/* Unpack the tiled weight layout to canonical codes[N][K/2], scales[N][K/16]. */
+nvfp4_status nvfp4_weight_to_canonical(const uint8_t* w_codes, const uint8_t* w_scales,
+                                       int64_t N, int64_t K,
+                                       uint8_t* codes, uint8_t* scales, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * The W4A4 GEMM with the per-module global-scale epilogue.
+ *
+ *   out[m][n] = fl(acc[m][n] * fl(a_g_dec * w_g_dec[seg(n)]))
+ *   acc[m][n] = sum_k (E2M1 * E4M3)(a)[m][k] * (E2M1 * E4M3)(w)[n][k]
+ * with seg(n) the segment holding column n.  Every product is exact (the
+ * operands are decoded exactly to fp16 and multiplied by the matrix cores);
+ * the sum is accumulated in fp32 (FP32 accumulation; order unspecified).
+ *
+ *   a_codes/a_scales  canonical activations from nvfp4_quantize_act, M x K.
+ *   a_g_dec           device pointer to the activations' g_dec.
+ *   w_codes/w_scales  tiled weights from nvfp4_pack_weight, N x K.
+ *   segs              HOST array of nseg segments tiling [0, N) in order.
+ *   w_g_dec           device array of nseg per-module g_dec values.
+ *   out               fp32 [M][ldo], ldo >= N; must not overlap any input.
+ * M <= 16 runs the bandwidth-bound skinny path; larger M the MFMA path.
+ * ------------------------------------------------------------------------- */
+nvfp4_status nvfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_g_dec,
+                        int64_t M, int64_t K,
+                        const uint8_t* w_codes, const uint8_t* w_scales, int64_t N,
+                        const nvfp4_segment* segs, const float* w_g_dec, int32_t nseg,
+                        float* out, int64_t ldo, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NVFP4_W4A4_H */

@@ -1,0 +1,167 @@
+// C ABI of the NVFP4 W4A4 linear layer: argument validation and dispatch.
+// Every check runs on the host before anything is enqueued, so a non-OK status
+// means no work was launched and no HIP call was made.
+#include <stdint.h>
+
+#include <cstring>
+
+#include "common.hpp"
+
+namespace {
+
+using nvfp4::round_up;
+
+constexpr int64_t kMaxDim = (int64_t)1 << 31;  // kernel index math is 32-bit per dimension
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// [p, p + n) and [q, q + m) overlap (both non-empty)?
+bool overlap(const void* p, size_t n, const void* q, size_t m) {
+  if (!p || !q || n == 0 || m == 0) return false;
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p), b = reinterpret_cast<uintptr_t>(q);
+  return a < b + m && b < a + n;
+}
+
+nvfp4_status check_segments(const nvfp4_segment* segs, int32_t nseg, int64_t N) {
+  if (!segs || nseg < 1 || nseg > NVFP4_MAX_SEGMENTS) return NVFP4_ESEGMENTS;
+  int64_t pos = 0;
+  for (int i = 0; i < nseg; ++i) {
+    if (segs[i].n_begin != pos || segs[i].n_end <= segs[i].n_begin) return NVFP4_ESEGMENTS;
+    pos = segs[i].n_end;
+  }
+  return pos == N ? NVFP4_OK : NVFP4_ESEGMENTS;
+}
+
+nvfp4_status launched(hipError_t e) { return e == hipSuccess ? NVFP4_OK : NVFP4_EHIP; }
+
+}  // namespace
+
+extern "C" {
+
+int nvfp4_abi_version(void) { return NVFP4_ABI_VERSION; }
+
+const char* nvfp4_status_str(int s) {
+  switch (s) {
+    case NVFP4_OK: return "ok";
+    case NVFP4_EINVAL: return "invalid argument (null pointer, negative size or overlapping buffers)";
+    case NVFP4_ESHAPE: return "invalid shape (K must be a multiple of 16; leading dimension too small; size too large)";
+    case NVFP4_EALIGN: return "misaligned buffer (16-byte alignment required; bf16 leading dimension must be a multiple of 8)";
+    case NVFP4_ESEGMENTS: return "invalid segment table (must tile [0, N) in order, 1..16 segments)";
+    case NVFP4_EWORKSPACE: return "workspace missing or too small";
+    case NVFP4_EHIP: return "HIP kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+size_t nvfp4_quantize_act_workspace_bytes(int64_t M, int64_t K) {
+  if (M < 0 || K < 0) return 0;
+  return nvfp4::quantize_act_workspace(M, K);
+}
+
+nvfp4_status nvfp4_quantize_act(const void* x_bf16, int64_t M, int64_t K, int64_t ldx, const float* amax_in,
+                                uint8_t* codes, uint8_t* scales, float* g_dec_out, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  if (M < 0 || K < 0) return NVFP4_EINVAL;
+  if (K % 16 != 0 || M >= kMaxDim || K >= kMaxDim || ldx < K) return NVFP4_ESHAPE;
+  if (!g_dec_out) return NVFP4_EINVAL;
+  const bool empty = (M == 0 || K == 0);
+  if (!empty && (!x_bf16 || !codes || !scales)) return NVFP4_EINVAL;
+  if (!empty && (!aligned16(x_bf16) || !aligned16(codes) || !aligned16(scales) || ldx % 8 != 0))
+    return NVFP4_EALIGN;
+  const size_t need = nvfp4::quantize_act_workspace(M, K);
+  if (!amax_in && need > 0 && (!workspace || workspace_bytes < need)) return NVFP4_EWORKSPACE;
+  if (!empty) {
+    const size_t xb = (size_t)((M - 1) * ldx + K) * 2, cb = (size_t)(M * K / 2), sb = (size_t)(M * K / 16);
+    if (overlap(x_bf16, xb, codes, cb) || overlap(x_bf16, xb, scales, sb) || overlap(codes, cb, scales, sb) ||
+        overlap(x_bf16, xb, g_dec_out, 4) || overlap(codes, cb, g_dec_out, 4) || overlap(scales, sb, g_dec_out, 4))
+      return NVFP4_EINVAL;
+  }
+  return launched(nvfp4::launch_quantize_act(static_cast<const uint16_t*>(x_bf16), M, K, ldx, amax_in, codes,
+                                             scales, g_dec_out, workspace, static_cast<hipStream_t>(stream)));
+}
+
+nvfp4_status nvfp4_packed_weight_bytes(int64_t N, int64_t K, size_t* codes_bytes, size_t* scales_bytes) {
+  if (N < 0 || K < 0 || !codes_bytes || !scales_bytes) return NVFP4_EINVAL;
+  if (K % 16 != 0 || N >= kMaxDim || K >= kMaxDim) return NVFP4_ESHAPE;
+  const int64_t Np = round_up(N, nvfp4::kStrip), Kp = round_up(K, nvfp4::kTileK);
+  *codes_bytes = (size_t)(Np * Kp / 2);
+  *scales_bytes = (size_t)(Np * Kp / 16);
+  return NVFP4_OK;
+}
+
+size_t nvfp4_pack_weight_workspace_bytes(int64_t N, int64_t K, int32_t nseg) {
+  if (N < 0 || K < 0 || nseg < 1 || nseg > NVFP4_MAX_SEGMENTS) return 0;
+  return nvfp4::pack_weight_workspace(N, K, nseg);
+}
+
+nvfp4_status nvfp4_pack_weight(const float* w, int64_t N, int64_t K, int64_t ldw, const nvfp4_segment* segs,
+                               int32_t nseg, uint8_t* w_codes, uint8_t* w_scales, float* w_g_dec,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  if (N < 1 || K < 0) return NVFP4_EINVAL;
+  if (K % 16 != 0 || N >= kMaxDim || K >= kMaxDim || ldw < K) return NVFP4_ESHAPE;
+  if ((!w && K > 0) || !w_codes || !w_scales || !w_g_dec) return NVFP4_EINVAL;
+  const nvfp4_status ss = check_segments(segs, nseg, N);
+  if (ss != NVFP4_OK) return ss;
+  if (!aligned16(w) || !aligned16(w_codes) || !aligned16(w_scales) || !aligned16(w_g_dec)) return NVFP4_EALIGN;
+  const size_t need = nvfp4::pack_weight_workspace(N, K, nseg);
+  if (!workspace || workspace_bytes < need) return NVFP4_EWORKSPACE;
+  size_t cb = 0, sb = 0;
+  nvfp4_packed_weight_bytes(N, K, &cb, &sb);
+  const size_t wb = (size_t)((N - 1) * ldw + K) * 4;
+  if (overlap(w, wb, w_codes, cb) || overlap(w, wb, w_scales, sb) || overlap(w_codes, cb, w_scales, sb) ||
+      overlap(w_g_dec, nseg * 4, w, wb) || overlap(w_g_dec, nseg * 4, w_codes, cb) ||
+      overlap(w_g_dec, nseg * 4, w_scales, sb) || overlap(workspace, need, w, wb) ||
+      overlap(workspace, need, w_codes, cb) || overlap(workspace, need, w_scales, sb))
+    return NVFP4_EINVAL;
+  return launched(nvfp4::launch_pack_weight(w, N, K, ldw, segs, nseg, w_codes, w_scales, w_g_dec, workspace,
+                                            static_cast<hipStream_t>(stream)));
+}
+
+nvfp4_status nvfp4_weight_to_canonical(const uint8_t* w_codes, const uint8_t* w_scales, int64_t N, int64_t K,
+                                       uint8_t* codes, uint8_t* scales, void* stream) {
+  if (N < 0 || K < 0) return NVFP4_EINVAL;
+  if (K % 16 != 0 || N >= kMaxDim || K >= kMaxDim) return NVFP4_ESHAPE;
+  if (N == 0 || K == 0) return NVFP4_OK;
+  if (!w_codes || !w_scales || !codes || !scales) return NVFP4_EINVAL;
+  if (!aligned16(w_codes) || !aligned16(w_scales) || !aligned16(codes) || !aligned16(scales)) return NVFP4_EALIGN;
+  return launched(nvfp4::launch_weight_to_canonical(w_codes, w_scales, N, K, codes, scales,
+                                                    static_cast<hipStream_t>(stream)));
+}
+
+nvfp4_status nvfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_g_dec, int64_t M,
+                        int64_t K, const uint8_t* w_codes, const uint8_t* w_scales, int64_t N,
+                        const nvfp4_segment* segs, const float* w_g_dec, int32_t nseg, float* out, int64_t ldo,
+                        void* stream) {
+  if (M < 0 || K < 0 || N < 1) return NVFP4_EINVAL;
+  if (K % 16 != 0 || M >= kMaxDim || K >= kMaxDim || N >= kMaxDim || ldo < N) return NVFP4_ESHAPE;
+  const nvfp4_status ss = check_segments(segs, nseg, N);
+  if (ss != NVFP4_OK) return ss;
+  if (M == 0) return NVFP4_OK;
+  if (K == 0) {  // empty sum: out = 0; no operand is read
+    if (!out) return NVFP4_EINVAL;
+    if (!aligned16(out)) return NVFP4_EALIGN;
+    return launched(nvfp4::launch_fill_zero(out, (int)M, (int)N, ldo, static_cast<hipStream_t>(stream)));
+  }
+  if (!a_codes || !a_scales || !a_g_dec || !w_codes || !w_scales || !w_g_dec || !out) return NVFP4_EINVAL;
+  if (!aligned16(a_codes) || !aligned16(a_scales) || !aligned16(w_codes) || !aligned16(w_scales) ||
+      !aligned16(out))
+    return NVFP4_EALIGN;
+  size_t cb = 0, sb = 0;
+  nvfp4_packed_weight_bytes(N, K, &cb, &sb);
+  const size_t ob = (size_t)((M - 1) * ldo + N) * 4;
+  if (overlap(out, ob, a_codes, (size_t)(M * K / 2)) || overlap(out, ob, a_scales, (size_t)(M * K / 16)) ||
+      overlap(out, ob, a_g_dec, 4) || overlap(out, ob, w_codes, cb) || overlap(out, ob, w_scales, sb) ||
+      overlap(out, ob, w_g_dec, (size_t)nseg * 4))
+    return NVFP4_EINVAL;
+  nvfp4::SegTable st{};
+  st.nseg = nseg;
+  for (int i = 0; i < nseg; ++i) st.end[i] = segs[i].n_end;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (M <= 16)
+    return launched(nvfp4::launch_gemm_skinny(a_codes, a_scales, a_g_dec, (int)M, (int)K, w_codes, w_scales,
+                                              (int)N, st, w_g_dec, out, ldo, s));
+  return launched(nvfp4::launch_gemm_mfma(a_codes, a_scales, a_g_dec, (int)M, (int)K, w_codes, w_scales, (int)N,
+                                          st, w_g_dec, out, ldo, s));
+}
+
+}  // extern "C"

@@ -1,0 +1,126 @@
+// Shared device helpers and layout constants for the gfx950 NVFP4 kernels.
+//
+// NVFP4 (Summary page "Summary of 'Why Gated DeltaNet Survives 4-Bit
+// Quantization'", Background, item 1): E2M1 element codes, one E4M3 scale per
+// 16 elements, one FP32 scale per tensor.  Bit layouts are the OCP ones:
+// E2M1 = sign | 2-bit exponent (bias 1) | 1-bit mantissa, magnitudes
+// 0, .5, 1, 1.5, 2, 3, 4, 6; E4M3FN = sign | 4-bit exponent (bias 7) | 3-bit
+// mantissa, subnormals m * 2^-9, largest finite 448 (0x7E).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/nvfp4.h"
+
+namespace nvfp4 {
+
+// ---- layout constants -------------------------------------------------------
+constexpr int kBlock = 16;        // elements per E4M3 scale
+constexpr int kTileK = 128;       // k extent of one weight chunk
+constexpr int kStrip = 16;        // rows (output columns) of one weight chunk
+constexpr int kChunkCodes = kStrip * kTileK / 2;        // 1024 bytes
+constexpr int kChunkScales = kStrip * kTileK / kBlock;  // 128 bytes
+constexpr float kGMax = 2688.0f;  // 6 * 448
+
+inline int64_t round_up(int64_t a, int64_t b) { return (a + b - 1) / b * b; }
+
+// Segment table passed by value to the GEMM kernels: column -> module index.
+struct SegTable {
+  int32_t end[NVFP4_MAX_SEGMENTS];  // exclusive end column of each segment
+  int32_t nseg;
+};
+
+__device__ __forceinline__ int seg_of(const SegTable& st, int n) {
+  int s = 0;
+#pragma unroll
+  for (int i = 0; i < NVFP4_MAX_SEGMENTS - 1; ++i)
+    s += (i < st.nseg - 1 && n >= st.end[i]) ? 1 : 0;
+  return s;
+}
+
+// ---- E4M3FN -----------------------------------------------------------------
+// Round a non-negative binary32 s (finite or +inf) to the nearest E4M3FN
+// magnitude code, ties to even mantissa, saturating at 448 (0x7E).
+__device__ __forceinline__ uint32_t e4m3_encode_rne_sat(float s) {
+  if (!(s < 448.0f)) return 0x7Eu;                 // also +inf
+  const uint32_t u = __float_as_uint(s);
+  const int e = (int)(u >> 23) - 127;
+  if (e < -6) {
+    // subnormal range: value m * 2^-9, m = rint(s * 2^9) in 0..8 (8 is 2^-6)
+    return (uint32_t)__builtin_rintf(s * 512.0f);
+  }
+  // normal: keep 3 mantissa bits, round the 20 dropped bits to nearest even;
+  // a carry out of the mantissa moves into the exponent field, as it should.
+  const uint32_t mant = u & 0x7FFFFFu;
+  uint32_t code = ((uint32_t)(e + 7) << 3) | (mant >> 20);
+  const uint32_t rem = mant & 0xFFFFFu;
+  code += (rem > 0x80000u || (rem == 0x80000u && (code & 1u))) ? 1u : 0u;
+  return code;                                      // <= 0x7E because s < 448
+}
+
+// Exact binary32 value of an E4M3FN magnitude code 0..0x7E.
+__device__ __forceinline__ float e4m3_value(uint32_t c) {
+  const uint32_t e = (c >> 3) & 0xF, m = c & 7;
+  if (e == 0) return (float)m * (1.0f / 512.0f);
+  return __uint_as_float(((e + 120u) << 23) | (m << 20));
+}
+
+// ---- decode to fp16 ---------------------------------------------------------
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef float float16_t __attribute__((ext_vector_type(16)));
+
+// 8 E2M1 codes (one dword, low nibble first) times one E4M3 scale, as 8 exact
+// fp16 values.  cvt_scalef32_pk_f16_fp4 with scale 1.0 gives the E2M1 values
+// exactly; multiplying by the scale in fp16 is exact because every product of
+// an E2M1 magnitude and an E4M3 value has at most 6 significant bits and lies
+// in [2^-10, 2688], inside fp16's normal range.
+__device__ __forceinline__ half8_t decode8(uint32_t w, half2_t s2) {
+  half2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0);
+  half2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1);
+  half2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2);
+  half2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3);
+  p0 *= s2; p1 *= s2; p2 *= s2; p3 *= s2;
+  half8_t r;
+  r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
+  r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
+  return r;
+}
+
+// E4M3 scale byte -> fp16 pair (exact: every E4M3 value is an fp16 normal).
+__device__ __forceinline__ half2_t scale_h2(uint32_t c) {
+  const _Float16 h = (_Float16)e4m3_value(c & 0x7F);
+  half2_t r = {h, h};
+  return r;
+}
+
+}  // namespace nvfp4
+
+// ---- host-side launchers (one per kernel family), defined in the .hip files --
+namespace nvfp4 {
+hipError_t launch_quantize_act(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+                               const float* amax_in, uint8_t* codes, uint8_t* scales,
+                               float* g_dec_out, void* workspace, hipStream_t stream);
+size_t quantize_act_workspace(int64_t M, int64_t K);
+
+hipError_t launch_pack_weight(const float* w, int64_t N, int64_t K, int64_t ldw,
+                              const nvfp4_segment* segs, int nseg,
+                              uint8_t* w_codes, uint8_t* w_scales, float* w_g_dec,
+                              void* workspace, hipStream_t stream);
+size_t pack_weight_workspace(int64_t N, int64_t K, int nseg);
+hipError_t launch_weight_to_canonical(const uint8_t* w_codes, const uint8_t* w_scales,
+                                      int64_t N, int64_t K, uint8_t* codes, uint8_t* scales,
+                                      hipStream_t stream);
+
+hipError_t launch_gemm_skinny(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_g,
+                              int M, int K, const uint8_t* w_codes, const uint8_t* w_scales, int N,
+                              const SegTable& st, const float* w_g, float* out, int64_t ldo,
+                              hipStream_t stream);
+hipError_t launch_fill_zero(float* out, int M, int N, int64_t ldo, hipStream_t stream);
+hipError_t launch_gemm_mfma(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_g,
+                            int M, int K, const uint8_t* w_codes, const uint8_t* w_scales, int N,
+                            const SegTable& st, const float* w_g, float* out, int64_t ldo,
+                            hipStream_t stream);
+}  // namespace nvfp4

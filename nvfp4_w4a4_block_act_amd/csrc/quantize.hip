@@ -1,0 +1,318 @@
+// NVFP4 encoder kernels: on-the-fly activation quantization (bf16 in) and the
+// per-module weight encoder's block step (fp32 in).
+//
+// Format: Summary page ("Summary of 'Why Gated DeltaNet Survives 4-Bit
+// Quantization'"), Background, item 1 -- E2M1 elements, an E4M3 scale per 16
+// elements from the block maximum / 6, an FP32 scale per tensor.  The FP32
+// scale maps the tensor maximum onto 6 * 448 = 2688; every rounding below is
+// one binary32 operation (this file is built with -ffp-contract=off and the
+// default correctly rounded fp32 division), so the codes are bit-identical to
+// the step-by-step definition in include/nvfp4.h.
+//
+// Work decomposition (HBM-bound: read 2 B, write 0.5625 B per element):
+//  * one thread encodes one 16-element block per loop trip: two 16-byte bf16
+//    loads (a wave reads 2 KB contiguous), block max on the bit patterns,
+//    two correctly rounded divisions per block, one multiply per element and
+//    the gfx950 fp4 converter (v_cvt_scalef32_pk_fp4_f32 with unit scale
+//    rounds to nearest even and saturates at 6, exactly the E2M1 rule);
+//  * dynamic amax of large tensors: a partial-max kernel writes one value per
+//    workgroup into the workspace and the encoder reduces them in its prologue
+//    (exact, order-independent, no atomics, no memset);
+//  * small tensors (decode-sized activations) use a single launch in which
+//    every workgroup recomputes the whole-tensor maximum from L2.
+#include <algorithm>
+
+#include "common.hpp"
+
+namespace nvfp4 {
+
+constexpr int kQThreads = 256;
+constexpr int kPartials = 1024;              // amax workgroups in the two-pass path
+constexpr int64_t kSmallElems = 1 << 18;     // single-launch path up to 256K elements
+
+// ---- block encoder ------------------------------------------------------------
+// x: the 16 values of one block as binary32 (exactly widened), bmax = max|x|.
+// Returns the E4M3 scale code; writes the 16 element codes (8 bytes) to out.
+__device__ __forceinline__ uint32_t encode_block(const float (&x)[16], float bmax, float g_enc,
+                                                 uint2& out) {
+  const float t = bmax / 6.0f;
+  const uint32_t sc = (t != 0.0f) ? e4m3_encode_rne_sat(t * g_enc) : 0u;
+  const float sdec = e4m3_value(sc);
+  // sdec == 0: every magnitude is 0; x * 0 keeps the sign bit, which the fp4
+  // converter then emits on its own.
+  const float rb = (sdec != 0.0f) ? g_enc / sdec : 0.0f;
+  float y[16];
+  if (__builtin_isinf(rb)) {
+    // g_enc overflowed (tensor maximum below ~1e-35): 0 * inf would be NaN,
+    // but a zero element encodes to magnitude 0.
+#pragma unroll
+    for (int i = 0; i < 16; ++i) y[i] = (x[i] == 0.0f) ? x[i] : x[i] * rb;
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) y[i] = x[i] * rb;
+  }
+  uint32_t lo = 0, hi = 0;
+  lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo, y[0], y[1], 1.0f, 0);
+  lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo, y[2], y[3], 1.0f, 1);
+  lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo, y[4], y[5], 1.0f, 2);
+  lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo, y[6], y[7], 1.0f, 3);
+  hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi, y[8], y[9], 1.0f, 0);
+  hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi, y[10], y[11], 1.0f, 1);
+  hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi, y[12], y[13], 1.0f, 2);
+  hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi, y[14], y[15], 1.0f, 3);
+  out = make_uint2(lo, hi);
+  return sc;
+}
+
+// Per-tensor encode factor from amax; amax == 0 makes every block's scale 0.
+__device__ __forceinline__ float g_enc_of(float amax) {
+  return (amax == 0.0f) ? 0.0f : kGMax / amax;
+}
+
+// Encode the bf16 block (m, b) of x.
+__device__ __forceinline__ void encode_bf16_block(const uint16_t* __restrict__ x, int64_t ldx, int K,
+                                                  int64_t m, int b, float g_enc,
+                                                  uint8_t* __restrict__ codes,
+                                                  uint8_t* __restrict__ scales) {
+  const uint4* p = reinterpret_cast<const uint4*>(x + m * ldx + (int64_t)b * kBlock);
+  const uint4 v0 = p[0];
+  const uint4 v1 = p[1];
+  const uint32_t d[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+  float xf[16];
+  uint32_t mb = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    xf[2 * i] = __uint_as_float(d[i] << 16);
+    xf[2 * i + 1] = __uint_as_float(d[i] & 0xFFFF0000u);
+    mb = max(mb, max(d[i] & 0x7FFFu, (d[i] >> 16) & 0x7FFFu));
+  }
+  uint2 c;
+  const uint32_t sc = encode_block(xf, __uint_as_float(mb << 16), g_enc, c);
+  *reinterpret_cast<uint2*>(codes + m * (K / 2) + (int64_t)b * 8) = c;
+  scales[m * (K / kBlock) + b] = (uint8_t)sc;
+}
+
+// ---- whole-tensor |x| maximum on bf16 bit patterns ------------------------------
+// For finite bf16, |x| orders exactly like (bits & 0x7FFF) as an unsigned integer.
+__device__ __forceinline__ uint32_t chunk_absmax(const uint16_t* __restrict__ x, int64_t ldx, int K,
+                                                 int64_t M, int64_t first, int64_t stride) {
+  // 8-element (16-byte) chunks of the M x K tensor, row-major over the valid region.
+  const int64_t cpr = K / 8;
+  const int64_t total = M * cpr;
+  uint32_t m = 0;
+  for (int64_t c = first; c < total; c += stride) {
+    const int64_t r = c / cpr;
+    const int64_t k = (c - r * cpr) * 8;
+    const uint4 v = *reinterpret_cast<const uint4*>(x + r * ldx + k);
+    const uint32_t a0 = max(v.x & 0x7FFFu, v.x >> 16 & 0x7FFFu), a1 = max(v.y & 0x7FFFu, v.y >> 16 & 0x7FFFu);
+    const uint32_t a2 = max(v.z & 0x7FFFu, v.z >> 16 & 0x7FFFu), a3 = max(v.w & 0x7FFFu, v.w >> 16 & 0x7FFFu);
+    m = max(m, max(max(a0, a1), max(a2, a3)));
+  }
+  return m;
+}
+
+__device__ __forceinline__ uint32_t block_reduce_max(uint32_t v, uint32_t* red) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o, 64));
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+  if (l == 0) red[w] = v;
+  __syncthreads();
+  uint32_t r = 0;
+  for (int i = 0; i < (int)(blockDim.x >> 6); ++i) r = max(r, red[i]);
+  __syncthreads();
+  return r;
+}
+
+__global__ __launch_bounds__(kQThreads) void amax_partial_kernel(const uint16_t* __restrict__ x, int64_t M,
+                                                                 int K, int64_t ldx,
+                                                                 uint32_t* __restrict__ partial) {
+  __shared__ uint32_t red[kQThreads / 64];
+  const uint32_t m = chunk_absmax(x, ldx, K, M, (int64_t)blockIdx.x * blockDim.x + threadIdx.x,
+                                  (int64_t)gridDim.x * blockDim.x);
+  const uint32_t r = block_reduce_max(m, red);
+  if (threadIdx.x == 0) partial[blockIdx.x] = r;
+}
+
+// mode 0: amax from `partial` (nparts values); mode 1: amax from *amax_in;
+// mode 2: every workgroup computes the whole-tensor maximum itself.
+__global__ __launch_bounds__(kQThreads) void quantize_act_kernel(
+    const uint16_t* __restrict__ x, int64_t M, int K, int64_t ldx, int mode,
+    const uint32_t* __restrict__ partial, int nparts, const float* __restrict__ amax_in,
+    uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, float* __restrict__ g_dec_out) {
+  __shared__ uint32_t red[kQThreads / 64];
+  float amax;
+  if (mode == 1) {
+    amax = *amax_in;
+  } else {
+    uint32_t m = 0;
+    if (mode == 0) {
+      for (int i = threadIdx.x; i < nparts; i += blockDim.x) m = max(m, partial[i]);
+    } else {
+      m = chunk_absmax(x, ldx, K, M, threadIdx.x, blockDim.x);
+    }
+    amax = __uint_as_float(block_reduce_max(m, red) << 16);
+  }
+  const float g_enc = g_enc_of(amax);
+  if (blockIdx.x == 0 && threadIdx.x == 0) *g_dec_out = amax / kGMax;
+
+  const int nb = K / kBlock;
+  const int64_t total = M * nb;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t m = i / nb;
+    const int b = (int)(i - m * nb);
+    encode_bf16_block(x, ldx, K, m, b, g_enc, codes, scales);
+  }
+}
+
+__global__ void g_dec_only_kernel(const float* __restrict__ amax_in, float* __restrict__ g_dec_out) {
+  *g_dec_out = amax_in ? *amax_in / kGMax : 0.0f;
+}
+
+size_t quantize_act_workspace(int64_t M, int64_t K) {
+  return (M * K > kSmallElems) ? kPartials * sizeof(uint32_t) : 0;
+}
+
+hipError_t launch_quantize_act(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+                               const float* amax_in, uint8_t* codes, uint8_t* scales,
+                               float* g_dec_out, void* workspace, hipStream_t stream) {
+  const int64_t blocks = M * (K / kBlock);
+  if (blocks == 0) {
+    g_dec_only_kernel<<<1, 1, 0, stream>>>(amax_in, g_dec_out);
+    return hipGetLastError();
+  }
+  // Enough workgroups to keep ~8 per CU busy; each thread then loops over blocks.
+  const int64_t want = (blocks + kQThreads - 1) / kQThreads;
+  if (amax_in) {
+    const int grid = (int)std::min<int64_t>(want, 256 * 8);
+    quantize_act_kernel<<<grid, kQThreads, 0, stream>>>(x, M, (int)K, ldx, 1, nullptr, 0, amax_in,
+                                                        codes, scales, g_dec_out);
+  } else if (M * K <= kSmallElems) {
+    const int grid = (int)std::min<int64_t>(want, 64);
+    quantize_act_kernel<<<grid, kQThreads, 0, stream>>>(x, M, (int)K, ldx, 2, nullptr, 0, nullptr,
+                                                        codes, scales, g_dec_out);
+  } else {
+    uint32_t* partial = static_cast<uint32_t*>(workspace);
+    const int64_t chunks = M * (K / 8);
+    const int pgrid = (int)std::max<int64_t>(1, std::min<int64_t>(kPartials, chunks / (kQThreads * 16)));
+    amax_partial_kernel<<<pgrid, kQThreads, 0, stream>>>(x, M, (int)K, ldx, partial);
+    const int grid = (int)std::min<int64_t>(want, 256 * 8);
+    quantize_act_kernel<<<grid, kQThreads, 0, stream>>>(x, M, (int)K, ldx, 0, partial, pgrid, nullptr,
+                                                        codes, scales, g_dec_out);
+  }
+  return hipGetLastError();
+}
+
+// ---- weights: per-module encode into the tiled layout ----------------------------
+constexpr int kSegParts = 64;   // amax workgroups per segment
+
+// partial[s * kSegParts + p] = max |w| bits over a slice of segment s's rows.
+__global__ __launch_bounds__(kQThreads) void seg_amax_kernel(const float* __restrict__ w, int K, int64_t ldw,
+                                                             SegTable st, uint32_t* __restrict__ partial) {
+  __shared__ uint32_t red[kQThreads / 64];
+  const int s = blockIdx.y;
+  const int64_t r0 = (s == 0) ? 0 : st.end[s - 1];
+  const int64_t rows = st.end[s] - r0;
+  const int64_t total = rows * K;
+  uint32_t m = 0;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t r = i / K;
+    const int64_t k = i - r * K;
+    m = max(m, __float_as_uint(w[(r0 + r) * ldw + k]) & 0x7FFFFFFFu);
+  }
+  const uint32_t r = block_reduce_max(m, red);
+  if (threadIdx.x == 0) partial[s * kSegParts + blockIdx.x] = r;
+}
+
+// One thread per 16-element block of the padded Np x Kp weight.
+__global__ __launch_bounds__(kQThreads) void pack_weight_kernel(
+    const float* __restrict__ w, int N, int K, int64_t ldw, int Np, int Kp, SegTable st,
+    const uint32_t* __restrict__ partial, uint8_t* __restrict__ w_codes, uint8_t* __restrict__ w_scales,
+    float* __restrict__ w_g_dec) {
+  __shared__ float s_genc[NVFP4_MAX_SEGMENTS];
+  if (threadIdx.x < st.nseg) {
+    uint32_t m = 0;
+    for (int p = 0; p < kSegParts; ++p) m = max(m, partial[threadIdx.x * kSegParts + p]);
+    const float amax = __uint_as_float(m);
+    s_genc[threadIdx.x] = g_enc_of(amax);
+    if (blockIdx.x == 0) w_g_dec[threadIdx.x] = amax / kGMax;
+  }
+  __syncthreads();
+  const int nbk = Kp / kBlock;
+  const int64_t total = (int64_t)Np * nbk;
+  const int tiles = Kp / kTileK;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int n = (int)(i / nbk);
+    const int b = (int)(i - (int64_t)n * nbk);
+    uint2 c = make_uint2(0u, 0u);
+    uint32_t sc = 0;
+    if (n < N && b * kBlock < K) {
+      const float* p = w + (int64_t)n * ldw + (int64_t)b * kBlock;
+      float xf[16];
+      float bmax = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        xf[j] = p[j];
+        bmax = fmaxf(bmax, fabsf(xf[j]));
+      }
+      sc = encode_block(xf, bmax, s_genc[seg_of(st, n)], c);
+    }
+    const int64_t chunk = (int64_t)(n / kStrip) * tiles + b / (kTileK / kBlock);
+    const int r = n % kStrip, bb = b % (kTileK / kBlock);
+    *reinterpret_cast<uint2*>(w_codes + chunk * kChunkCodes + r * (kTileK / 2) + bb * 8) = c;
+    w_scales[chunk * kChunkScales + r * (kTileK / kBlock) + bb] = (uint8_t)sc;
+  }
+}
+
+__global__ __launch_bounds__(kQThreads) void weight_to_canonical_kernel(
+    const uint8_t* __restrict__ w_codes, const uint8_t* __restrict__ w_scales, int N, int K, int Kp,
+    uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
+  const int nb = K / kBlock;
+  const int64_t total = (int64_t)N * nb;
+  const int tiles = Kp / kTileK;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int n = (int)(i / nb);
+    const int b = (int)(i - (int64_t)n * nb);
+    const int64_t chunk = (int64_t)(n / kStrip) * tiles + b / (kTileK / kBlock);
+    const int r = n % kStrip, bb = b % (kTileK / kBlock);
+    const uint2 c = *reinterpret_cast<const uint2*>(w_codes + chunk * kChunkCodes + r * (kTileK / 2) + bb * 8);
+    *reinterpret_cast<uint2*>(codes + (int64_t)n * (K / 2) + (int64_t)b * 8) = c;
+    scales[(int64_t)n * nb + b] = w_scales[chunk * kChunkScales + r * (kTileK / kBlock) + bb];
+  }
+}
+
+size_t pack_weight_workspace(int64_t, int64_t, int nseg) {
+  return (size_t)nseg * kSegParts * sizeof(uint32_t);
+}
+
+hipError_t launch_pack_weight(const float* w, int64_t N, int64_t K, int64_t ldw,
+                              const nvfp4_segment* segs, int nseg, uint8_t* w_codes,
+                              uint8_t* w_scales, float* w_g_dec, void* workspace,
+                              hipStream_t stream) {
+  SegTable st{};
+  st.nseg = nseg;
+  for (int i = 0; i < nseg; ++i) st.end[i] = segs[i].n_end;
+  uint32_t* partial = static_cast<uint32_t*>(workspace);
+  seg_amax_kernel<<<dim3(kSegParts, nseg), kQThreads, 0, stream>>>(w, (int)K, ldw, st, partial);
+  const int64_t Np = round_up(N, kStrip), Kp = round_up(K, kTileK);
+  const int64_t total = Np * (Kp / kBlock);
+  const int grid = (int)std::max<int64_t>(1, std::min<int64_t>((total + kQThreads - 1) / kQThreads, 256 * 16));
+  pack_weight_kernel<<<grid, kQThreads, 0, stream>>>(w, (int)N, (int)K, ldw, (int)Np, (int)Kp, st, partial,
+                                                     w_codes, w_scales, w_g_dec);
+  return hipGetLastError();
+}
+
+hipError_t launch_weight_to_canonical(const uint8_t* w_codes, const uint8_t* w_scales, int64_t N,
+                                      int64_t K, uint8_t* codes, uint8_t* scales, hipStream_t stream) {
+  const int64_t total = N * (K / kBlock);
+  if (total == 0) return hipSuccess;
+  const int grid = (int)std::max<int64_t>(1, std::min<int64_t>((total + kQThreads - 1) / kQThreads, 256 * 16));
+  weight_to_canonical_kernel<<<grid, kQThreads, 0, stream>>>(w_codes, w_scales, (int)N, (int)K,
+                                                             (int)round_up(K, kTileK), codes, scales);
+  return hipGetLastError();
+}
+
+}  // namespace nvfp4

@@ -1,0 +1,315 @@
+#!/usr/bin/env python3
+"""Benchmark of the NVFP4 W4A4 linear layer on one MI355X.
+
+Default workload: the decode skinny GEMM -- M in {1, 4, 16} tokens, K = 5120,
+N = 12288, weights N(0, 0.02) pre-packed, bf16 Student-t(3) activations with
+0.1% of channels x100 quantized on the fly.  One step = the whole hot path for
+the three token counts: activation quantization (dynamic per-tensor scale) +
+W4A4 GEMM + per-segment epilogue, three times.  The packed weight is kept in
+16 device copies (566 MB, more than the 256 MB MALL) and each step uses the
+next copy, so every call streams its weights from HBM.  The 16 steps that use
+the 16 copies in turn are captured in one HIP graph, replayed once per 16
+timed steps (remainders replay single-step graphs); inputs are resident in HBM
+before the timed region starts.
+
+Prints one JSON line (see the keys below).  ``--config`` selects another
+workload (prefill_gate_up, gdn_in_proj, down_proj, down_proj_quantize, tiny).
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBS = 8000.0          # MI355X published HBM3E bandwidth
+F16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X published dense fp16/bf16 matrix peak
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=480)
+    ap.add_argument("--warmup", type=int, default=48)
+    ap.add_argument("--config", default="decode",
+                    choices=["decode", "prefill_gate_up", "gdn_in_proj", "down_proj", "down_proj_quantize", "tiny"])
+    ap.add_argument("--copies", type=int, default=16, help="device copies of the packed weight (decode)")
+    ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying HIP graphs")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(sharding is described in DESIGN.md); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import nvfp4_w4a4_block_act_amd as nv
+    import workloads as W
+    torch.cuda.init()
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+
+    if args.config == "decode":
+        res = bench_decode(args, torch, nv, W, dev)
+    elif args.config == "down_proj_quantize":
+        res = bench_quantize(args, torch, nv, W, dev)
+    else:
+        res = bench_gemm(args, torch, nv, W, dev)
+    print(json.dumps(res), flush=True)
+
+
+# ---------------------------------------------------------------------------------------
+def to_dev_bf16(torch, bits, dev):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+
+def time_region(torch, fn, steps, warmup):
+    """Warm up, then time exactly `steps` calls of fn between synchronizations.
+    fn(i) is called with i >= 1 for warmup calls and i = 0 .. steps-1 when timed."""
+    for i in range(warmup):
+        fn(i + 1)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for i in range(steps):
+        fn(i)
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return e0.elapsed_time(e1) / 1e3, wall
+
+
+def kernel_time_pairs(torch, launch, n, warmup=5):
+    """Average duration of one launch from HIP event pairs recorded around each launch
+    on the launch stream (torch's current stream, which the library launches on)."""
+    for i in range(warmup):
+        launch(i)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for i, (a, b) in enumerate(evs):
+        a.record()
+        launch(i)
+        b.record()
+    torch.cuda.synchronize()
+    d = np.array([a.elapsed_time(b) for a, b in evs]) / 1e3
+    return float(np.mean(d)), float(np.median(d))
+
+
+def cpu_threads():
+    try:
+        return len(os.sched_getaffinity(0))
+    except Exception:
+        return os.cpu_count()
+
+
+# ---------------------------------------------------------------------------------------
+def bench_decode(args, torch, nv, W, dev):
+    Ms = (1, 4, 16)
+    d16 = W.decode(M=16)
+    K, N = d16.K, d16.N
+    w = torch.from_numpy(d16.w).to(dev)
+    pw0 = nv.pack_weight(w, d16.segments)
+    del w
+    copies = [pw0] + [nv.PackedWeight(pw0.codes.clone(), pw0.scales.clone(), pw0.g_dec.clone(), N, K,
+                                      pw0.segments) for _ in range(args.copies - 1)]
+    xs = {M: to_dev_bf16(torch, d16.x_bits[:M], dev) for M in Ms}
+    acts = {M: (torch.empty((M, K // 2), dtype=torch.uint8, device=dev),
+                torch.empty((M, K // 16), dtype=torch.uint8, device=dev),
+                torch.empty(1, dtype=torch.float32, device=dev)) for M in Ms}
+    outs = {M: torch.empty((M, N), dtype=torch.float32, device=dev) for M in Ms}
+    ws = nv.Workspace(dev)
+    torch.cuda.synchronize()
+
+    def step_eager(r):
+        for M in Ms:
+            c, s, g = nv.quantize_act(xs[M], None, ws, out=acts[M])
+            nv.gemm(c, s, g, copies[r % len(copies)], out=outs[M])
+
+    nc = len(copies)
+    if args.no_graph:
+        sec, wall = time_region(torch, step_eager, args.steps, args.warmup)
+    else:
+        # one graph per weight copy (a single step) and one graph of all copies in
+        # order (nc consecutive steps), so the host submits one replay per nc steps
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for r in range(nc):                # run the path once on a side stream before capture
+                step_eager(r)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        long_graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(long_graph):
+            for r in range(nc):
+                step_eager(r)
+        singles = []
+        for r in range(nc):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step_eager(r)
+            singles.append(g)
+        torch.cuda.synchronize()
+
+        def run_steps(n):
+            for _ in range(n // nc):
+                long_graph.replay()
+            for r in range(n % nc):
+                singles[r].replay()
+
+        sec, wall = time_region(torch, lambda i: run_steps(args.steps) if i == 0 else run_steps(args.warmup),
+                                1, 1)
+    # algorithmic bytes of one step: packed weight + bf16 activations + fp32 outputs, per call
+    wbytes = pw0.nbytes()
+    step_bytes = sum(wbytes + 2 * M * K + 4 * M * N for M in Ms)
+    value = step_bytes * args.steps / sec / 1e9
+
+    # dominant kernel: the skinny GEMM.  Per M, a graph of nc back-to-back launches
+    # (one per weight copy) is replayed with a HIP event pair around each replay on
+    # the launch stream; average launch duration = event time / launches.
+    # Algorithmic bytes per launch = weight codes+scales + activation codes+scales
+    # + fp32 output.
+    kern = {}
+    for M in Ms:
+        nv.quantize_act(xs[M], None, ws, out=acts[M])
+        torch.cuda.synchronize()
+        if args.no_graph:
+            launch = lambda i, M=M: [nv.gemm(acts[M][0], acts[M][1], acts[M][2], copies[r], out=outs[M])
+                                     for r in range(nc)]
+        else:
+            gg = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gg):
+                for r in range(nc):
+                    nv.gemm(acts[M][0], acts[M][1], acts[M][2], copies[r], out=outs[M])
+            launch = lambda i, gg=gg: gg.replay()
+        mean, med = kernel_time_pairs(torch, launch, max(8, args.steps // nc))
+        mean, med = mean / nc, med / nc
+        kb = wbytes + M * K * 9 // 16 + 4 * M * N
+        kern[M] = {"mean_us": mean * 1e6, "median_us": med * 1e6, "bytes": kb, "GBps": kb / mean / 1e9}
+    tot_b = sum(k["bytes"] for k in kern.values())
+    tot_t = sum(k["mean_us"] for k in kern.values()) * 1e-6
+    achieved = tot_b / tot_t / 1e9
+
+    res = {
+        "metric": "NVFP4 W4A4 decode GEMM GB/s (quantize + GEMM + epilogue), % of MI355X HBM roofline",
+        "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(sec / args.steps * 1e3, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f16",
+        "dtype_note": "NVFP4 operands decoded exactly to fp16, fp16 MFMA products, fp32 accumulation",
+        "data": "synthetic",
+        "config": {"workload": "decode_skinny_gemm_m1_m4_m16_k5120_n12288", "M": list(Ms), "K": K, "N": N,
+                   "segments": 1, "weight_copies": len(copies), "graphs": not args.no_graph,
+                   "step_bytes": step_bytes, "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
+                   "gemm_kernel": {str(M): {k: round(v, 3) if isinstance(v, float) else v for k, v in kern[M].items()}
+                                   for M in Ms}},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "gemm_skinny_kernel", "per_launch_bytes": {str(M): kern[M]["bytes"] for M in Ms}},
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_decode(d16, Ms, args.cpu_seconds, step_bytes)
+    return res
+
+
+def cpu_baseline_decode(d16, Ms, target_s, step_bytes):
+    """The oracle on the host: per call, quantize + decode the activations and run the fp64
+    GEMM against pre-decoded weights.  Sample: a slice of the weight's output columns
+    (weights are encoded outside the timed part, like the GPU's pre-packed weights)."""
+    from oracle import gemm as G
+    from oracle import nvfp4 as Q
+    from workloads import bf16_to_f32
+    N, K = d16.N, d16.K
+    cols = 1536
+    wc, ws, wg, _ = Q.quantize(d16.w[:cols], np.float32(np.max(np.abs(d16.w))))
+    t_all, reps = 0.0, 0
+    while t_all < target_s and reps < 1000:
+        t0 = time.perf_counter()
+        w_hat = Q.dequantize(wc, ws, wg)
+        for M in Ms:
+            c, s, g, _ = Q.quantize(bf16_to_f32(d16.x_bits[:M]))
+            G.gemm_f64(Q.dequantize(c, s, g), w_hat)
+        t_all += time.perf_counter() - t0
+        reps += 1
+    per_step = t_all / reps * (N / cols)
+    return {"value": round(step_bytes / per_step / 1e9, 4), "unit": "GB/s", "cores": cpu_threads(),
+            "kind": "oracle",
+            "sample": f"{reps} oracle steps over {cols} of {N} output columns (all three token counts), "
+                      f"scaled by {N / cols:.1f} to the full step; {t_all:.1f} s of CPU time"}
+
+
+# ---------------------------------------------------------------------------------------
+GEMM_CONFIGS = {
+    "tiny": lambda W: W.tiny(),
+    "prefill_gate_up": lambda W: W.prefill_gate_up(),
+    "gdn_in_proj": lambda W: W.gdn_in_proj(),
+    "down_proj": lambda W: W.down_proj(),
+}
+
+
+def bench_gemm(args, torch, nv, W, dev):
+    d = GEMM_CONFIGS[args.config](W)
+    M, K, N = d.M, d.K, d.N
+    pw = nv.pack_weight(torch.from_numpy(d.w).to(dev), d.segments)
+    x = to_dev_bf16(torch, d.x_bits, dev)
+    c = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
+    s = torch.empty((M, K // 16), dtype=torch.uint8, device=dev)
+    g = torch.empty(1, dtype=torch.float32, device=dev)
+    out = torch.empty((M, N), dtype=torch.float32, device=dev)
+    ws = nv.Workspace(dev)
+    torch.cuda.synchronize()
+
+    def step(i):
+        nv.quantize_act(x, None, ws, out=(c, s, g))
+        nv.gemm(c, s, g, pw, out=out)
+
+    steps = max(1, args.steps)
+    sec, wall = time_region(torch, step, steps, min(args.warmup, 5))
+    flops = 2.0 * M * N * K
+    value = flops * steps / sec / 1e12
+    mean, med = kernel_time_pairs(torch, lambda i: nv.gemm(c, s, g, pw, out=out), max(8, steps // 2), 2)
+    achieved = flops / mean / 1e12
+    return {
+        "metric": "NVFP4 W4A4 prefill GEMM TFLOP/s (quantize + GEMM + epilogue), % of MI355X fp16 MFMA roofline",
+        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": steps, "warmup": min(args.warmup, 5),
+        "ms_per_step": round(sec / steps * 1e3, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f16",
+        "dtype_note": "NVFP4 operands decoded exactly to fp16, fp16 MFMA products, fp32 accumulation",
+        "data": "synthetic",
+        "config": {"workload": d.name, "M": M, "K": K, "N": N, "segments": len(d.segments),
+                   "gemm_kernel_mean_ms": round(mean * 1e3, 4), "gemm_kernel_median_ms": round(med * 1e3, 4)},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": F16_MFMA_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / F16_MFMA_PEAK_TFLOPS, 4), "traffic": None,
+                     "kernel": "gemm_mfma_kernel"},
+    }
+
+
+def bench_quantize(args, torch, nv, W, dev):
+    rng = np.random.default_rng(0)
+    M, K = 32768, 17408
+    x = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+    for r0 in range(0, M, 2048):
+        x[r0:r0 + 2048] = to_dev_bf16(torch, W.swiglu_rows(rng, 2048, K), dev)
+    c = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
+    s = torch.empty((M, K // 16), dtype=torch.uint8, device=dev)
+    g = torch.empty(1, dtype=torch.float32, device=dev)
+    ws = nv.Workspace(dev)
+    torch.cuda.synchronize()
+    sec, _ = time_region(torch, lambda i: nv.quantize_act(x, None, ws, out=(c, s, g)), args.steps, 3)
+    nbytes = M * K * (2 + 2 + 9 / 16)      # amax pass reads x, encode pass reads x and writes codes+scales
+    value = nbytes * args.steps / sec / 1e9
+    return {"metric": "NVFP4 activation quantize GB/s (dynamic scale), % of MI355X HBM roofline",
+            "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": 3,
+            "ms_per_step": round(sec / args.steps * 1e3, 4), "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+            "config": {"workload": "down_proj_activation_quantize_m32768_k17408"},
+            "roofline": {"bound": "hbm", "achieved": round(value, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(value / HBM_PEAK_GBS, 4), "traffic": None}}
+
+
+if __name__ == "__main__":
+    main()

@@ -72,28 +72,35 @@ typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 typedef float float16_t __attribute__((ext_vector_type(16)));
 
-// 8 E2M1 codes (one dword, low nibble first) times one E4M3 scale, as 8 exact
-// fp16 values.  cvt_scalef32_pk_f16_fp4 with scale 1.0 gives the E2M1 values
-// exactly; multiplying by the scale in fp16 is exact because every product of
-// an E2M1 magnitude and an E4M3 value has at most 6 significant bits and lies
-// in [2^-10, 2688], inside fp16's normal range.
-__device__ __forceinline__ half8_t decode8(uint32_t w, half2_t s2) {
-  half2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0);
-  half2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1);
-  half2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2);
-  half2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3);
-  p0 *= s2; p1 *= s2; p2 *= s2; p3 *= s2;
-  half8_t r;
-  r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
-  r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
-  return r;
+// Weight chunk layout (16 rows n x 128 k): the 16 code bytes holding row n's k
+// group g (k in [32g, 32g + 32)) sit at byte (g * 16 + n) * 16, the two scale
+// bytes of blocks 2g, 2g + 1 at byte (g * 16 + n) * 2.  Lane l = g * 16 + n of a
+// wave therefore reads bytes [16 l, 16 l + 16) of a chunk: one fully coalesced
+// 1 KB wave load that lands in the 16 x 16 x 32 MFMA operand layout.
+__host__ __device__ inline int64_t chunk_code_off(int n, int g) { return (int64_t)(g * kStrip + n) * 16; }
+__host__ __device__ inline int64_t chunk_scale_off(int n, int g) { return (int64_t)(g * kStrip + n) * 2; }
+
+// fp16 bit pattern (c << 7) read as an IEEE half is exactly E4M3(c) * 2^-8 for
+// every code 0..0x7E (normal codes map onto fp16 normals, E4M3 subnormals onto
+// fp16 subnormals).  scale_pair(c) puts that half in both lanes of a half2.
+__device__ __forceinline__ half2_t scale_pair(uint32_t c) {
+  const uint32_t b = (c & 0x7Fu) * 0x00800080u;           // (c << 7) | (c << 23)
+  return __builtin_bit_cast(half2_t, b);
 }
 
-// E4M3 scale byte -> fp16 pair (exact: every E4M3 value is an fp16 normal).
-__device__ __forceinline__ half2_t scale_h2(uint32_t c) {
-  const _Float16 h = (_Float16)e4m3_value(c & 0x7F);
-  half2_t r = {h, h};
-  return r;
+// 8 E2M1 codes (one dword, low nibble first) times one E4M3 scale as 8 exact
+// fp16 values.  The fp4 converter with scale 2^8 yields E2M1 * 256 exactly;
+// the packed fp16 multiply by E4M3 * 2^-8 then gives E2M1 * E4M3, exact because
+// every such product has at most 6 significant bits and lies in [2^-10, 2688],
+// inside fp16's normal range.
+__device__ __forceinline__ half8_t decode8(uint32_t w, half2_t s2) {
+  const half2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 256.0f, 0) * s2;
+  const half2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 256.0f, 1) * s2;
+  const half2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 256.0f, 2) * s2;
+  const half2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 256.0f, 3) * s2;
+  const auto lo = __builtin_shufflevector(p0, p1, 0, 1, 2, 3);
+  const auto hi = __builtin_shufflevector(p2, p3, 0, 1, 2, 3);
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
 }  // namespace nvfp4

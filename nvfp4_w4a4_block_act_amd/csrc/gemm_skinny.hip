@@ -27,117 +27,150 @@
 
 namespace nvfp4 {
 
-constexpr int kSkWaves = 4;
-constexpr int kSkThreads = 64 * kSkWaves;
-
-// 16 contiguous code bytes (32 elements) of activation row m starting at
-// element k0; zero past K.  `al16` says whether rows start 16-byte aligned.
-__device__ __forceinline__ uint4 load_act_codes(const uint8_t* __restrict__ a, int64_t m, int K, int k0,
-                                                bool al16) {
-  uint4 v = make_uint4(0u, 0u, 0u, 0u);
-  if (k0 >= K) return v;
-  const uint8_t* p = a + m * (K / 2) + k0 / 2;
-  if (k0 + 32 <= K) {
-    if (al16) {
-      v = *reinterpret_cast<const uint4*>(p);
-    } else {
-      const uint2 x0 = reinterpret_cast<const uint2*>(p)[0];
-      const uint2 x1 = reinterpret_cast<const uint2*>(p)[1];
-      v = make_uint4(x0.x, x0.y, x1.x, x1.y);
-    }
-  } else {  // k0 + 16 == K: the last block of the row
-    const uint2 x0 = *reinterpret_cast<const uint2*>(p);
-    v.x = x0.x;
-    v.y = x0.y;
+// Activation fragment of one lane for a full 128-k tile: row `row`, k in
+// [t * 128 + 32 g, + 32).  Codes are 16 bytes (one 16-byte load when rows are
+// 16-byte aligned, i.e. K % 32 == 0), scales two bytes.
+template <bool AL16>
+__device__ __forceinline__ void load_a_full(const uint8_t* __restrict__ ac, const uint8_t* __restrict__ as, int t,
+                                            uint4& v, uint32_t& sc) {
+  if constexpr (AL16) {
+    v = *reinterpret_cast<const uint4*>(ac + t * 64);
+    sc = *reinterpret_cast<const uint16_t*>(as + t * 8);
+  } else {
+    const uint2 x0 = reinterpret_cast<const uint2*>(ac + t * 64)[0];
+    const uint2 x1 = reinterpret_cast<const uint2*>(ac + t * 64)[1];
+    v = make_uint4(x0.x, x0.y, x1.x, x1.y);
+    sc = (uint32_t)as[t * 8] | ((uint32_t)as[t * 8 + 1] << 8);
   }
-  return v;
 }
 
-// Two scale bytes (blocks k0/16 and k0/16 + 1) of activation row m; zero past K.
-__device__ __forceinline__ uint32_t load_act_scales(const uint8_t* __restrict__ s, int64_t m, int K, int k0) {
-  if (k0 >= K) return 0u;
-  const uint8_t* p = s + m * (K / kBlock) + k0 / kBlock;
-  uint32_t r = p[0];
-  if (k0 + 16 < K) r |= (uint32_t)p[1] << 8;
-  return r;
+// Same for the ragged last tile (K % 128 != 0): zero past K (K % 16 == 0).
+__device__ __forceinline__ void load_a_tail(const uint8_t* __restrict__ ac, const uint8_t* __restrict__ as, int t,
+                                            int k0, int K, uint4& v, uint32_t& sc) {
+  v = make_uint4(0u, 0u, 0u, 0u);
+  sc = 0u;
+  if (k0 >= K) return;
+  const uint2 x0 = reinterpret_cast<const uint2*>(ac + t * 64)[0];
+  v.x = x0.x;
+  v.y = x0.y;
+  sc = as[t * 8];
+  if (k0 + 16 < K) {
+    const uint2 x1 = reinterpret_cast<const uint2*>(ac + t * 64)[1];
+    v.z = x1.x;
+    v.w = x1.y;
+    sc |= (uint32_t)as[t * 8 + 1] << 8;
+  }
 }
 
-template <int SW, int U>
-__global__ __launch_bounds__(kSkThreads) void gemm_skinny_kernel(
+// One 128-k tile for one strip: four 16x16x32 MFMAs on exactly decoded operands.
+__device__ __forceinline__ void tile_mfma(const half8_t (&A)[4], uint4 w, uint32_t wsc, float4_t& acc) {
+  const half2_t s0 = scale_pair(wsc & 0xFF), s1 = scale_pair(wsc >> 8);
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[0], decode8(w.x, s0), acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[1], decode8(w.y, s0), acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[2], decode8(w.z, s1), acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[3], decode8(w.w, s1), acc, 0, 0, 0);
+}
+
+__device__ __forceinline__ void decode_a(uint4 v, uint32_t sc, uint32_t amask, half8_t (&A)[4]) {
+  sc &= amask;                    // padded rows (m >= M) decode to zeros
+  const half2_t s0 = scale_pair(sc & 0xFF), s1 = scale_pair(sc >> 8);
+  A[0] = decode8(v.x, s0);
+  A[1] = decode8(v.y, s0);
+  A[2] = decode8(v.z, s1);
+  A[3] = decode8(v.w, s1);
+}
+
+// S strips of 16 columns per workgroup, NW waves splitting the k tiles
+// (wave w takes tiles w, w + NW, ...), U tiles per load batch.
+template <int S, int NW, int U, bool AL16>
+__global__ __launch_bounds__(64 * NW) void gemm_skinny_kernel(
     const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales, const float* __restrict__ a_g,
     int M, int K, const uint8_t* __restrict__ w_codes, const uint8_t* __restrict__ w_scales, int N,
     SegTable st, const float* __restrict__ w_g, float* __restrict__ out, int64_t ldo) {
-  __shared__ float red[kSkWaves][SW][4][64];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __shared__ float red[NW][S][4][64];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = lane & 15, g = lane >> 4;
-  const int tiles = (K + kTileK - 1) / kTileK;
+  const int tiles = (K + kTileK - 1) / kTileK;       // tiles of the packed weight
+  const int full = K / kTileK;                       // tiles with no k tail
   const int nstrips = (N + kStrip - 1) / kStrip;
-  const int strip0 = blockIdx.x * SW;
-  const bool arow = r < M;
-  const bool al16 = (K % 32) == 0;
+  const int strip0 = blockIdx.x * S;
 
-  float4_t acc[SW];
+  // A: row r (clamped; padded rows are zeroed through their scale)
+  const int arow = min(r, M - 1);
+  const uint32_t amask = (r < M) ? 0xFFFFu : 0u;
+  const uint8_t* ac = a_codes + (int64_t)arow * (K / 2) + g * 16;
+  const uint8_t* as = a_scales + (int64_t)arow * (K / kBlock) + g * 2;
+  // W: strip pointers (clamped; columns past N are never stored)
+  const uint8_t* wc[S];
+  const uint8_t* ws[S];
 #pragma unroll
-  for (int s = 0; s < SW; ++s) acc[s] = float4_t{0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < S; ++s) {
+    const int64_t strip = min(strip0 + s, nstrips - 1);
+    wc[s] = w_codes + strip * tiles * kChunkCodes + lane * 16;
+    ws[s] = w_scales + strip * tiles * kChunkScales + lane * 2;
+  }
 
-  for (int t0 = wave; t0 < tiles; t0 += kSkWaves * U) {
-    uint4 av[U], wv[U][SW];
-    uint32_t as[U], ws[U][SW];
-    // issue every load of this batch first
+  float4_t acc[S];
+#pragma unroll
+  for (int s = 0; s < S; ++s) acc[s] = float4_t{0.f, 0.f, 0.f, 0.f};
+
+  // Batches of U tiles; every load of a batch is issued before any decode, and the
+  // batch has no branches (tiles past the end are clamped and their activation
+  // scales zeroed), so the waits before each tile's MFMAs stay progressive.
+  for (int t0 = wave; t0 < full; t0 += NW * U) {
+    uint4 av[U], wv[U][S];
+    uint32_t asc[U], wsc[U][S];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int t = t0 + u * kSkWaves;
-      const int k0 = t * kTileK + 32 * g;
-      const bool tv = t < tiles;
-      av[u] = (tv && arow) ? load_act_codes(a_codes, r, K, k0, al16) : make_uint4(0u, 0u, 0u, 0u);
-      as[u] = (tv && arow) ? load_act_scales(a_scales, r, K, k0) : 0u;
+      const int t = min(t0 + u * NW, full - 1);
+      load_a_full<AL16>(ac, as, t, av[u], asc[u]);
 #pragma unroll
-      for (int s = 0; s < SW; ++s) {
-        const int strip = strip0 + s;
-        if (tv && strip < nstrips) {
-          const int64_t chunk = (int64_t)strip * tiles + t;
-          wv[u][s] = *reinterpret_cast<const uint4*>(w_codes + chunk * kChunkCodes + r * 64 + g * 16);
-          ws[u][s] = *reinterpret_cast<const uint16_t*>(w_scales + chunk * kChunkScales + r * 8 + g * 2);
-        } else {
-          wv[u][s] = make_uint4(0u, 0u, 0u, 0u);
-          ws[u][s] = 0u;
-        }
+      for (int s = 0; s < S; ++s) {
+        wv[u][s] = *reinterpret_cast<const uint4*>(wc[s] + (int64_t)t * kChunkCodes);
+        wsc[u][s] = *reinterpret_cast<const uint16_t*>(ws[s] + (int64_t)t * kChunkScales);
       }
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const half2_t sa0 = scale_h2(as[u] & 0xFF), sa1 = scale_h2(as[u] >> 8);
-      const half8_t A0 = decode8(av[u].x, sa0), A1 = decode8(av[u].y, sa0);
-      const half8_t A2 = decode8(av[u].z, sa1), A3 = decode8(av[u].w, sa1);
+      const uint32_t live = (t0 + u * NW < full) ? amask : 0u;
+      half8_t A[4];
+      decode_a(av[u], asc[u], live, A);
 #pragma unroll
-      for (int s = 0; s < SW; ++s) {
-        const half2_t sb0 = scale_h2(ws[u][s] & 0xFF), sb1 = scale_h2(ws[u][s] >> 8);
-        acc[s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A0, decode8(wv[u][s].x, sb0), acc[s], 0, 0, 0);
-        acc[s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A1, decode8(wv[u][s].y, sb0), acc[s], 0, 0, 0);
-        acc[s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A2, decode8(wv[u][s].z, sb1), acc[s], 0, 0, 0);
-        acc[s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A3, decode8(wv[u][s].w, sb1), acc[s], 0, 0, 0);
-      }
+      for (int s = 0; s < S; ++s) tile_mfma(A, wv[u][s], wsc[u][s], acc[s]);
+    }
+  }
+  if (full < tiles && wave == full % NW) {           // ragged last tile
+    const int t = full;
+    uint4 v;
+    uint32_t sc;
+    load_a_tail(ac, as, t, t * kTileK + 32 * g, K, v, sc);
+    half8_t A[4];
+    decode_a(v, sc, amask, A);
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      const uint4 w = *reinterpret_cast<const uint4*>(wc[s] + (int64_t)t * kChunkCodes);
+      const uint32_t wsv = *reinterpret_cast<const uint16_t*>(ws[s] + (int64_t)t * kChunkScales);
+      tile_mfma(A, w, wsv, acc[s]);
     }
   }
 
 #pragma unroll
-  for (int s = 0; s < SW; ++s)
+  for (int s = 0; s < S; ++s)
 #pragma unroll
     for (int i = 0; i < 4; ++i) red[wave][s][i][lane] = acc[s][i];
   __syncthreads();
 
-  // thread -> (i, l): output row 4 * (l / 16) + i, column l % 16 of each strip
-  const int i = threadIdx.x >> 6, l = threadIdx.x & 63;
-  const int row = 4 * (l >> 4) + i;
-  if (row >= M) return;
+  // output element e = (s, i, l): row 4 * (l / 16) + i, column (strip0 + s) * 16 + l % 16
   const float ag = *a_g;
-#pragma unroll
-  for (int s = 0; s < SW; ++s) {
+  for (int e = threadIdx.x; e < S * 256; e += 64 * NW) {
+    const int s = e >> 8, i = (e >> 6) & 3, l = e & 63;
+    const int row = 4 * (l >> 4) + i;
     const int n = (strip0 + s) * kStrip + (l & 15);
-    if (n >= N) continue;
+    if (row >= M || n >= N) continue;
     float v = 0.f;
 #pragma unroll
-    for (int w = 0; w < kSkWaves; ++w) v += red[w][s][i][l];
+    for (int w = 0; w < NW; ++w) v += red[w][s][i][l];
     out[(int64_t)row * ldo + n] = v * (ag * w_g[seg_of(st, n)]);
   }
 }
@@ -159,11 +192,15 @@ hipError_t launch_gemm_skinny(const uint8_t* a_codes, const uint8_t* a_scales, c
                               int K, const uint8_t* w_codes, const uint8_t* w_scales, int N,
                               const SegTable& st, const float* w_g, float* out, int64_t ldo,
                               hipStream_t stream) {
-  constexpr int SW = 2, U = 5;
+  constexpr int S = 3, NW = 8, U = 5;
   const int nstrips = (N + kStrip - 1) / kStrip;
-  const int grid = (nstrips + SW - 1) / SW;
-  gemm_skinny_kernel<SW, U><<<grid, kSkThreads, 0, stream>>>(a_codes, a_scales, a_g, M, K, w_codes, w_scales,
-                                                             N, st, w_g, out, ldo);
+  const int grid = (nstrips + S - 1) / S;
+  if (K % 32 == 0)
+    gemm_skinny_kernel<S, NW, U, true><<<grid, 64 * NW, 0, stream>>>(a_codes, a_scales, a_g, M, K, w_codes,
+                                                                      w_scales, N, st, w_g, out, ldo);
+  else
+    gemm_skinny_kernel<S, NW, U, false><<<grid, 64 * NW, 0, stream>>>(a_codes, a_scales, a_g, M, K, w_codes,
+                                                                       w_scales, N, st, w_g, out, ldo);
   return hipGetLastError();
 }
 

@@ -19,7 +19,8 @@
 //    workgroup into the workspace and the encoder reduces them in its prologue
 //    (exact, order-independent, no atomics, no memset);
 //  * small tensors (decode-sized activations) use a single launch in which
-//    every workgroup recomputes the whole-tensor maximum from L2.
+//    every 1024-thread workgroup recomputes the whole-tensor maximum from L2
+//    with all of its loads in flight at once.
 #include <algorithm>
 
 #include "common.hpp"
@@ -28,7 +29,7 @@ namespace nvfp4 {
 
 constexpr int kQThreads = 256;
 constexpr int kPartials = 1024;              // amax workgroups in the two-pass path
-constexpr int64_t kSmallElems = 1 << 18;     // single-launch path up to 256K elements
+constexpr int64_t kSmallElems = 1 << 17;     // single-launch path up to 128K elements
 
 // ---- block encoder ------------------------------------------------------------
 // x: the 16 values of one block as binary32 (exactly widened), bmax = max|x|.
@@ -69,14 +70,9 @@ __device__ __forceinline__ float g_enc_of(float amax) {
   return (amax == 0.0f) ? 0.0f : kGMax / amax;
 }
 
-// Encode the bf16 block (m, b) of x.
-__device__ __forceinline__ void encode_bf16_block(const uint16_t* __restrict__ x, int64_t ldx, int K,
-                                                  int64_t m, int b, float g_enc,
-                                                  uint8_t* __restrict__ codes,
-                                                  uint8_t* __restrict__ scales) {
-  const uint4* p = reinterpret_cast<const uint4*>(x + m * ldx + (int64_t)b * kBlock);
-  const uint4 v0 = p[0];
-  const uint4 v1 = p[1];
+// Encode one bf16 block given as two 16-byte chunks; writes 8 code bytes and 1 scale.
+__device__ __forceinline__ void encode_bf16_chunks(uint4 v0, uint4 v1, float g_enc, uint8_t* __restrict__ code_dst,
+                                                   uint8_t* __restrict__ scale_dst) {
   const uint32_t d[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
   float xf[16];
   uint32_t mb = 0;
@@ -88,8 +84,17 @@ __device__ __forceinline__ void encode_bf16_block(const uint16_t* __restrict__ x
   }
   uint2 c;
   const uint32_t sc = encode_block(xf, __uint_as_float(mb << 16), g_enc, c);
-  *reinterpret_cast<uint2*>(codes + m * (K / 2) + (int64_t)b * 8) = c;
-  scales[m * (K / kBlock) + b] = (uint8_t)sc;
+  *reinterpret_cast<uint2*>(code_dst) = c;
+  *scale_dst = (uint8_t)sc;
+}
+
+// Encode the bf16 block (m, b) of x.
+__device__ __forceinline__ void encode_bf16_block(const uint16_t* __restrict__ x, int64_t ldx, int K,
+                                                  int64_t m, int b, float g_enc,
+                                                  uint8_t* __restrict__ codes,
+                                                  uint8_t* __restrict__ scales) {
+  const uint4* p = reinterpret_cast<const uint4*>(x + m * ldx + (int64_t)b * kBlock);
+  encode_bf16_chunks(p[0], p[1], g_enc, codes + m * (K / 2) + (int64_t)b * 8, scales + m * (K / kBlock) + b);
 }
 
 // ---- whole-tensor |x| maximum on bf16 bit patterns ------------------------------
@@ -133,8 +138,7 @@ __global__ __launch_bounds__(kQThreads) void amax_partial_kernel(const uint16_t*
   if (threadIdx.x == 0) partial[blockIdx.x] = r;
 }
 
-// mode 0: amax from `partial` (nparts values); mode 1: amax from *amax_in;
-// mode 2: every workgroup computes the whole-tensor maximum itself.
+// mode 0: amax from `partial` (nparts values); mode 1: amax from *amax_in.
 __global__ __launch_bounds__(kQThreads) void quantize_act_kernel(
     const uint16_t* __restrict__ x, int64_t M, int K, int64_t ldx, int mode,
     const uint32_t* __restrict__ partial, int nparts, const float* __restrict__ amax_in,
@@ -145,11 +149,7 @@ __global__ __launch_bounds__(kQThreads) void quantize_act_kernel(
     amax = *amax_in;
   } else {
     uint32_t m = 0;
-    if (mode == 0) {
-      for (int i = threadIdx.x; i < nparts; i += blockDim.x) m = max(m, partial[i]);
-    } else {
-      m = chunk_absmax(x, ldx, K, M, threadIdx.x, blockDim.x);
-    }
+    for (int i = threadIdx.x; i < nparts; i += blockDim.x) m = max(m, partial[i]);
     amax = __uint_as_float(block_reduce_max(m, red) << 16);
   }
   const float g_enc = g_enc_of(amax);
@@ -162,6 +162,61 @@ __global__ __launch_bounds__(kQThreads) void quantize_act_kernel(
     const int64_t m = i / nb;
     const int b = (int)(i - m * nb);
     encode_bf16_block(x, ldx, K, m, b, g_enc, codes, scales);
+  }
+}
+
+// Decode-sized tensors (M * K <= kSmallElems): one launch, at most 8 workgroups
+// of 1024 threads.  Thread t of workgroup b encodes block i = 1024 b + t, whose
+// two 16-byte chunks are chunks 2i and 2i + 1 of the row-major chunk order.
+// Every workgroup reads the whole tensor once for the maximum, all loads in
+// flight at once: thread t takes chunk slots (2048 b + 2t + h + 2048 j) mod
+// 16384 for h = 0, 1 and j = 0..7, which cover every slot and start with its
+// own block, so the encode step needs no second load.
+constexpr int kSmallThreads = 1024;
+constexpr int kSmallSlots = 16384;                  // chunks of 8 elements
+
+__global__ __launch_bounds__(kSmallThreads) void quantize_act_small_kernel(
+    const uint16_t* __restrict__ x, int M, int K, int64_t ldx, float inv_cpr, uint8_t* __restrict__ codes,
+    uint8_t* __restrict__ scales, float* __restrict__ g_dec_out) {
+  __shared__ uint32_t red[kSmallThreads / 64];
+  const int cpr = K / 8;
+  const int total = M * cpr;
+  uint4 v[16];
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int c = (2048 * (int)blockIdx.x + 2 * (int)threadIdx.x + h + 2048 * j) & (kSmallSlots - 1);
+      uint4 val = make_uint4(0u, 0u, 0u, 0u);
+      if (c < total) {
+        // c / cpr via a float reciprocal, corrected to exact (c < 2^24)
+        int r = (int)((float)c * inv_cpr);
+        int k = c - r * cpr;
+        if (k < 0) { --r; k += cpr; }
+        if (k >= cpr) { ++r; k -= cpr; }
+        val = *reinterpret_cast<const uint4*>(x + (int64_t)r * ldx + (int64_t)k * 8);
+      }
+      v[2 * j + h] = val;
+    }
+  uint32_t m = 0;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    // per 16-bit half: a packed pair must not be compared as one 32-bit word
+    const uint32_t a0 = max(v[j].x & 0x7FFFu, (v[j].x >> 16) & 0x7FFFu);
+    const uint32_t a1 = max(v[j].y & 0x7FFFu, (v[j].y >> 16) & 0x7FFFu);
+    const uint32_t a2 = max(v[j].z & 0x7FFFu, (v[j].z >> 16) & 0x7FFFu);
+    const uint32_t a3 = max(v[j].w & 0x7FFFu, (v[j].w >> 16) & 0x7FFFu);
+    m = max(m, max(max(a0, a1), max(a2, a3)));
+  }
+  const float amax = __uint_as_float(block_reduce_max(m, red) << 16);
+  const float g_enc = g_enc_of(amax);
+  if (blockIdx.x == 0 && threadIdx.x == 0) *g_dec_out = amax / kGMax;
+  const int nb = K / kBlock;
+  const int i = blockIdx.x * kSmallThreads + threadIdx.x;
+  if (i < M * nb) {
+    const int row = i / nb, b = i - row * nb;
+    encode_bf16_chunks(v[0], v[1], g_enc, codes + (int64_t)row * (K / 2) + (int64_t)b * 8,
+                       scales + (int64_t)row * nb + b);
   }
 }
 
@@ -188,9 +243,9 @@ hipError_t launch_quantize_act(const uint16_t* x, int64_t M, int64_t K, int64_t 
     quantize_act_kernel<<<grid, kQThreads, 0, stream>>>(x, M, (int)K, ldx, 1, nullptr, 0, amax_in,
                                                         codes, scales, g_dec_out);
   } else if (M * K <= kSmallElems) {
-    const int grid = (int)std::min<int64_t>(want, 64);
-    quantize_act_kernel<<<grid, kQThreads, 0, stream>>>(x, M, (int)K, ldx, 2, nullptr, 0, nullptr,
-                                                        codes, scales, g_dec_out);
+    const int grid = (int)((blocks + kSmallThreads - 1) / kSmallThreads);
+    quantize_act_small_kernel<<<grid, kSmallThreads, 0, stream>>>(x, (int)M, (int)K, ldx, 1.0f / (float)(K / 8),
+                                                                   codes, scales, g_dec_out);
   } else {
     uint32_t* partial = static_cast<uint32_t*>(workspace);
     const int64_t chunks = M * (K / 8);
@@ -260,9 +315,9 @@ __global__ __launch_bounds__(kQThreads) void pack_weight_kernel(
       sc = encode_block(xf, bmax, s_genc[seg_of(st, n)], c);
     }
     const int64_t chunk = (int64_t)(n / kStrip) * tiles + b / (kTileK / kBlock);
-    const int r = n % kStrip, bb = b % (kTileK / kBlock);
-    *reinterpret_cast<uint2*>(w_codes + chunk * kChunkCodes + r * (kTileK / 2) + bb * 8) = c;
-    w_scales[chunk * kChunkScales + r * (kTileK / kBlock) + bb] = (uint8_t)sc;
+    const int r = n % kStrip, bb = b % (kTileK / kBlock);   // block bb of the chunk: group bb / 2
+    *reinterpret_cast<uint2*>(w_codes + chunk * kChunkCodes + chunk_code_off(r, bb >> 1) + (bb & 1) * 8) = c;
+    w_scales[chunk * kChunkScales + chunk_scale_off(r, bb >> 1) + (bb & 1)] = (uint8_t)sc;
   }
 }
 
@@ -278,9 +333,10 @@ __global__ __launch_bounds__(kQThreads) void weight_to_canonical_kernel(
     const int b = (int)(i - (int64_t)n * nb);
     const int64_t chunk = (int64_t)(n / kStrip) * tiles + b / (kTileK / kBlock);
     const int r = n % kStrip, bb = b % (kTileK / kBlock);
-    const uint2 c = *reinterpret_cast<const uint2*>(w_codes + chunk * kChunkCodes + r * (kTileK / 2) + bb * 8);
+    const uint2 c = *reinterpret_cast<const uint2*>(w_codes + chunk * kChunkCodes + chunk_code_off(r, bb >> 1) +
+                                                    (bb & 1) * 8);
     *reinterpret_cast<uint2*>(codes + (int64_t)n * (K / 2) + (int64_t)b * 8) = c;
-    scales[(int64_t)n * nb + b] = w_scales[chunk * kChunkScales + r * (kTileK / kBlock) + bb];
+    scales[(int64_t)n * nb + b] = w_scales[chunk * kChunkScales + chunk_scale_off(r, bb >> 1) + (bb & 1)];
   }
 }
 

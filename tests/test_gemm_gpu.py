@@ -52,7 +52,8 @@ def test_pack_ragged(N, K, segs):
 
 
 def test_pack_layout_is_the_documented_tiling():
-    """Tiled buffer = canonical codes/scales re-blocked into 16-row x 128-k chunks, strip major."""
+    """Tiled buffer = canonical codes/scales re-blocked into 16-row x 128-k chunks, strip major;
+    inside a chunk the 16 code bytes (2 scale bytes) of row n, k group g sit at slot g * 16 + n."""
     rng = np.random.default_rng(3)
     N, K = 40, 272
     w = (0.02 * rng.standard_normal((N, K))).astype(np.float32)
@@ -62,8 +63,8 @@ def test_pack_layout_is_the_documented_tiling():
     cpad[:N, :K // 2] = oc
     spad = np.zeros((Np, Kp // 16), np.uint8)
     spad[:N, :K // 16] = os_
-    ct = cpad.reshape(Np // 16, 16, Kp // 128, 64).transpose(0, 2, 1, 3).ravel()
-    st = spad.reshape(Np // 16, 16, Kp // 128, 8).transpose(0, 2, 1, 3).ravel()
+    ct = cpad.reshape(Np // 16, 16, Kp // 128, 4, 16).transpose(0, 2, 3, 1, 4).ravel()
+    st = spad.reshape(Np // 16, 16, Kp // 128, 4, 2).transpose(0, 2, 3, 1, 4).ravel()
     assert np.array_equal(pw.codes.cpu().numpy(), ct)
     assert np.array_equal(pw.scales.cpu().numpy(), st)
 
@@ -97,6 +98,7 @@ def test_gemm_decode_full(M):
 @pytest.mark.parametrize("M,N,K,nseg", [
     (1, 16, 16, 1), (2, 37, 48, 2), (5, 200, 272, 3), (16, 129, 144, 2), (17, 16, 16, 1),
     (17, 130, 144, 3), (33, 300, 5136, 4), (130, 257, 400, 5), (256, 128, 256, 1), (300, 520, 1040, 16),
+    (64, 100, 320, 2), (40, 64, 192, 1), (9, 70, 320, 2), (513, 300, 128, 3),
 ])
 def test_gemm_ragged(M, N, K, nseg):
     rng = np.random.default_rng(M * 1000 + N + K)
@@ -107,6 +109,25 @@ def test_gemm_ragged(M, N, K, nseg):
                         for i, (b, e) in enumerate(segs)])
     x = W.random_act(M + N, M, K, "student_t")
     check_linear(x, w, segs, f"ragged M={M} N={N} K={K}")
+
+
+@pytest.mark.parametrize("M", [7, 300])
+def test_gemm_subnormal_block_scales(M):
+    """Blocks 10^0 .. 10^-6 below the tensor maximum get E4M3 subnormal (or zero) scales
+    on both operands; their decoded values must still be exact in the GEMM."""
+    rng = np.random.default_rng(90 + M)
+    K, N = 512, 96
+    x = rng.standard_normal((M, K)).astype(np.float32)
+    x *= (10.0 ** -rng.integers(0, 7, size=(M, K // 16))).repeat(16, axis=1).astype(np.float32)
+    x[0, 0] = 50.0
+    w = (0.02 * rng.standard_normal((N, K))).astype(np.float32)
+    w *= (10.0 ** -rng.integers(0, 7, size=(N, K // 16))).repeat(16, axis=1).astype(np.float32)
+    w[0, 0] = 1.0
+    from workloads import bf16_bits
+    xb = bf16_bits(x)
+    sc = Q.quantize(W.bf16_to_f32(xb))[1]
+    assert np.any((sc > 0) & (sc < 8)), "no subnormal activation scales"
+    check_linear(xb, w, [(0, 40), (40, N)], f"subnormal scales M={M}")
 
 
 def test_gemm_k_zero_and_m_zero():

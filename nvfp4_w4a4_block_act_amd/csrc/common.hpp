@@ -103,6 +103,10 @@ __device__ __forceinline__ half8_t decode8(uint32_t w, half2_t s2) {
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
+__device__ __forceinline__ uint32_t u4_dword_sel(uint4 v, int d) {
+  return d == 0 ? v.x : d == 1 ? v.y : d == 2 ? v.z : v.w;
+}
+
 }  // namespace nvfp4
 
 // ---- host-side launchers (one per kernel family), defined in the .hip files --

@@ -14,16 +14,24 @@
 // Tiling (512 threads, 256 x 256 output tile, k tile 128):
 //  * eight waves in a 4 (M) x 2 (N) grid, each owning 64 x 128 = 2 x 4 MFMA
 //    32x32x16 tiles (128 fp32 accumulators per lane);
-//  * activations are decoded straight into MFMA operand registers by the wave
-//    that uses them: under a K-permutation shared by both operands (MFMA step
-//    j of a tile takes k = 64 h + 8 j + e for lane group h = lane / 32), each
-//    lane's operand bytes are 32 contiguous bytes of a canonical row, loaded
-//    one k tile ahead;
-//  * weights (shared by the four M-waves) are loaded two k tiles ahead as
-//    fully coalesced 1 KB chunk reads, decoded once per workgroup to fp16 and
-//    written to a double-buffered LDS tile (row stride 272 bytes: the 16-byte
-//    operand reads of 16 consecutive lanes hit distinct banks); the decode of
-//    tile t + 1 is interleaved with the MFMAs of tile t;
+//  * K-permutation shared by both operands: MFMA step j of a tile takes
+//    k = 64 h + 8 j + e for lane group h = lane / 32, so a lane's activation
+//    operand for a step is one dword of canonical codes and its weight operand
+//    one 16-byte piece of a decoded row;
+//  * activation codes: 16 KB per k tile loaded coalesced (four lanes per
+//    64-byte row segment) into registers, written one tile later to a
+//    double-buffered LDS tile, read back by the wave that needs them and
+//    decoded to fp16 in registers; their scales go straight to the lanes;
+//  * weights (shared by the four M-waves): coalesced chunk reads, loaded two k
+//    tiles ahead, decoded once per workgroup to fp16 into double-buffered LDS
+//    half-tiles (64 k each: MFMA steps 0-3 use k groups 0 and 2 of a chunk,
+//    steps 4-7 groups 1 and 3); the decode of the next half-tile is
+//    interleaved with the MFMAs of the current one.  Rows are padded to 144
+//    bytes, so the 16-byte operand reads of 16 consecutive lanes hit distinct
+//    banks and each step's reads are constant offsets from one base;
+//  * the activation tile is XOR-swizzled at 16-byte granularity (piece p of row
+//    r at p ^ ((r >> 1 ^ r >> 2) & 3)) so its coalesced writes and its operand
+//    reads are bank-conflict free without padding;
 //  * workgroups are numbered XCD-major, then in groups of four row panels, so
 //    the 32 workgroups resident on an XCD share one activation slab in its L2
 //    while they stream weight column panels.
@@ -33,80 +41,139 @@ namespace nvfp4 {
 
 constexpr int kBM = 256, kBN = 256;
 constexpr int kMfWaves = 8, kMfThreads = 64 * kMfWaves;
-constexpr int kLdsRow = kTileK + 8;                  // halfs per LDS row
 constexpr int kGroupM = 4;
+constexpr int kHalfRow = 9;                            // uint4 pieces per LDS weight row (8 + 1 pad)
 
-struct RawA {                                          // one lane's activation bytes for one k tile
-  uint4 c[2][2];                                       // [row tile][16-byte half]
-  uint32_t s[2];                                       // 4 scale bytes per row tile
+__device__ __forceinline__ int swz_a(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
+
+// Per-thread coalesced activation slots: slot q = tid + 512 s covers row q / 4
+// of the tile and its 16-byte piece q % 4.
+struct ASlots {
+  const uint8_t* p[2];
+  int lds[2];                                          // uint4 index inside an LDS stage
+  int koff[2];                                         // k offset of the piece inside a tile
 };
 
-struct RawW {                                          // one thread's two weight slots for one k tile
+template <bool AL16, bool TAIL>
+__device__ __forceinline__ void load_a_codes(const ASlots& as, int t, int full, int K, uint4 (&r)[2]) {
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    const uint8_t* p = as.p[s] + (int64_t)t * 64;
+    if (TAIL && t == full) {
+      const int k0 = t * kTileK + as.koff[s];
+      uint4 v = make_uint4(0u, 0u, 0u, 0u);
+      if (k0 < K) {
+        const uint2 x0 = reinterpret_cast<const uint2*>(p)[0];
+        v.x = x0.x;
+        v.y = x0.y;
+        if (k0 + 16 < K) {
+          const uint2 x1 = reinterpret_cast<const uint2*>(p)[1];
+          v.z = x1.x;
+          v.w = x1.y;
+        }
+      }
+      r[s] = v;
+    } else if (AL16) {
+      r[s] = *reinterpret_cast<const uint4*>(p);
+    } else {
+      const uint2 x0 = reinterpret_cast<const uint2*>(p)[0], x1 = reinterpret_cast<const uint2*>(p)[1];
+      r[s] = make_uint4(x0.x, x0.y, x1.x, x1.y);
+    }
+  }
+}
+
+// A lane's four scale bytes (blocks 4h .. 4h + 3 of the tile) for each row tile.
+template <bool AL4, bool TAIL>
+__device__ __forceinline__ void load_a_scales(const uint8_t* const (&sp)[2], int t, int full, int kbase, int K,
+                                              uint32_t (&r)[2]) {
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt) {
+    const uint8_t* q = sp[rt] + (int64_t)t * 8;
+    if (TAIL && t == full) {
+      uint32_t v = 0;
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+        if (kbase + 16 * b < K) v |= (uint32_t)q[b] << (8 * b);
+      r[rt] = v;
+    } else if (AL4) {
+      r[rt] = *reinterpret_cast<const uint32_t*>(q);
+    } else {
+      r[rt] = (uint32_t)q[0] | ((uint32_t)q[1] << 8) | ((uint32_t)q[2] << 16) | ((uint32_t)q[3] << 24);
+    }
+  }
+}
+
+// Weight slots: thread tid owns chunk row n = tid % 16 of strip tid / 32 and the
+// k groups g = 2 * ((tid / 16) % 2) + s for s = 0, 1; slot s is decoded into the
+// half-tile s (groups 0 and 2 feed MFMA steps 0-3, groups 1 and 3 steps 4-7).
+struct WSlots {
+  const uint8_t* wp[2];
+  const uint8_t* wsp[2];
+  int lds;                                             // uint4 index of this thread's row + piece 4 * (g / 2)
+};
+
+struct RawW {
   uint4 c[2];
   uint32_t s[2];
 };
 
-template <bool AL>
-__device__ __forceinline__ void load_a_tile(const uint8_t* const (&ap)[2], const uint8_t* const (&asp)[2], int t,
-                                            RawA& r) {
+__device__ __forceinline__ void load_w_tile(const WSlots& ws, int t, RawW& r) {
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    r.c[s] = *reinterpret_cast<const uint4*>(ws.wp[s] + (int64_t)t * kChunkCodes);
+    r.s[s] = *reinterpret_cast<const uint16_t*>(ws.wsp[s] + (int64_t)t * kChunkScales);
+  }
+}
+
+// Decode dword d of slot s (one 8-element piece) into its half-tile stage.
+__device__ __forceinline__ void store_w_piece(const WSlots& ws, const RawW& r, int s, int d, uint4* stage) {
+  const uint32_t sc = (d < 2) ? (r.s[s] & 0xFF) : ((r.s[s] >> 8) & 0xFF);
+  const uint32_t w = u4_dword_sel(r.c[s], d);
+  stage[ws.lds + d] = __builtin_bit_cast(uint4, decode8(w, scale_pair(sc)));
+}
+
+// Four MFMA steps (one half-tile, global steps 4 * HALF .. 4 * HALF + 3) on the
+// activation codes of LDS stage `sa` and the decoded weights of half-stage `sw`,
+// while one weight piece per step of the next half-tile is decoded into `sw_next`.
+template <int HALF>
+__device__ __forceinline__ void mfma_half(const uint4* sa, const uint4* sw, const uint32_t (&asc)[2],
+                                          const uint32_t (&amask)[2], int arow0, int bbase, int h,
+                                          const WSlots& ws, const RawW& wstore, int wslot, uint4* sw_next,
+                                          float16_t (&acc)[2][4]) {
+  uint4 araw[2];
 #pragma unroll
   for (int rt = 0; rt < 2; ++rt) {
-    const uint8_t* p = ap[rt] + (int64_t)t * 64;
-    const uint8_t* q = asp[rt] + (int64_t)t * 8;
-    if constexpr (AL) {
-      r.c[rt][0] = reinterpret_cast<const uint4*>(p)[0];
-      r.c[rt][1] = reinterpret_cast<const uint4*>(p)[1];
-      r.s[rt] = *reinterpret_cast<const uint32_t*>(q);
-    } else {
-      const uint2* p2 = reinterpret_cast<const uint2*>(p);
-      const uint2 x0 = p2[0], x1 = p2[1], x2 = p2[2], x3 = p2[3];
-      r.c[rt][0] = make_uint4(x0.x, x0.y, x1.x, x1.y);
-      r.c[rt][1] = make_uint4(x2.x, x2.y, x3.x, x3.y);
-      r.s[rt] = (uint32_t)q[0] | ((uint32_t)q[1] << 8) | ((uint32_t)q[2] << 16) | ((uint32_t)q[3] << 24);
-    }
+    const int r = arow0 + 32 * rt;
+    araw[rt] = sa[r * 4 + ((2 * h + HALF) ^ swz_a(r))];
   }
-}
-
-// Ragged last tile: per 16-element block, load only blocks that start before K.
-__device__ __forceinline__ void load_a_tail(const uint8_t* const (&ap)[2], const uint8_t* const (&asp)[2], int t,
-                                            int kbase, int K, RawA& r) {
 #pragma unroll
-  for (int rt = 0; rt < 2; ++rt) {
-    const uint8_t* p = ap[rt] + (int64_t)t * 64;
-    const uint8_t* q = asp[rt] + (int64_t)t * 8;
-    uint32_t d[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
-    uint32_t s = 0;
+  for (int jj = 0; jj < 4; ++jj) {
+    const int j = 4 * HALF + jj;
+    half8_t af[2], bf[4];
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      if (kbase + 16 * b < K) {
-        const uint2 x = reinterpret_cast<const uint2*>(p)[b];
-        d[2 * b] = x.x;
-        d[2 * b + 1] = x.y;
-        s |= (uint32_t)q[b] << (8 * b);
-      }
+    for (int rt = 0; rt < 2; ++rt) {
+      const uint32_t sc = ((asc[rt] & amask[rt]) >> (8 * (j >> 1))) & 0xFF;
+      af[rt] = decode8(u4_dword_sel(araw[rt], jj), scale_pair(sc));
     }
-    r.c[rt][0] = make_uint4(d[0], d[1], d[2], d[3]);
-    r.c[rt][1] = make_uint4(d[4], d[5], d[6], d[7]);
-    r.s[rt] = s;
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      bf[c] = __builtin_bit_cast(half8_t, sw[bbase + 32 * c * kHalfRow + jj]);
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        acc[rt][c] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[rt], bf[c], acc[rt][c], 0, 0, 0);
+    store_w_piece(ws, wstore, wslot, jj, sw_next);
   }
 }
 
-__device__ __forceinline__ uint32_t dword_of(const uint4 (&c)[2], int j) {
-  const uint4 v = c[j >> 2];
-  switch (j & 3) {
-    case 0: return v.x;
-    case 1: return v.y;
-    case 2: return v.z;
-    default: return v.w;
-  }
-}
-
-template <bool AL>
+template <bool AL16, bool AL4, bool TAIL>
 __global__ __launch_bounds__(kMfThreads, 1) void gemm_mfma_kernel(
     const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales, const float* __restrict__ a_g,
     int M, int K, const uint8_t* __restrict__ w_codes, const uint8_t* __restrict__ w_scales, int N,
     SegTable st, const float* __restrict__ w_g, float* __restrict__ out, int64_t ldo) {
-  __shared__ __attribute__((aligned(16))) _Float16 sB[2][kBN * kLdsRow];
+  __shared__ uint4 sW[2][kBN * kHalfRow];              // decoded weight half-tiles, 2 x 36 KB
+  __shared__ uint4 sA[2][kBM * 4];                     // activation codes, 2 x 16 KB
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -126,50 +193,39 @@ __global__ __launch_bounds__(kMfThreads, 1) void gemm_mfma_kernel(
   const int tn = (pid % per_group) / gsz;
   const int m0 = tm * kBM, n0 = tn * kBN;
 
-  // ---- activation lane constants: rows m0 + wm*64 + rt*32 + i, k group h
+  // ---- activation code slots (coalesced loads) and this lane's scale rows
+  ASlots as;
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    const int q = tid + kMfThreads * s;
+    const int r = q >> 2, p = q & 3;
+    const int rc = min(m0 + r, M - 1);
+    as.p[s] = a_codes + (int64_t)rc * (K / 2) + 16 * p;
+    as.lds[s] = r * 4 + (p ^ swz_a(r));
+    as.koff[s] = 32 * p;
+  }
   const int i = lane & 31, h = lane >> 5;
-  const uint8_t* ap[2];
   const uint8_t* asp[2];
   uint32_t amask[2];
 #pragma unroll
   for (int rt = 0; rt < 2; ++rt) {
     const int row = m0 + wm * 64 + rt * 32 + i;
-    const int rc = min(row, M - 1);
-    ap[rt] = a_codes + (int64_t)rc * (K / 2) + 32 * h;
-    asp[rt] = a_scales + (int64_t)rc * (K / kBlock) + 4 * h;
+    asp[rt] = a_scales + (int64_t)min(row, M - 1) * (K / kBlock) + 4 * h;
     amask[rt] = row < M ? 0xFFFFFFFFu : 0u;    // padded rows decode to zeros
   }
-  // ---- weight slots: slot q = tid + 512 * s covers strip q / 64, chunk lane q % 64
-  const uint8_t* wp[2];
-  const uint8_t* wsp[2];
-  int woff[2];
-#pragma unroll
-  for (int s = 0; s < 2; ++s) {
-    const int q = tid + kMfThreads * s;
-    const int64_t strip = min(n0 / kStrip + (q >> 6), nstrips - 1);
-    const int c = q & 63;
-    wp[s] = w_codes + strip * tiles * kChunkCodes + c * 16;
-    wsp[s] = w_scales + strip * tiles * kChunkScales + c * 2;
-    woff[s] = ((q >> 6) * kStrip + (c & 15)) * kLdsRow + (c >> 4) * 32;   // LDS row n, k group g
-  }
-
-  auto load_w = [&](int t, RawW& r) {
+  // ---- weight slots
+  WSlots ws;
+  {
+    const int sl = tid >> 5, n = tid & 15, gg = (tid >> 4) & 1;
+    const int64_t strip = min(n0 / kStrip + sl, nstrips - 1);
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      r.c[s] = *reinterpret_cast<const uint4*>(wp[s] + (int64_t)t * kChunkCodes);
-      r.s[s] = *reinterpret_cast<const uint16_t*>(wsp[s] + (int64_t)t * kChunkScales);
+      const int g = 2 * gg + s;
+      ws.wp[s] = w_codes + strip * tiles * kChunkCodes + chunk_code_off(n, g);
+      ws.wsp[s] = w_scales + strip * tiles * kChunkScales + chunk_scale_off(n, g);
     }
-  };
-  auto store_w_part = [&](const RawW& r, int stage, int part) {   // part 0..7: slot part/4, dword part%4
-    const int s = part >> 2, d = part & 3;
-    const uint32_t sc = (d < 2) ? (r.s[s] & 0xFF) : (r.s[s] >> 8);
-    const uint32_t w = (d == 0) ? r.c[s].x : (d == 1) ? r.c[s].y : (d == 2) ? r.c[s].z : r.c[s].w;
-    *reinterpret_cast<half8_t*>(&sB[stage][woff[s] + 8 * d]) = decode8(w, scale_pair(sc));
-  };
-  auto load_a = [&](int t, RawA& r) {
-    if (t < full) load_a_tile<AL>(ap, asp, t, r);
-    else load_a_tail(ap, asp, t, t * kTileK + 64 * h, K, r);
-  };
+    ws.lds = (sl * kStrip + n) * kHalfRow + 4 * gg;
+  }
 
   float16_t acc[2][4];
 #pragma unroll
@@ -179,47 +235,54 @@ __global__ __launch_bounds__(kMfThreads, 1) void gemm_mfma_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[rt][c][r] = 0.f;
 
-  RawA ra0, ra1;
-  RawW rw0, rw1;
-  load_a(0, ra0);
-  load_w(0, rw0);
-  if (tiles > 1) load_w(1, rw1);
+  const int last = tiles - 1;
+  const int kb = 64 * h;
+  const int arow0 = wm * 64 + i;
+  const int bbase = (wn * 128 + i) * kHalfRow + 4 * h;
+  uint4 an[2];                                          // activation codes in flight (next tile)
+  uint32_t sc0[2];                                      // activation scales of tile 0
+  RawW rw0, rw1;                                        // weights of tiles 0 and 1
+  {
+    uint4 a0[2];
+    load_a_codes<AL16, TAIL>(as, 0, full, K, a0);
+    load_a_scales<AL4, TAIL>(asp, 0, full, kb, K, sc0);
+    load_w_tile(ws, 0, rw0);
+    load_a_codes<AL16, TAIL>(as, min(1, last), full, K, an);
+    load_w_tile(ws, min(1, last), rw1);
 #pragma unroll
-  for (int p = 0; p < 8; ++p) store_w_part(rw0, 0, p);
+    for (int d = 0; d < 4; ++d) store_w_piece(ws, rw0, 0, d, sW[0]);
+    sA[0][as.lds[0]] = a0[0];
+    sA[0][as.lds[1]] = a0[1];
+  }
   __syncthreads();
 
-  const int brow = wn * 128 + i;                       // this lane's B row within the tile (+ 32 c)
-  // One k tile: MFMAs on tile t (activations in `acur`, weights in LDS stage t & 1)
-  // while tile t + 1's activations load into `anext`, tile t + 2's weights into
-  // `wload` and tile t + 1's weights (`wstore`) are decoded into the other stage.
-  auto step = [&](int t, const RawA& acur, RawA& anext, RawW& wload, const RawW& wstore) {
-    const int cur = t & 1;
-    if (t + 1 < tiles) load_a(t + 1, anext);
-    if (t + 2 < tiles) load_w(t + 2, wload);
-    const _Float16* B = sB[cur];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      half8_t af[2], bf[4];
-#pragma unroll
-      for (int rt = 0; rt < 2; ++rt) {
-        const uint32_t sc = (acur.s[rt] & amask[rt]) >> (8 * (j >> 1));
-        af[rt] = decode8(dword_of(acur.c[rt], j), scale_pair(sc & 0xFF));
-      }
-#pragma unroll
-      for (int c = 0; c < 4; ++c)
-        bf[c] = *reinterpret_cast<const half8_t*>(&B[(brow + 32 * c) * kLdsRow + 64 * h + 8 * j]);
-#pragma unroll
-      for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-          acc[rt][c] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[rt], bf[c], acc[rt][c], 0, 0, 0);
-      if (t + 1 < tiles) store_w_part(wstore, cur ^ 1, j);
-    }
+  // Per tile t (two half-tiles): half 0 runs MFMA steps 0-3 on sW[0] while the
+  // second half of tile t's weights (rwc, slot 1) is decoded into sW[1] and
+  // tile t + 1's activation codes are written to the other activation stage;
+  // half 1 runs steps 4-7 on sW[1] while the first half of tile t + 1's weights
+  // (rwn, slot 0) is decoded into sW[0].  Tile t + 1's scales load at the top
+  // of tile t, tile t + 2's codes after half 0 and tile t + 2's weights after
+  // half 1.  Tile indices are clamped to the last tile, so every load is
+  // unconditional and in bounds.  The loop body is one tile; the raw register
+  // sets change roles through plain copies at its end.
+  uint32_t scc[2] = {sc0[0], sc0[1]};
+  RawW rwc = rw0, rwn = rw1;
+  for (int t = 0; t < tiles; ++t) {
+    const uint4* sa = sA[t & 1];
+    uint4* sa_next = sA[(t + 1) & 1];
+    uint32_t scn[2];
+    load_a_scales<AL4, TAIL>(asp, min(t + 1, last), full, min(t + 1, last) * kTileK + kb, K, scn);
+    mfma_half<0>(sa, sW[0], scc, amask, arow0, bbase, h, ws, rwc, 1, sW[1], acc);
+    sa_next[as.lds[0]] = an[0];
+    sa_next[as.lds[1]] = an[1];
+    load_a_codes<AL16, TAIL>(as, min(t + 2, last), full, K, an);
     __syncthreads();
-  };
-  for (int t = 0; t < tiles; t += 2) {
-    step(t, ra0, ra1, rw0, rw1);
-    if (t + 1 < tiles) step(t + 1, ra1, ra0, rw1, rw0);
+    mfma_half<1>(sa, sW[1], scc, amask, arow0, bbase, h, ws, rwn, 0, sW[0], acc);
+    rwc = rwn;
+    load_w_tile(ws, min(t + 2, last), rwn);
+    scc[0] = scn[0];
+    scc[1] = scn[1];
+    __syncthreads();
   }
 
   // ---- epilogue: lane holds rows 8*(r/4) + 4*h + r%4, column i of each 32x32 tile
@@ -243,12 +306,14 @@ hipError_t launch_gemm_mfma(const uint8_t* a_codes, const uint8_t* a_scales, con
                             const uint8_t* w_codes, const uint8_t* w_scales, int N, const SegTable& st,
                             const float* w_g, float* out, int64_t ldo, hipStream_t stream) {
   const int grid = ((M + kBM - 1) / kBM) * ((N + kBN - 1) / kBN);
-  if (K % 64 == 0)
-    gemm_mfma_kernel<true><<<grid, kMfThreads, 0, stream>>>(a_codes, a_scales, a_g, M, K, w_codes, w_scales, N,
-                                                            st, w_g, out, ldo);
-  else
-    gemm_mfma_kernel<false><<<grid, kMfThreads, 0, stream>>>(a_codes, a_scales, a_g, M, K, w_codes, w_scales, N,
-                                                             st, w_g, out, ldo);
+#define NVFP4_MFMA_LAUNCH(A16, A4, T)                                                                            \
+  gemm_mfma_kernel<A16, A4, T><<<grid, kMfThreads, 0, stream>>>(a_codes, a_scales, a_g, M, K, w_codes, w_scales, \
+                                                                N, st, w_g, out, ldo)
+  if (K % kTileK == 0) NVFP4_MFMA_LAUNCH(true, true, false);
+  else if (K % 64 == 0) NVFP4_MFMA_LAUNCH(true, true, true);
+  else if (K % 32 == 0) NVFP4_MFMA_LAUNCH(true, false, true);
+  else NVFP4_MFMA_LAUNCH(false, false, true);
+#undef NVFP4_MFMA_LAUNCH
   return hipGetLastError();
 }
 

@@ -5,7 +5,8 @@ Default workload: the decode skinny GEMM -- M in {1, 4, 16} tokens, K = 5120,
 N = 12288, weights N(0, 0.02) pre-packed, bf16 Student-t(3) activations with
 0.1% of channels x100 quantized on the fly.  One step = the whole hot path for
 the three token counts: activation quantization (dynamic per-tensor scale) +
-W4A4 GEMM + per-segment epilogue, three times.  The packed weight is kept in
+W4A4 GEMM + per-segment epilogue, three times, each one nvfp4_linear call
+(a single fused launch at these sizes).  The packed weight is kept in
 16 device copies (566 MB, more than the 256 MB MALL) and each step uses the
 next copy, so every call streams its weights from HBM.  The 16 steps that use
 the 16 copies in turn are captured in one HIP graph, replayed once per 16
@@ -127,9 +128,12 @@ def bench_decode(args, torch, nv, W, dev):
     torch.cuda.synchronize()
 
     def step_eager(r):
-        for M in Ms:
-            c, s, g = nv.quantize_act(xs[M], None, ws, out=acts[M])
-            nv.gemm(c, s, g, copies[r % len(copies)], out=outs[M])
+        # one nvfp4_linear call per token count: for these sizes a single launch
+        # (activation quantization + GEMM + epilogue)
+        # every call streams a different weight copy, so no call finds its
+        # weights in the 256 MB last-level cache (16 copies = 566 MB)
+        for i, M in enumerate(Ms):
+            nv.linear(xs[M], copies[(len(Ms) * r + i) % len(copies)], None, ws, out=outs[M], act_out=acts[M])
 
     nc = len(copies)
     if args.no_graph:
@@ -169,34 +173,33 @@ def bench_decode(args, torch, nv, W, dev):
     step_bytes = sum(wbytes + 2 * M * K + 4 * M * N for M in Ms)
     value = step_bytes * args.steps / sec / 1e9
 
-    # dominant kernel: the skinny GEMM.  Per M, a graph of nc back-to-back launches
-    # (one per weight copy) is replayed with a HIP event pair around each replay on
-    # the launch stream; average launch duration = event time / launches.
-    # Algorithmic bytes per launch = weight codes+scales + activation codes+scales
-    # + fp32 output.
+    # dominant kernel: the one-launch decode linear (linear_decode_kernel), one per
+    # call.  Per M, a graph of nc back-to-back calls (one per weight copy) is
+    # replayed with a HIP event pair around each replay on the launch stream;
+    # average launch duration = event time / launches.  Algorithmic bytes per
+    # launch = weight codes+scales + bf16 activations + activation codes+scales
+    # written + fp32 output.
     kern = {}
     for M in Ms:
-        nv.quantize_act(xs[M], None, ws, out=acts[M])
-        torch.cuda.synchronize()
         if args.no_graph:
-            launch = lambda i, M=M: [nv.gemm(acts[M][0], acts[M][1], acts[M][2], copies[r], out=outs[M])
+            launch = lambda i, M=M: [nv.linear(xs[M], copies[r], None, ws, out=outs[M], act_out=acts[M])
                                      for r in range(nc)]
         else:
             gg = torch.cuda.CUDAGraph()
             with torch.cuda.graph(gg):
                 for r in range(nc):
-                    nv.gemm(acts[M][0], acts[M][1], acts[M][2], copies[r], out=outs[M])
+                    nv.linear(xs[M], copies[r], None, ws, out=outs[M], act_out=acts[M])
             launch = lambda i, gg=gg: gg.replay()
         mean, med = kernel_time_pairs(torch, launch, max(8, args.steps // nc))
         mean, med = mean / nc, med / nc
-        kb = wbytes + M * K * 9 // 16 + 4 * M * N
+        kb = wbytes + 2 * M * K + M * K * 9 // 16 + 4 * M * N
         kern[M] = {"mean_us": mean * 1e6, "median_us": med * 1e6, "bytes": kb, "GBps": kb / mean / 1e9}
     tot_b = sum(k["bytes"] for k in kern.values())
     tot_t = sum(k["mean_us"] for k in kern.values()) * 1e-6
     achieved = tot_b / tot_t / 1e9
 
     res = {
-        "metric": "NVFP4 W4A4 decode GEMM GB/s (quantize + GEMM + epilogue), % of MI355X HBM roofline",
+        "metric": "NVFP4 W4A4 decode linear GB/s (quantize + GEMM + epilogue), % of MI355X HBM roofline",
         "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(sec / args.steps * 1e3, 5), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f16",
@@ -205,11 +208,11 @@ def bench_decode(args, torch, nv, W, dev):
         "config": {"workload": "decode_skinny_gemm_m1_m4_m16_k5120_n12288", "M": list(Ms), "K": K, "N": N,
                    "segments": 1, "weight_copies": len(copies), "graphs": not args.no_graph,
                    "step_bytes": step_bytes, "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
-                   "gemm_kernel": {str(M): {k: round(v, 3) if isinstance(v, float) else v for k, v in kern[M].items()}
+                   "linear_kernel": {str(M): {k: round(v, 3) if isinstance(v, float) else v for k, v in kern[M].items()}
                                    for M in Ms}},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "gemm_skinny_kernel", "per_launch_bytes": {str(M): kern[M]["bytes"] for M in Ms}},
+                     "kernel": "linear_decode_kernel", "per_launch_bytes": {str(M): kern[M]["bytes"] for M in Ms}},
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline_decode(d16, Ms, args.cpu_seconds, step_bytes)

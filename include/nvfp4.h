@@ -105,9 +105,12 @@ nvfp4_status nvfp4_quantize_act(const void* x_bf16, int64_t M, int64_t K, int64_
  * weight layout the GEMM reads, with N padded to a multiple of 16 and K to a
  * multiple of 128 with zero codes and zero scales (sizes from
  * nvfp4_packed_weight_bytes).  The layout: chunks of 16 rows x 128 k, strip
- * major (chunk = (n / 16) * (Kp / 128) + k / 128); each code chunk is
- * 16 x 64 bytes and each scale chunk 16 x 8 bytes, both row-major in the
- * canonical encoding.  `segs` is a HOST array.
+ * major (chunk = (n / 16) * (Kp / 128) + k / 128), 1024 code bytes and 128
+ * scale bytes per chunk.  Inside a chunk, the 16 canonical code bytes of row n,
+ * k group g (k in [32 g, 32 g + 32)) sit at byte (16 g + n) * 16 and its two
+ * scale bytes at byte (16 g + n) * 2, so lane l of a 64-lane wave reading bytes
+ * [16 l, 16 l + 16) gets exactly the 16x16x32 MFMA operand of column l % 16,
+ * k group l / 16.  `segs` is a HOST array.
  * ------------------------------------------------------------------------- */
 nvfp4_status nvfp4_packed_weight_bytes(int64_t N, int64_t K, size_t* codes_bytes, size_t* scales_bytes);
 
@@ -145,6 +148,31 @@ nvfp4_status nvfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const f
                         const uint8_t* w_codes, const uint8_t* w_scales, int64_t N,
                         const nvfp4_segment* segs, const float* w_g_dec, int32_t nseg,
                         float* out, int64_t ldo, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * The whole W4A4 linear layer in one call: on-the-fly activation quantization
+ * (as nvfp4_quantize_act) followed by the GEMM with the per-module epilogue (as
+ * nvfp4_gemm).  The activation codes, scales and g_dec are written to the
+ * caller's buffers as well, in the canonical layout.  Results are bit-identical
+ * to calling nvfp4_quantize_act then nvfp4_gemm.
+ *
+ * Decode-sized inputs (1 <= M <= 16, K <= 5120) run as ONE launch: every GEMM
+ * workgroup encodes the (small) activation tensor itself while its weight loads
+ * are in flight, so no workspace and no hand-over between workgroups is needed.
+ * Other inputs run the quantizer and the GEMM kernels back to back on the
+ * stream.
+ *
+ *   workspace  device scratch of nvfp4_linear_workspace_bytes(M, K) bytes
+ *              (NULL allowed when that is 0 or amax_in is given); contents
+ *              need no setup.
+ * ------------------------------------------------------------------------- */
+size_t nvfp4_linear_workspace_bytes(int64_t M, int64_t K);
+
+nvfp4_status nvfp4_linear(const void* x_bf16, int64_t M, int64_t K, int64_t ldx, const float* amax_in,
+                          uint8_t* a_codes, uint8_t* a_scales, float* a_g_dec,
+                          const uint8_t* w_codes, const uint8_t* w_scales, int64_t N,
+                          const nvfp4_segment* segs, const float* w_g_dec, int32_t nseg,
+                          float* out, int64_t ldo, void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -64,6 +64,11 @@ def _lib():
         lib.nvfp4_gemm.restype = ctypes.c_int
         lib.nvfp4_gemm.argtypes = [_vp, _vp, _vp, _i64, _i64, _vp, _vp, _i64, ctypes.POINTER(Segment), _vp,
                                    ctypes.c_int32, _vp, _i64, _vp]
+        lib.nvfp4_linear_workspace_bytes.restype = _sz
+        lib.nvfp4_linear_workspace_bytes.argtypes = [_i64, _i64]
+        lib.nvfp4_linear.restype = ctypes.c_int
+        lib.nvfp4_linear.argtypes = [_vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _i64,
+                                     ctypes.POINTER(Segment), _vp, ctypes.c_int32, _vp, _i64, _vp, _sz, _vp]
         _LIB = lib
     return _LIB
 
@@ -142,6 +147,18 @@ def nvfp4_gemm(a_codes, a_scales, a_g_dec, M, K, w_codes, w_scales, N, segments,
     arr, n = _segs(segments)
     _check(_lib().nvfp4_gemm(_ptr(a_codes), _ptr(a_scales), _ptr(a_g_dec), M, K, _ptr(w_codes), _ptr(w_scales),
                              N, arr, _ptr(w_g_dec), n, _ptr(out), ldo, _stream(stream)), "nvfp4_gemm")
+
+
+def nvfp4_linear_workspace_bytes(M, K):
+    return _lib().nvfp4_linear_workspace_bytes(int(M), int(K))
+
+
+def nvfp4_linear(x, M, K, ldx, amax_in, a_codes, a_scales, a_g_dec, w_codes, w_scales, N, segments, w_g_dec,
+                 out, ldo, workspace, workspace_bytes, stream=None):
+    arr, n = _segs(segments)
+    _check(_lib().nvfp4_linear(_ptr(x), M, K, ldx, _ptr(amax_in), _ptr(a_codes), _ptr(a_scales), _ptr(a_g_dec),
+                               _ptr(w_codes), _ptr(w_scales), N, arr, _ptr(w_g_dec), n, _ptr(out), ldo,
+                               _ptr(workspace), workspace_bytes, _stream(stream)), "nvfp4_linear")
 
 
 # ---- convenience layer: allocate with torch, call the C ABI --------------------------
@@ -232,7 +249,24 @@ def gemm(a_codes, a_scales, a_g_dec, pw, out=None, g_dec=None, stream=None):
     return out
 
 
-def linear(x, pw, amax=None, workspace=None, stream=None):
-    """The whole W4A4 linear layer: quantize bf16 x on the fly, then GEMM + epilogue."""
-    c, s, g = quantize_act(x, amax, workspace, stream=stream)
-    return gemm(c, s, g, pw, stream=stream)
+def linear(x, pw, amax=None, workspace=None, out=None, act_out=None, stream=None):
+    """The whole W4A4 linear layer via nvfp4_linear: bf16 x [M, K] -> fp32 [M, N].
+
+    Also returns the activation codes, scales and g_dec it produced."""
+    assert x.dtype == torch.bfloat16 and x.dim() == 2 and (x.stride(1) == 1 or x.shape[1] <= 1)
+    M, K = x.shape
+    assert K == pw.K
+    dev = x.device
+    if act_out is None:
+        codes = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
+        scales = torch.empty((M, K // 16), dtype=torch.uint8, device=dev)
+        g = torch.empty(1, dtype=torch.float32, device=dev)
+    else:
+        codes, scales, g = act_out
+    if out is None:
+        out = torch.empty((M, pw.N), dtype=torch.float32, device=dev)
+    ws = workspace if workspace is not None else Workspace(dev)
+    buf, nbytes = ws.get(nvfp4_linear_workspace_bytes(M, K))
+    nvfp4_linear(x, M, K, max(x.stride(0), K), amax, codes, scales, g, pw.codes, pw.scales, pw.N, pw.segments,
+                 pw.g_dec, out, out.stride(0), buf, nbytes, stream)
+    return out, (codes, scales, g)

@@ -164,4 +164,66 @@ nvfp4_status nvfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const f
                                           st, w_g_dec, out, ldo, s));
 }
 
+// ---- nvfp4_linear: the workspace holds the quantizer's amax partials (large inputs only)
+size_t nvfp4_linear_workspace_bytes(int64_t M, int64_t K) {
+  if (M < 0 || K < 0) return 0;
+  return nvfp4::quantize_act_workspace(M, K);
+}
+
+nvfp4_status nvfp4_linear(const void* x_bf16, int64_t M, int64_t K, int64_t ldx, const float* amax_in,
+                          uint8_t* a_codes, uint8_t* a_scales, float* a_g_dec, const uint8_t* w_codes,
+                          const uint8_t* w_scales, int64_t N, const nvfp4_segment* segs, const float* w_g_dec,
+                          int32_t nseg, float* out, int64_t ldo, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  if (M < 0 || K < 0 || N < 1) return NVFP4_EINVAL;
+  if (K % 16 != 0 || M >= kMaxDim || K >= kMaxDim || N >= kMaxDim || ldx < K || ldo < N) return NVFP4_ESHAPE;
+  const nvfp4_status ss = check_segments(segs, nseg, N);
+  if (ss != NVFP4_OK) return ss;
+  if (!a_g_dec) return NVFP4_EINVAL;
+  const size_t need = nvfp4_linear_workspace_bytes(M, K);
+  if (!amax_in && need > 0 && (!workspace || workspace_bytes < need)) return NVFP4_EWORKSPACE;
+  if (workspace && !aligned16(workspace)) return NVFP4_EALIGN;
+  if (M == 0 || K == 0) {   // nothing to encode or nothing to sum: the separate calls cover both
+    const nvfp4_status q = nvfp4_quantize_act(x_bf16, M, K, ldx, amax_in, a_codes, a_scales, a_g_dec, workspace,
+                                              workspace_bytes, stream);
+    if (q != NVFP4_OK || M == 0) return q;
+    return nvfp4_gemm(a_codes, a_scales, a_g_dec, M, K, w_codes, w_scales, N, segs, w_g_dec, nseg, out, ldo,
+                      stream);
+  }
+  if (!x_bf16 || !a_codes || !a_scales || !w_codes || !w_scales || !w_g_dec || !out) return NVFP4_EINVAL;
+  if (!aligned16(x_bf16) || !aligned16(a_codes) || !aligned16(a_scales) || !aligned16(w_codes) ||
+      !aligned16(w_scales) || !aligned16(out) || ldx % 8 != 0)
+    return NVFP4_EALIGN;
+  size_t cb = 0, sb = 0;
+  nvfp4_packed_weight_bytes(N, K, &cb, &sb);
+  const size_t xb = (size_t)((M - 1) * ldx + K) * 2, acb = (size_t)(M * K / 2), asb = (size_t)(M * K / 16);
+  const size_t ob = (size_t)((M - 1) * ldo + N) * 4;
+  const void* outs[4] = {a_codes, a_scales, a_g_dec, out};
+  const size_t osz[4] = {acb, asb, 4, ob};
+  const void* ins[6] = {x_bf16, w_codes, w_scales, w_g_dec, workspace, amax_in};
+  const size_t isz[6] = {xb, cb, sb, (size_t)nseg * 4, need, 4};
+  for (int i = 0; i < 4; ++i) {
+    for (int j = 0; j < 6; ++j)
+      if (overlap(outs[i], osz[i], ins[j], isz[j])) return NVFP4_EINVAL;
+    for (int j = i + 1; j < 4; ++j)
+      if (overlap(outs[i], osz[i], outs[j], osz[j])) return NVFP4_EINVAL;
+  }
+  nvfp4::SegTable st{};
+  st.nseg = nseg;
+  for (int i = 0; i < nseg; ++i) st.end[i] = segs[i].n_end;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (nvfp4::linear_decode_fits(M, K))
+    return launched(nvfp4::launch_linear_decode(static_cast<const uint16_t*>(x_bf16), ldx, amax_in, a_codes, a_scales,
+                                                a_g_dec, (int)M, (int)K, w_codes, w_scales, (int)N, st, w_g_dec, out,
+                                                ldo, s));
+  const hipError_t e = nvfp4::launch_quantize_act(static_cast<const uint16_t*>(x_bf16), M, K, ldx, amax_in, a_codes,
+                                                  a_scales, a_g_dec, workspace, s);
+  if (e != hipSuccess) return NVFP4_EHIP;
+  if (M <= 16)
+    return launched(nvfp4::launch_gemm_skinny(a_codes, a_scales, a_g_dec, (int)M, (int)K, w_codes, w_scales, (int)N,
+                                              st, w_g_dec, out, ldo, s));
+  return launched(nvfp4::launch_gemm_mfma(a_codes, a_scales, a_g_dec, (int)M, (int)K, w_codes, w_scales, (int)N,
+                                          st, w_g_dec, out, ldo, s));
+}
+
 }  // extern "C"

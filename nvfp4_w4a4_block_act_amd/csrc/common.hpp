@@ -130,6 +130,15 @@ hipError_t launch_gemm_skinny(const uint8_t* a_codes, const uint8_t* a_scales, c
                               const SegTable& st, const float* w_g, float* out, int64_t ldo,
                               hipStream_t stream);
 hipError_t launch_fill_zero(float* out, int M, int N, int64_t ldo, hipStream_t stream);
+// Fused decode-form linear layer (quantize + skinny GEMM in one launch); `sync`
+// points at 16 zero-initialised bytes of the caller's workspace.
+// One-launch decode-form linear layer (activation quantization fused into the
+// skinny GEMM); valid when linear_decode_fits(M, K).
+bool linear_decode_fits(int64_t M, int64_t K);
+hipError_t launch_linear_decode(const uint16_t* x, int64_t ldx, const float* amax_in, uint8_t* a_codes,
+                                uint8_t* a_scales, float* a_g, int M, int K, const uint8_t* w_codes,
+                                const uint8_t* w_scales, int N, const SegTable& st, const float* w_g, float* out,
+                                int64_t ldo, hipStream_t stream);
 hipError_t launch_gemm_mfma(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_g,
                             int M, int K, const uint8_t* w_codes, const uint8_t* w_scales, int N,
                             const SegTable& st, const float* w_g, float* out, int64_t ldo,

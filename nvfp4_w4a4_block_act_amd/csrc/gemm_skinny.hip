@@ -8,10 +8,11 @@
 //
 // Design (gfx950):
 //  * each weight byte is read from HBM exactly once: 0.5625 B per weight
-//    (codes + scales); a workgroup of four waves owns `SW` strips of 16 output
-//    columns, and its waves split the K tiles of those strips (split-K inside
-//    the workgroup, reduced through LDS), so ~1.5 waves per SIMD each keep
-//    several KB of independent 16-byte loads in flight;
+//    (codes + scales); a workgroup of eight waves owns S = 3 strips of 16
+//    output columns (256 workgroups for N = 12288, one per CU), and its waves
+//    split the K tiles of those strips (split-K inside the workgroup, reduced
+//    through LDS); each wave requests all of its tiles (5 x 3 KB at K = 5120)
+//    before it decodes any, so every CU keeps its whole share in flight;
 //  * the 16 x 16 x 32 fp16 MFMA does the arithmetic with M padded to 16:
 //    lane l holds row/column l % 16 and the 32 k of group g = l / 16 of a
 //    128-k tile.  A K-permutation shared by both operands makes each lane's
@@ -20,10 +21,13 @@
 //    are decoded exactly to fp16 in registers (fp4 converter + packed fp16
 //    multiply by the E4M3 scale); no LDS staging, since each weight is used
 //    once;
-//  * the epilogue applies the per-segment scale during the cross-wave sum.
+//  * the epilogue applies the per-segment scale during the cross-wave sum;
+//  * for decode-sized activations a second kernel also quantizes them inside
+//    the same launch (linear_decode_kernel below).
 #include <algorithm>
 
 #include "common.hpp"
+#include "quant_device.hpp"
 
 namespace nvfp4 {
 
@@ -80,8 +84,49 @@ __device__ __forceinline__ void decode_a(uint4 v, uint32_t sc, uint32_t amask, h
   A[3] = decode8(v.w, s1);
 }
 
-// S strips of 16 columns per workgroup, NW waves splitting the k tiles
-// (wave w takes tiles w, w + NW, ...), U tiles per load batch.
+// Cross-wave sum of the per-wave partial tiles and the epilogue: output element
+// e = (s, i, l) is row 4 * (l / 16) + i, column (strip0 + s) * 16 + l % 16, and is
+// stored as fl(sum * fl(a_g * w_g[seg(n)])).
+template <int S, int NW>
+__device__ __forceinline__ void reduce_store(const float4_t (&acc)[S], float (&red)[NW][S][4][64], int strip0, int M,
+                                             int N, const SegTable& st, float ag, const float* __restrict__ w_g,
+                                             float* __restrict__ out, int64_t ldo) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int s = 0; s < S; ++s)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) red[wave][s][i][lane] = acc[s][i];
+  __syncthreads();
+  for (int e = threadIdx.x; e < S * 256; e += 64 * NW) {
+    const int s = e >> 8, i = (e >> 6) & 3, l = e & 63;
+    const int row = 4 * (l >> 4) + i;
+    const int n = (strip0 + s) * kStrip + (l & 15);
+    if (row >= M || n >= N) continue;
+    float v = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) v += red[w][s][i][l];
+    out[(int64_t)row * ldo + n] = v * (ag * w_g[seg_of(st, n)]);
+  }
+}
+
+// Weight pointers of lane `lane` for the S strips starting at strip0 (clamped;
+// columns past N are never stored).
+template <int S>
+__device__ __forceinline__ void strip_pointers(const uint8_t* w_codes, const uint8_t* w_scales, int strip0, int nstrips,
+                                               int tiles, int lane, const uint8_t* (&wc)[S], const uint8_t* (&ws)[S]) {
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    const int64_t strip = min(strip0 + s, nstrips - 1);
+    wc[s] = w_codes + strip * tiles * kChunkCodes + lane * 16;
+    ws[s] = w_scales + strip * tiles * kChunkScales + lane * 2;
+  }
+}
+
+// The skinny GEMM of one workgroup: S strips of 16 columns, NW waves splitting
+// the k tiles (wave w takes tiles w, w + NW, ...), U tiles per load batch.  Every
+// load of a batch is issued before any decode and batches have no branches
+// (tiles past the end are clamped and their activation scales zeroed), so the
+// waits before each tile's MFMAs stay progressive.
 template <int S, int NW, int U, bool AL16>
 __global__ __launch_bounds__(64 * NW) void gemm_skinny_kernel(
     const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales, const float* __restrict__ a_g,
@@ -101,36 +146,30 @@ __global__ __launch_bounds__(64 * NW) void gemm_skinny_kernel(
   const uint32_t amask = (r < M) ? 0xFFFFu : 0u;
   const uint8_t* ac = a_codes + (int64_t)arow * (K / 2) + g * 16;
   const uint8_t* as = a_scales + (int64_t)arow * (K / kBlock) + g * 2;
-  // W: strip pointers (clamped; columns past N are never stored)
   const uint8_t* wc[S];
   const uint8_t* ws[S];
-#pragma unroll
-  for (int s = 0; s < S; ++s) {
-    const int64_t strip = min(strip0 + s, nstrips - 1);
-    wc[s] = w_codes + strip * tiles * kChunkCodes + lane * 16;
-    ws[s] = w_scales + strip * tiles * kChunkScales + lane * 2;
-  }
+  strip_pointers<S>(w_codes, w_scales, strip0, nstrips, tiles, lane, wc, ws);
 
   float4_t acc[S];
 #pragma unroll
   for (int s = 0; s < S; ++s) acc[s] = float4_t{0.f, 0.f, 0.f, 0.f};
 
-  // Batches of U tiles; every load of a batch is issued before any decode, and the
-  // batch has no branches (tiles past the end are clamped and their activation
-  // scales zeroed), so the waits before each tile's MFMAs stay progressive.
   for (int t0 = wave; t0 < full; t0 += NW * U) {
-    uint4 av[U], wv[U][S];
-    uint32_t asc[U], wsc[U][S];
+    uint4 wv[U][S];
+    uint32_t wsc[U][S];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int t = min(t0 + u * NW, full - 1);
-      load_a_full<AL16>(ac, as, t, av[u], asc[u]);
 #pragma unroll
       for (int s = 0; s < S; ++s) {
         wv[u][s] = *reinterpret_cast<const uint4*>(wc[s] + (int64_t)t * kChunkCodes);
         wsc[u][s] = *reinterpret_cast<const uint16_t*>(ws[s] + (int64_t)t * kChunkScales);
       }
     }
+    uint4 av[U];
+    uint32_t asc[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) load_a_full<AL16>(ac, as, min(t0 + u * NW, full - 1), av[u], asc[u]);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const uint32_t live = (t0 + u * NW < full) ? amask : 0u;
@@ -154,26 +193,179 @@ __global__ __launch_bounds__(64 * NW) void gemm_skinny_kernel(
       tile_mfma(A, w, wsv, acc[s]);
     }
   }
+  reduce_store<S, NW>(acc, red, strip0, M, N, st, *a_g, w_g, out, ldo);
+}
 
+// ---- decode-form linear layer in one launch (M <= 16, K <= 5120).
+// Every workgroup quantizes the whole activation tensor itself: it is at most
+// 16 x 5120 bf16 (160 KB, L2-resident once the first workgroups have read it),
+// and encoding it redundantly costs less than the alternatives measured on this
+// chip: a separate quantizer launch (about 5 us of launch and latency for a few
+// KB of work), or producer workgroups handing codes to the GEMM workgroups
+// (which needs a device-scope release/acquire, an L2 write-back and invalidate,
+// and whose loads queue behind the 35 MB weight stream).  Steps:
+//  1. every thread loads the bf16 blocks tid, tid + 64 NW, ... (coalesced);
+//  2. each wave requests its first PRE weight batches, so the weight stream
+//     starts before the activation work;
+//  3. amax: per-thread maximum, wave reduction, one barrier (which also
+//     publishes the reciprocal table of the fast encoder);
+//  4. every thread encodes its blocks into LDS in the canonical layout (rows
+//     padded by 16 bytes against bank conflicts); workgroup 0 also writes the
+//     canonical codes, scales and g_dec to memory;
+//  5. the remaining weight batches are requested (a wave that has requested
+//     its weights stalls at issue while the memory system back-pressures the
+//     loads, so they go out only once the encode is done), then a barrier;
+//  6. the skinny-GEMM tiles read their activation operand from LDS.
+// The results are bit-identical to the activation quantizer followed by the
+// skinny GEMM.
+constexpr int kDecMaxM = 16;
+constexpr int kDecMaxK = 5120;
+constexpr int kDecCodeStride = kDecMaxK / 2 + 16;       // LDS bytes per activation row
+constexpr int kDecScaleStride = kDecMaxK / kBlock + 4;
+
+// b = r * nb + c with 0 <= c < nb, via a float reciprocal corrected to exact (b < 2^24).
+__device__ __forceinline__ void split_block(int b, int nb, float inv_nb, int& r, int& c) {
+  r = (int)((float)b * inv_nb);
+  c = b - r * nb;
+  if (c < 0) { --r; c += nb; }
+  if (c >= nb) { ++r; c -= nb; }
+}
+
+template <int S, int NW, int U, int PRE>
+__global__ __launch_bounds__(64 * NW) void linear_decode_kernel(
+    const uint16_t* __restrict__ x, int64_t ldx, const float* __restrict__ amax_in, uint8_t* __restrict__ a_codes,
+    uint8_t* __restrict__ a_scales, float* __restrict__ a_g, int M, int K, float inv_nb,
+    const uint8_t* __restrict__ w_codes, const uint8_t* __restrict__ w_scales, int N, SegTable st,
+    const float* __restrict__ w_g, float* __restrict__ out, int64_t ldo) {
+  constexpr int kThreads = 64 * NW;
+  constexpr int kPer = kDecMaxM * kDecMaxK / kBlock / kThreads;   // blocks per thread at most
+  static_assert(kPer * kThreads == kDecMaxM * kDecMaxK / kBlock, "block split");
+  static_assert(NW * U * kTileK >= kDecMaxK, "one batch set covers K");
+  __shared__ float red[NW][S][4][64];
+  __shared__ __align__(16) uint8_t lcodes[kDecMaxM * kDecCodeStride];
+  __shared__ __align__(16) uint8_t lscales[kDecMaxM * kDecScaleStride];
+  __shared__ float rtab[128];
+  __shared__ uint32_t wmax[NW];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nb = K / kBlock;
+  const int B = M * nb;
+  const int tiles = (K + kTileK - 1) / kTileK;
+  const int nstrips = (N + kStrip - 1) / kStrip;
+  const int strip0 = blockIdx.x * S;
+
+  // 1. activations: block b = tid + kThreads j is row b / nb, block column b % nb
+  uint4 xv[kPer][2];
 #pragma unroll
-  for (int s = 0; s < S; ++s)
+  for (int j = 0; j < kPer; ++j) {
+    const int b = tid + kThreads * j;
+    int r, c;
+    split_block(b, nb, inv_nb, r, c);
+    const bool ok = b < B;
+    const uint4* q = reinterpret_cast<const uint4*>(x + (ok ? (int64_t)r * ldx + (int64_t)c * kBlock : 0));
+    xv[j][0] = ok ? q[0] : make_uint4(0u, 0u, 0u, 0u);
+    xv[j][1] = ok ? q[1] : make_uint4(0u, 0u, 0u, 0u);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  // 2. first weight batches: tile t = wave + NW u (clamped past the end)
+  const uint8_t* wc[S];
+  const uint8_t* ws[S];
+  strip_pointers<S>(w_codes, w_scales, strip0, nstrips, tiles, lane, wc, ws);
+  uint4 wv[U][S];
+  uint32_t wsc[U][S];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) red[wave][s][i][lane] = acc[s][i];
+  for (int u = 0; u < PRE; ++u) {
+    const int t = min(wave + NW * u, tiles - 1);
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      wv[u][s] = *reinterpret_cast<const uint4*>(wc[s] + (int64_t)t * kChunkCodes);
+      wsc[u][s] = *reinterpret_cast<const uint16_t*>(ws[s] + (int64_t)t * kChunkScales);
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  // 3. reciprocal table and tensor amax (max of |x| as bf16 bit patterns)
+  fill_rcp_table(rtab);
+  float amax;
+  if (amax_in) {
+    amax = *amax_in;
+    __syncthreads();
+  } else {
+    u16x2_t mp = {0, 0};
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) mp = absmax_pk(xv[j][1], absmax_pk(xv[j][0], mp));
+    uint32_t m = max(mp.x, mp.y);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o, 64));
+    if (lane == 0) wmax[wave] = m;
+    __syncthreads();
+    m = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) m = max(m, wmax[w]);
+    amax = __uint_as_float(m << 16);
+  }
+  const EncCtx cx = make_ctx(amax, rtab);
+  const float g_dec = amax / kGMax;
+  const bool writer = blockIdx.x == 0;
+  if (writer && tid == 0) *a_g = g_dec;
+
+  // 4. encode into LDS (and, in workgroup 0, to the canonical output buffers)
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int b = tid + kThreads * j;
+    if (b < B) {
+      int row, col;
+      split_block(b, nb, inv_nb, row, col);
+      uint2 c;
+      const uint32_t sc = encode_bf16_block(xv[j][0], xv[j][1], cx, c);
+      *reinterpret_cast<uint2*>(lcodes + row * kDecCodeStride + col * 8) = c;
+      lscales[row * kDecScaleStride + col] = (uint8_t)sc;
+      if (writer) {
+        *reinterpret_cast<uint2*>(a_codes + (int64_t)row * (K / 2) + col * 8) = c;
+        a_scales[(int64_t)row * nb + col] = (uint8_t)sc;
+      }
+    }
+  }
+
+  // 5. remaining weight batches, then publish the LDS activations
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int u = PRE; u < U; ++u) {
+    const int t = min(wave + NW * u, tiles - 1);
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      wv[u][s] = *reinterpret_cast<const uint4*>(wc[s] + (int64_t)t * kChunkCodes);
+      wsc[u][s] = *reinterpret_cast<const uint16_t*>(ws[s] + (int64_t)t * kChunkScales);
+    }
+  }
   __syncthreads();
 
-  // output element e = (s, i, l): row 4 * (l / 16) + i, column (strip0 + s) * 16 + l % 16
-  const float ag = *a_g;
-  for (int e = threadIdx.x; e < S * 256; e += 64 * NW) {
-    const int s = e >> 8, i = (e >> 6) & 3, l = e & 63;
-    const int row = 4 * (l >> 4) + i;
-    const int n = (strip0 + s) * kStrip + (l & 15);
-    if (row >= M || n >= N) continue;
-    float v = 0.f;
+  // 6. MFMAs: lane (r, g) of tile t takes row r, k in [t * 128 + 32 g, + 32)
+  const int r = lane & 15, g = lane >> 4;
+  const int arow = min(r, M - 1);
+  const uint8_t* lc = lcodes + arow * kDecCodeStride + g * 16;
+  const uint8_t* ls = lscales + arow * kDecScaleStride + g * 2;
+  float4_t acc[S];
 #pragma unroll
-    for (int w = 0; w < NW; ++w) v += red[w][s][i][l];
-    out[(int64_t)row * ldo + n] = v * (ag * w_g[seg_of(st, n)]);
+  for (int s = 0; s < S; ++s) acc[s] = float4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int t = min(wave + NW * u, tiles - 1);
+    const int k0 = t * kTileK + 32 * g;
+    const bool live0 = (wave + NW * u < tiles) && (r < M) && (k0 < K);
+    const bool live1 = live0 && (k0 + kBlock < K);
+    const uint2 c0 = *reinterpret_cast<const uint2*>(lc + t * 64);
+    const uint2 c1 = *reinterpret_cast<const uint2*>(lc + t * 64 + 8);
+    const uint32_t sc = (live0 ? (uint32_t)ls[t * 8] : 0u) | (live1 ? (uint32_t)ls[t * 8 + 1] << 8 : 0u);
+    half8_t A[4];
+    decode_a(make_uint4(c0.x, c0.y, c1.x, c1.y), sc, 0xFFFFu, A);
+#pragma unroll
+    for (int s = 0; s < S; ++s) tile_mfma(A, wv[u][s], wsc[u][s], acc[s]);
   }
+  reduce_store<S, NW>(acc, red, strip0, M, N, st, g_dec, w_g, out, ldo);
 }
+
 
 __global__ void fill_zero_kernel(float* __restrict__ out, int M, int N, int64_t ldo) {
   const int64_t total = (int64_t)M * N;
@@ -188,19 +380,38 @@ hipError_t launch_fill_zero(float* out, int M, int N, int64_t ldo, hipStream_t s
   return hipGetLastError();
 }
 
+constexpr int kSkS = 3, kSkNW = 8, kSkU = 5;
+
 hipError_t launch_gemm_skinny(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_g, int M,
                               int K, const uint8_t* w_codes, const uint8_t* w_scales, int N,
                               const SegTable& st, const float* w_g, float* out, int64_t ldo,
                               hipStream_t stream) {
-  constexpr int S = 3, NW = 8, U = 5;
   const int nstrips = (N + kStrip - 1) / kStrip;
-  const int grid = (nstrips + S - 1) / S;
+  const int grid = (nstrips + kSkS - 1) / kSkS;
   if (K % 32 == 0)
-    gemm_skinny_kernel<S, NW, U, true><<<grid, 64 * NW, 0, stream>>>(a_codes, a_scales, a_g, M, K, w_codes,
-                                                                      w_scales, N, st, w_g, out, ldo);
+    gemm_skinny_kernel<kSkS, kSkNW, kSkU, true><<<grid, 64 * kSkNW, 0, stream>>>(
+        a_codes, a_scales, a_g, M, K, w_codes, w_scales, N, st, w_g, out, ldo);
   else
-    gemm_skinny_kernel<S, NW, U, false><<<grid, 64 * NW, 0, stream>>>(a_codes, a_scales, a_g, M, K, w_codes,
-                                                                       w_scales, N, st, w_g, out, ldo);
+    gemm_skinny_kernel<kSkS, kSkNW, kSkU, false><<<grid, 64 * kSkNW, 0, stream>>>(
+        a_codes, a_scales, a_g, M, K, w_codes, w_scales, N, st, w_g, out, ldo);
+  return hipGetLastError();
+}
+
+constexpr int kDecPre = 2;
+
+bool linear_decode_fits(int64_t M, int64_t K) {
+  return M >= 1 && M <= kDecMaxM && K >= kBlock && K <= kDecMaxK;
+}
+
+hipError_t launch_linear_decode(const uint16_t* x, int64_t ldx, const float* amax_in, uint8_t* a_codes,
+                                uint8_t* a_scales, float* a_g, int M, int K, const uint8_t* w_codes,
+                                const uint8_t* w_scales, int N, const SegTable& st, const float* w_g, float* out,
+                                int64_t ldo, hipStream_t stream) {
+  const int nstrips = (N + kStrip - 1) / kStrip;
+  const int grid = (nstrips + kSkS - 1) / kSkS;
+  linear_decode_kernel<kSkS, kSkNW, kSkU, kDecPre><<<grid, 64 * kSkNW, 0, stream>>>(
+      x, ldx, amax_in, a_codes, a_scales, a_g, M, K, 1.0f / (float)(K / kBlock), w_codes, w_scales, N, st, w_g, out,
+      ldo);
   return hipGetLastError();
 }
 

@@ -12,7 +12,8 @@
 // Work decomposition (HBM-bound: read 2 B, write 0.5625 B per element):
 //  * one thread encodes one 16-element block per loop trip: two 16-byte bf16
 //    loads (a wave reads 2 KB contiguous), block max on the bit patterns,
-//    two correctly rounded divisions per block, one multiply per element and
+//    two correctly rounded divisions per block (reciprocal multiply plus one
+//    fused-multiply-add correction), one multiply per element and
 //    the gfx950 fp4 converter (v_cvt_scalef32_pk_fp4_f32 with unit scale
 //    rounds to nearest even and saturates at 6, exactly the E2M1 rule);
 //  * dynamic amax of large tensors: a partial-max kernel writes one value per
@@ -24,6 +25,7 @@
 #include <algorithm>
 
 #include "common.hpp"
+#include "quant_device.hpp"
 
 namespace nvfp4 {
 
@@ -31,70 +33,12 @@ constexpr int kQThreads = 256;
 constexpr int kPartials = 1024;              // amax workgroups in the two-pass path
 constexpr int64_t kSmallElems = 1 << 17;     // single-launch path up to 128K elements
 
-// ---- block encoder ------------------------------------------------------------
-// x: the 16 values of one block as binary32 (exactly widened), bmax = max|x|.
-// Returns the E4M3 scale code; writes the 16 element codes (8 bytes) to out.
-__device__ __forceinline__ uint32_t encode_block(const float (&x)[16], float bmax, float g_enc,
-                                                 uint2& out) {
-  const float t = bmax / 6.0f;
-  const uint32_t sc = (t != 0.0f) ? e4m3_encode_rne_sat(t * g_enc) : 0u;
-  const float sdec = e4m3_value(sc);
-  // sdec == 0: every magnitude is 0; x * 0 keeps the sign bit, which the fp4
-  // converter then emits on its own.
-  const float rb = (sdec != 0.0f) ? g_enc / sdec : 0.0f;
-  float y[16];
-  if (__builtin_isinf(rb)) {
-    // g_enc overflowed (tensor maximum below ~1e-35): 0 * inf would be NaN,
-    // but a zero element encodes to magnitude 0.
-#pragma unroll
-    for (int i = 0; i < 16; ++i) y[i] = (x[i] == 0.0f) ? x[i] : x[i] * rb;
-  } else {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) y[i] = x[i] * rb;
-  }
-  uint32_t lo = 0, hi = 0;
-  lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo, y[0], y[1], 1.0f, 0);
-  lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo, y[2], y[3], 1.0f, 1);
-  lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo, y[4], y[5], 1.0f, 2);
-  lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo, y[6], y[7], 1.0f, 3);
-  hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi, y[8], y[9], 1.0f, 0);
-  hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi, y[10], y[11], 1.0f, 1);
-  hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi, y[12], y[13], 1.0f, 2);
-  hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi, y[14], y[15], 1.0f, 3);
-  out = make_uint2(lo, hi);
-  return sc;
-}
-
-// Per-tensor encode factor from amax; amax == 0 makes every block's scale 0.
-__device__ __forceinline__ float g_enc_of(float amax) {
-  return (amax == 0.0f) ? 0.0f : kGMax / amax;
-}
-
-// Encode one bf16 block given as two 16-byte chunks; writes 8 code bytes and 1 scale.
-__device__ __forceinline__ void encode_bf16_chunks(uint4 v0, uint4 v1, float g_enc, uint8_t* __restrict__ code_dst,
-                                                   uint8_t* __restrict__ scale_dst) {
-  const uint32_t d[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-  float xf[16];
-  uint32_t mb = 0;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    xf[2 * i] = __uint_as_float(d[i] << 16);
-    xf[2 * i + 1] = __uint_as_float(d[i] & 0xFFFF0000u);
-    mb = max(mb, max(d[i] & 0x7FFFu, (d[i] >> 16) & 0x7FFFu));
-  }
-  uint2 c;
-  const uint32_t sc = encode_block(xf, __uint_as_float(mb << 16), g_enc, c);
-  *reinterpret_cast<uint2*>(code_dst) = c;
-  *scale_dst = (uint8_t)sc;
-}
-
 // Encode the bf16 block (m, b) of x.
-__device__ __forceinline__ void encode_bf16_block(const uint16_t* __restrict__ x, int64_t ldx, int K,
-                                                  int64_t m, int b, float g_enc,
-                                                  uint8_t* __restrict__ codes,
-                                                  uint8_t* __restrict__ scales) {
+__device__ __forceinline__ void encode_block_at(const uint16_t* __restrict__ x, int64_t ldx, int K, int64_t m,
+                                                int b, const EncCtx& cx, uint8_t* __restrict__ codes,
+                                                uint8_t* __restrict__ scales) {
   const uint4* p = reinterpret_cast<const uint4*>(x + m * ldx + (int64_t)b * kBlock);
-  encode_bf16_chunks(p[0], p[1], g_enc, codes + m * (K / 2) + (int64_t)b * 8, scales + m * (K / kBlock) + b);
+  encode_bf16_chunks(p[0], p[1], cx, codes + m * (K / 2) + (int64_t)b * 8, scales + m * (K / kBlock) + b);
 }
 
 // ---- whole-tensor |x| maximum on bf16 bit patterns ------------------------------
@@ -116,18 +60,6 @@ __device__ __forceinline__ uint32_t chunk_absmax(const uint16_t* __restrict__ x,
   return m;
 }
 
-__device__ __forceinline__ uint32_t block_reduce_max(uint32_t v, uint32_t* red) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o, 64));
-  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
-  if (l == 0) red[w] = v;
-  __syncthreads();
-  uint32_t r = 0;
-  for (int i = 0; i < (int)(blockDim.x >> 6); ++i) r = max(r, red[i]);
-  __syncthreads();
-  return r;
-}
-
 __global__ __launch_bounds__(kQThreads) void amax_partial_kernel(const uint16_t* __restrict__ x, int64_t M,
                                                                  int K, int64_t ldx,
                                                                  uint32_t* __restrict__ partial) {
@@ -144,15 +76,18 @@ __global__ __launch_bounds__(kQThreads) void quantize_act_kernel(
     const uint32_t* __restrict__ partial, int nparts, const float* __restrict__ amax_in,
     uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, float* __restrict__ g_dec_out) {
   __shared__ uint32_t red[kQThreads / 64];
+  __shared__ float rtab[128];
+  fill_rcp_table(rtab);
   float amax;
   if (mode == 1) {
     amax = *amax_in;
+    __syncthreads();
   } else {
     uint32_t m = 0;
     for (int i = threadIdx.x; i < nparts; i += blockDim.x) m = max(m, partial[i]);
     amax = __uint_as_float(block_reduce_max(m, red) << 16);
   }
-  const float g_enc = g_enc_of(amax);
+  const EncCtx cx = make_ctx(amax, rtab);
   if (blockIdx.x == 0 && threadIdx.x == 0) *g_dec_out = amax / kGMax;
 
   const int nb = K / kBlock;
@@ -161,7 +96,7 @@ __global__ __launch_bounds__(kQThreads) void quantize_act_kernel(
        i += (int64_t)gridDim.x * blockDim.x) {
     const int64_t m = i / nb;
     const int b = (int)(i - m * nb);
-    encode_bf16_block(x, ldx, K, m, b, g_enc, codes, scales);
+    encode_block_at(x, ldx, K, m, b, cx, codes, scales);
   }
 }
 
@@ -179,6 +114,8 @@ __global__ __launch_bounds__(kSmallThreads) void quantize_act_small_kernel(
     const uint16_t* __restrict__ x, int M, int K, int64_t ldx, float inv_cpr, uint8_t* __restrict__ codes,
     uint8_t* __restrict__ scales, float* __restrict__ g_dec_out) {
   __shared__ uint32_t red[kSmallThreads / 64];
+  __shared__ float rtab[128];
+  fill_rcp_table(rtab);
   const int cpr = K / 8;
   const int total = M * cpr;
   uint4 v[16];
@@ -209,13 +146,13 @@ __global__ __launch_bounds__(kSmallThreads) void quantize_act_small_kernel(
     m = max(m, max(max(a0, a1), max(a2, a3)));
   }
   const float amax = __uint_as_float(block_reduce_max(m, red) << 16);
-  const float g_enc = g_enc_of(amax);
+  const EncCtx cx = make_ctx(amax, rtab);
   if (blockIdx.x == 0 && threadIdx.x == 0) *g_dec_out = amax / kGMax;
   const int nb = K / kBlock;
   const int i = blockIdx.x * kSmallThreads + threadIdx.x;
   if (i < M * nb) {
     const int row = i / nb, b = i - row * nb;
-    encode_bf16_chunks(v[0], v[1], g_enc, codes + (int64_t)row * (K / 2) + (int64_t)b * 8,
+    encode_bf16_chunks(v[0], v[1], cx, codes + (int64_t)row * (K / 2) + (int64_t)b * 8,
                        scales + (int64_t)row * nb + b);
   }
 }

@@ -134,13 +134,13 @@ def test_gemm_k_zero_and_m_zero():
     w = np.zeros((16, 0), np.float32)
     pw = gpu_pack(w, [(0, 16)])
     x = torch.zeros((3, 0), dtype=torch.bfloat16, device=DEV)
-    out = nv.linear(x, pw)
+    out, _ = nv.linear(x, pw)
     torch.cuda.synchronize()
     assert out.shape == (3, 16) and torch.all(out == 0)
     d = W.tiny()
     pw = gpu_pack(d.w, d.segments)
     x = torch.zeros((0, 256), dtype=torch.bfloat16, device=DEV)
-    out = nv.linear(x, pw)
+    out, _ = nv.linear(x, pw)
     assert out.shape == (0, 128)
 
 

@@ -1,0 +1,76 @@
+"""GPU parity of nvfp4_linear (quantize + GEMM in one call).  Decode-sized inputs
+(M <= 16, K <= 5120) run as one launch in which every GEMM workgroup encodes the
+activations itself; its results must be bit-identical to the separate
+nvfp4_quantize_act + nvfp4_gemm calls (codes, scales, g_dec and output) and
+within tolerance of the oracle.  Larger inputs take the two-kernel route and are
+held to the same bar."""
+import numpy as np
+import pytest
+import torch
+
+import nvfp4_w4a4_block_act_amd as nv
+import workloads as W
+from gpu_util import DEV, assert_within_tol, gpu_pack, oracle_linear_rows, say, to_dev_bf16
+from oracle import nvfp4 as Q
+
+pytestmark = pytest.mark.gpu
+
+
+def run_both(x_bits, pw, amax=None, ws=None):
+    x = to_dev_bf16(x_bits)
+    am = None if amax is None else torch.tensor([amax], dtype=torch.float32, device=DEV)
+    ws = ws if ws is not None else nv.Workspace(DEV)
+    out, (c, s, g) = nv.linear(x, pw, am, workspace=ws)
+    c2, s2, g2 = nv.quantize_act(x, am)
+    ref_out = nv.gemm(c2, s2, g2, pw)
+    torch.cuda.synchronize()
+    assert torch.equal(c, c2) and torch.equal(s, s2) and torch.equal(g, g2)
+    assert torch.equal(out, ref_out), "fused result differs from quantize + gemm"
+    return out, c.cpu().numpy(), s.cpu().numpy()
+
+
+@pytest.mark.parametrize("M", [1, 4, 16])
+def test_linear_decode_full(M):
+    d = W.decode(M=M)
+    say(f"[linear] decode M={M}")
+    pw = gpu_pack(d.w, d.segments)
+    ws = nv.Workspace(DEV)
+    for rep in range(3):                       # repeated calls give identical results
+        out, c, s = run_both(d.x_bits, pw, ws=ws)
+    ref, bnd = oracle_linear_rows(d.x_bits, d.w, d.segments)
+    assert_within_tol(out.cpu().numpy().astype(np.float64), ref, bnd, f"linear decode M={M}")
+    oc, os_, _, _ = Q.quantize(W.bf16_to_f32(d.x_bits))
+    assert np.array_equal(c, oc) and np.array_equal(s, os_)
+
+
+@pytest.mark.parametrize("M,N,K,nseg", [
+    (1, 16, 16, 1), (3, 37, 48, 2), (7, 200, 272, 3), (16, 129, 144, 2), (16, 520, 5136, 4), (5, 64, 4112, 1),
+    (16, 300, 17408, 2),
+])
+def test_linear_ragged(M, N, K, nseg):
+    rng = np.random.default_rng(M * 7 + N + K)
+    cuts = sorted(rng.choice(np.arange(1, N), nseg - 1, replace=False).tolist()) if nseg > 1 else []
+    bounds = [0] + cuts + [N]
+    segs = list(zip(bounds[:-1], bounds[1:]))
+    w = np.concatenate([(0.02 * (1 + i) * rng.standard_normal((e - b, K))).astype(np.float32)
+                        for i, (b, e) in enumerate(segs)])
+    x = W.random_act(M + 3 * N, M, K, "student_t")
+    say(f"[linear] ragged M={M} N={N} K={K}")
+    pw = gpu_pack(w, segs)
+    out, _, _ = run_both(x, pw)
+    ref, bnd = oracle_linear_rows(x, w, segs)
+    assert_within_tol(out.cpu().numpy().astype(np.float64), ref, bnd, f"linear ragged {M}x{K}x{N}")
+
+
+def test_linear_static_amax_and_prefill_path():
+    d = W.tiny()
+    pw = gpu_pack(d.w, d.segments)
+    amax = float(np.max(np.abs(W.bf16_to_f32(d.x_bits)))) / 4
+    out, c, s = run_both(d.x_bits, pw, amax=np.float32(amax))
+    oc, os_, _, _ = Q.quantize(W.bf16_to_f32(d.x_bits), np.float32(amax))
+    assert np.array_equal(c, oc) and np.array_equal(s, os_)
+    # M > 16 goes through the separate kernels
+    x = W.random_act(5, 40, 256, "normal")
+    out, _, _ = run_both(x, pw)
+    ref, bnd = oracle_linear_rows(x, d.w, d.segments)
+    assert_within_tol(out.cpu().numpy().astype(np.float64), ref, bnd, "linear prefill path")

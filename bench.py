@@ -34,7 +34,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=480)
     ap.add_argument("--warmup", type=int, default=48)
     ap.add_argument("--config", default="decode",
-                    choices=["decode", "prefill_gate_up", "gdn_in_proj", "down_proj", "down_proj_quantize", "tiny"])
+                    choices=["decode", "prefill_gate_up", "gdn_in_proj", "down_proj", "down_proj_quantize", "tiny",
+                             "copy_calibration"])
     ap.add_argument("--copies", type=int, default=16, help="device copies of the packed weight (decode)")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying HIP graphs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -57,6 +58,8 @@ def main():
 
     if args.config == "decode":
         res = bench_decode(args, torch, nv, W, dev)
+    elif args.config == "copy_calibration":
+        res = bench_copy(args, torch, dev)
     elif args.config == "down_proj_quantize":
         res = bench_quantize(args, torch, nv, W, dev)
     else:
@@ -65,6 +68,54 @@ def main():
 
 
 # ---------------------------------------------------------------------------------------
+PROFILES = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles")
+PKG_CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "nvfp4_w4a4_block_act_amd", "csrc")
+
+
+def source_digest(files):
+    import hashlib
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(PKG_CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(summary, files):
+    """HBM bytes per launch recorded by the rocprofv3 counter runs in profiles/<summary>
+    (FETCH_SIZE + WRITE_SIZE, each scaled by the copy-kernel calibration), or None when
+    the summary is missing or was taken on kernel sources other than the current ones."""
+    path = os.path.join(PROFILES, summary)
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as fh:
+        for line in fh:
+            if ":" in line and line.startswith("- "):
+                k, v = line[2:].split(":", 1)
+                vals[k.strip()] = v.strip().strip("`")
+    if vals.get("source_sha256") != source_digest(files):
+        return None
+    try:
+        return float(vals["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def bench_copy(args, torch, dev):
+    """A plain device-to-device copy of known size: the calibration run for the
+    FETCH_SIZE / WRITE_SIZE counters (one read and one write of 512 MiB per launch)."""
+    n = 512 << 20
+    src = torch.ones(n, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    sec, wall = time_region(torch, lambda i: dst.copy_(src), args.steps, args.warmup)
+    return {"metric": "device copy GB/s (counter calibration)", "value": round(2 * n * args.steps / sec / 1e9, 1),
+            "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": round(sec / args.steps * 1e3, 5), "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "u8", "data": "synthetic",
+            "config": {"workload": "copy_512MiB", "bytes_read_per_launch": n, "bytes_written_per_launch": n}}
+
+
 def to_dev_bf16(torch, bits, dev):
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
 
@@ -110,6 +161,10 @@ def cpu_threads():
 
 
 # ---------------------------------------------------------------------------------------
+DECODE_COUNTERS = "linear_decode_kernel_decode_k5120_n12288_counters.md"
+DECODE_SOURCES = ("gemm_skinny.hip", "quant_device.hpp", "common.hpp")
+
+
 def bench_decode(args, torch, nv, W, dev):
     Ms = (1, 4, 16)
     d16 = W.decode(M=16)
@@ -211,7 +266,10 @@ def bench_decode(args, torch, nv, W, dev):
                    "linear_kernel": {str(M): {k: round(v, 3) if isinstance(v, float) else v for k, v in kern[M].items()}
                                    for M in Ms}},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(DECODE_COUNTERS, DECODE_SOURCES),
+                     "traffic_unit": "bytes per launch (mean over the three token counts)",
+                     "algorithmic_bytes_per_launch": round(tot_b / len(Ms), 1),
                      "kernel": "linear_decode_kernel", "per_launch_bytes": {str(M): kern[M]["bytes"] for M in Ms}},
     }
     if not args.no_cpu_baseline:

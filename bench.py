@@ -138,8 +138,9 @@ def time_region(torch, fn, steps, warmup):
 
 
 def kernel_time_pairs(torch, launch, n, warmup=5):
-    """Average duration of one launch from HIP event pairs recorded around each launch
-    on the launch stream (torch's current stream, which the library launches on)."""
+    """Per-launch durations from HIP event pairs recorded around each launch on the launch
+    stream (torch's current stream, which the library launches on).  Returns seconds:
+    (mean, median, p10, p90)."""
     for i in range(warmup):
         launch(i)
     torch.cuda.synchronize()
@@ -150,7 +151,16 @@ def kernel_time_pairs(torch, launch, n, warmup=5):
         b.record()
     torch.cuda.synchronize()
     d = np.array([a.elapsed_time(b) for a, b in evs]) / 1e3
-    return float(np.mean(d)), float(np.median(d))
+    return float(np.mean(d)), float(np.median(d)), float(np.percentile(d, 10)), float(np.percentile(d, 90))
+
+
+def copy_bandwidth(torch, dev, nbytes=512 << 20, reps=20):
+    """Device-to-device copy GB/s (read + write), context for the HBM roofline."""
+    src = torch.ones(nbytes, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    sec, _ = time_region(torch, lambda i: dst.copy_(src), reps, 3)
+    del src, dst
+    return 2 * nbytes * reps / sec / 1e9
 
 
 def cpu_threads():
@@ -231,27 +241,42 @@ def bench_decode(args, torch, nv, W, dev):
     # dominant kernel: the one-launch decode linear (linear_decode_kernel), one per
     # call.  Per M, a graph of nc back-to-back calls (one per weight copy) is
     # replayed with a HIP event pair around each replay on the launch stream;
-    # average launch duration = event time / launches.  Algorithmic bytes per
-    # launch = weight codes+scales + bf16 activations + activation codes+scales
-    # written + fp32 output.
-    kern = {}
-    for M in Ms:
+    # per-launch duration = event time / nc.  Algorithmic bytes per launch =
+    # weight codes+scales + bf16 activations + activation codes+scales written +
+    # fp32 output.  The same is measured for two other forms of the call:
+    # the GEMM alone on pre-quantized activations, and the quantizer followed by
+    # the GEMM (two launches).
+    def per_launch(call):
         if args.no_graph:
-            launch = lambda i, M=M: [nv.linear(xs[M], copies[r], None, ws, out=outs[M], act_out=acts[M])
-                                     for r in range(nc)]
+            launch = lambda i: [call(r) for r in range(nc)]
         else:
             gg = torch.cuda.CUDAGraph()
             with torch.cuda.graph(gg):
                 for r in range(nc):
-                    nv.linear(xs[M], copies[r], None, ws, out=outs[M], act_out=acts[M])
+                    call(r)
             launch = lambda i, gg=gg: gg.replay()
-        mean, med = kernel_time_pairs(torch, launch, max(8, args.steps // nc))
-        mean, med = mean / nc, med / nc
+        return [v / nc for v in kernel_time_pairs(torch, launch, max(8, args.steps // nc))]
+
+    kern, forms = {}, {}
+    for M in Ms:
+        mean, med, p10, p90 = per_launch(
+            lambda r, M=M: nv.linear(xs[M], copies[r], None, ws, out=outs[M], act_out=acts[M]))
         kb = wbytes + 2 * M * K + M * K * 9 // 16 + 4 * M * N
-        kern[M] = {"mean_us": mean * 1e6, "median_us": med * 1e6, "bytes": kb, "GBps": kb / mean / 1e9}
+        kern[M] = {"mean_us": mean * 1e6, "median_us": med * 1e6, "p10_us": p10 * 1e6, "p90_us": p90 * 1e6,
+                   "bytes": kb, "GBps": kb / mean / 1e9}
+        c, sc, g = acts[M]
+        gemv = per_launch(lambda r, M=M, c=c, sc=sc, g=g: nv.gemm(c, sc, g, copies[r], out=outs[M]))
+        qg = per_launch(lambda r, M=M: nv.gemm(*nv.quantize_act(xs[M], None, ws, out=acts[M]), copies[r],
+                                               out=outs[M]))
+        gb = wbytes + M * K * 9 // 16 + 4 * M * N
+        forms[M] = {"gemm_only_us": round(gemv[0] * 1e6, 3), "gemm_only_GBps": round(gb / gemv[0] / 1e9, 1),
+                    "quantize_then_gemm_us": round(qg[0] * 1e6, 3),
+                    "quantize_then_gemm_GBps": round(kb / qg[0] / 1e9, 1),
+                    "one_launch_us": round(mean * 1e6, 3)}
     tot_b = sum(k["bytes"] for k in kern.values())
     tot_t = sum(k["mean_us"] for k in kern.values()) * 1e-6
     achieved = tot_b / tot_t / 1e9
+    copy_gbs = copy_bandwidth(torch, dev)
 
     res = {
         "metric": "NVFP4 W4A4 decode linear GB/s (quantize + GEMM + epilogue), % of MI355X HBM roofline",
@@ -264,7 +289,9 @@ def bench_decode(args, torch, nv, W, dev):
                    "segments": 1, "weight_copies": len(copies), "graphs": not args.no_graph,
                    "step_bytes": step_bytes, "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
                    "linear_kernel": {str(M): {k: round(v, 3) if isinstance(v, float) else v for k, v in kern[M].items()}
-                                   for M in Ms}},
+                                   for M in Ms},
+                   "call_forms": {str(M): forms[M] for M in Ms},
+                   "device_copy_GBps": round(copy_gbs, 1)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic(DECODE_COUNTERS, DECODE_SOURCES),
@@ -332,7 +359,7 @@ def bench_gemm(args, torch, nv, W, dev):
     sec, wall = time_region(torch, step, steps, min(args.warmup, 5))
     flops = 2.0 * M * N * K
     value = flops * steps / sec / 1e12
-    mean, med = kernel_time_pairs(torch, lambda i: nv.gemm(c, s, g, pw, out=out), max(8, steps // 2), 2)
+    mean, med, p10, p90 = kernel_time_pairs(torch, lambda i: nv.gemm(c, s, g, pw, out=out), max(8, steps // 2), 2)
     achieved = flops / mean / 1e12
     return {
         "metric": "NVFP4 W4A4 prefill GEMM TFLOP/s (quantize + GEMM + epilogue), % of MI355X fp16 MFMA roofline",
@@ -342,7 +369,8 @@ def bench_gemm(args, torch, nv, W, dev):
         "dtype_note": "NVFP4 operands decoded exactly to fp16, fp16 MFMA products, fp32 accumulation",
         "data": "synthetic",
         "config": {"workload": d.name, "M": M, "K": K, "N": N, "segments": len(d.segments),
-                   "gemm_kernel_mean_ms": round(mean * 1e3, 4), "gemm_kernel_median_ms": round(med * 1e3, 4)},
+                   "gemm_kernel_mean_ms": round(mean * 1e3, 4), "gemm_kernel_median_ms": round(med * 1e3, 4),
+                   "gemm_kernel_p10_ms": round(p10 * 1e3, 4), "gemm_kernel_p90_ms": round(p90 * 1e3, 4)},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": F16_MFMA_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / F16_MFMA_PEAK_TFLOPS, 4), "traffic": None,
                      "kernel": "gemm_mfma_kernel"},

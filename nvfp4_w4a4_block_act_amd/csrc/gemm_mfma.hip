@@ -35,6 +35,8 @@
 //  * workgroups are numbered XCD-major, then in groups of four row panels, so
 //    the 32 workgroups resident on an XCD share one activation slab in its L2
 //    while they stream weight column panels.
+#include <algorithm>
+
 #include "common.hpp"
 
 namespace nvfp4 {
@@ -167,11 +169,15 @@ __device__ __forceinline__ void mfma_half(const uint4* sa, const uint4* sw, cons
   }
 }
 
-template <bool AL16, bool AL4, bool TAIL>
+// One launch covers output columns [n_lo, n_hi) (n_lo a multiple of 256).  With
+// SPLIT, blockIdx.y selects one of gridDim.y contiguous slices of the k tiles and
+// the workgroup adds its scaled partial sums into `out` (zeroed beforehand) with
+// fp32 atomics; otherwise it stores them.
+template <bool AL16, bool AL4, bool TAIL, bool SPLIT>
 __global__ __launch_bounds__(kMfThreads, 1) void gemm_mfma_kernel(
     const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales, const float* __restrict__ a_g,
-    int M, int K, const uint8_t* __restrict__ w_codes, const uint8_t* __restrict__ w_scales, int N,
-    SegTable st, const float* __restrict__ w_g, float* __restrict__ out, int64_t ldo) {
+    int M, int K, const uint8_t* __restrict__ w_codes, const uint8_t* __restrict__ w_scales, int N, int n_lo,
+    int n_hi, SegTable st, const float* __restrict__ w_g, float* __restrict__ out, int64_t ldo) {
   __shared__ uint4 sW[2][kBN * kHalfRow];              // decoded weight half-tiles, 2 x 36 KB
   __shared__ uint4 sA[2][kBM * 4];                     // activation codes, 2 x 16 KB
 
@@ -180,9 +186,12 @@ __global__ __launch_bounds__(kMfThreads, 1) void gemm_mfma_kernel(
   const int wm = wave >> 1, wn = wave & 1;
   const int tiles = (K + kTileK - 1) / kTileK, full = K / kTileK;
   const int nstrips = (N + kStrip - 1) / kStrip;
+  // this workgroup's k tiles [tb, te)
+  const int tb = SPLIT ? (int)((int64_t)blockIdx.y * tiles / gridDim.y) : 0;
+  const int te = SPLIT ? (int)((int64_t)(blockIdx.y + 1) * tiles / gridDim.y) : tiles;
 
   // ---- workgroup -> output tile: XCD-major numbering, then grouped row panels
-  const int num_m = (M + kBM - 1) / kBM, num_n = (N + kBN - 1) / kBN;
+  const int num_m = (M + kBM - 1) / kBM, num_n = (n_hi - n_lo + kBN - 1) / kBN;
   const int nwg = num_m * num_n;
   int pid = blockIdx.x;
   if (nwg % 8 == 0) pid = (pid & 7) * (nwg >> 3) + (pid >> 3);
@@ -191,7 +200,7 @@ __global__ __launch_bounds__(kMfThreads, 1) void gemm_mfma_kernel(
   const int gsz = min(num_m - first_m, kGroupM);
   const int tm = first_m + (pid % per_group) % gsz;
   const int tn = (pid % per_group) / gsz;
-  const int m0 = tm * kBM, n0 = tn * kBN;
+  const int m0 = tm * kBM, n0 = n_lo + tn * kBN;
 
   // ---- activation code slots (coalesced loads) and this lane's scale rows
   ASlots as;
@@ -235,7 +244,7 @@ __global__ __launch_bounds__(kMfThreads, 1) void gemm_mfma_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[rt][c][r] = 0.f;
 
-  const int last = tiles - 1;
+  const int last = te - 1;
   const int kb = 64 * h;
   const int arow0 = wm * 64 + i;
   const int bbase = (wn * 128 + i) * kHalfRow + 4 * h;
@@ -244,11 +253,11 @@ __global__ __launch_bounds__(kMfThreads, 1) void gemm_mfma_kernel(
   RawW rw0, rw1;                                        // weights of tiles 0 and 1
   {
     uint4 a0[2];
-    load_a_codes<AL16, TAIL>(as, 0, full, K, a0);
-    load_a_scales<AL4, TAIL>(asp, 0, full, kb, K, sc0);
-    load_w_tile(ws, 0, rw0);
-    load_a_codes<AL16, TAIL>(as, min(1, last), full, K, an);
-    load_w_tile(ws, min(1, last), rw1);
+    load_a_codes<AL16, TAIL>(as, tb, full, K, a0);
+    load_a_scales<AL4, TAIL>(asp, tb, full, tb * kTileK + kb, K, sc0);
+    load_w_tile(ws, tb, rw0);
+    load_a_codes<AL16, TAIL>(as, min(tb + 1, last), full, K, an);
+    load_w_tile(ws, min(tb + 1, last), rw1);
 #pragma unroll
     for (int d = 0; d < 4; ++d) store_w_piece(ws, rw0, 0, d, sW[0]);
     sA[0][as.lds[0]] = a0[0];
@@ -267,9 +276,9 @@ __global__ __launch_bounds__(kMfThreads, 1) void gemm_mfma_kernel(
   // sets change roles through plain copies at its end.
   uint32_t scc[2] = {sc0[0], sc0[1]};
   RawW rwc = rw0, rwn = rw1;
-  for (int t = 0; t < tiles; ++t) {
-    const uint4* sa = sA[t & 1];
-    uint4* sa_next = sA[(t + 1) & 1];
+  for (int t = tb; t < te; ++t) {
+    const uint4* sa = sA[(t - tb) & 1];
+    uint4* sa_next = sA[(t - tb + 1) & 1];
     uint32_t scn[2];
     load_a_scales<AL4, TAIL>(asp, min(t + 1, last), full, min(t + 1, last) * kTileK + kb, K, scn);
     mfma_half<0>(sa, sW[0], scc, amask, arow0, bbase, h, ws, rwc, 1, sW[1], acc);
@@ -290,29 +299,57 @@ __global__ __launch_bounds__(kMfThreads, 1) void gemm_mfma_kernel(
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
     const int n = n0 + wn * 128 + 32 * c + i;
-    if (n >= N) continue;
+    if (n >= n_hi) continue;
     const float alpha = ag * w_g[seg_of(st, n)];
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int m = m0 + wm * 64 + rt * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-        if (m < M) out[(int64_t)m * ldo + n] = acc[rt][c][r] * alpha;
+        if (m < M) {
+          if constexpr (SPLIT)
+            unsafeAtomicAdd(out + (int64_t)m * ldo + n, acc[rt][c][r] * alpha);
+          else
+            out[(int64_t)m * ldo + n] = acc[rt][c][r] * alpha;
+        }
       }
   }
 }
 
+// Number of waves of 256 workgroups a launch of `tiles` workgroups takes.
+static int rounds(int64_t tiles) { return (int)((tiles + 255) / 256); }
+
 hipError_t launch_gemm_mfma(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_g, int M, int K,
                             const uint8_t* w_codes, const uint8_t* w_scales, int N, const SegTable& st,
                             const float* w_g, float* out, int64_t ldo, hipStream_t stream) {
-  const int grid = ((M + kBM - 1) / kBM) * ((N + kBN - 1) / kBN);
-#define NVFP4_MFMA_LAUNCH(A16, A4, T)                                                                            \
-  gemm_mfma_kernel<A16, A4, T><<<grid, kMfThreads, 0, stream>>>(a_codes, a_scales, a_g, M, K, w_codes, w_scales, \
-                                                                N, st, w_g, out, ldo)
-  if (K % kTileK == 0) NVFP4_MFMA_LAUNCH(true, true, false);
-  else if (K % 64 == 0) NVFP4_MFMA_LAUNCH(true, true, true);
-  else if (K % 32 == 0) NVFP4_MFMA_LAUNCH(true, false, true);
-  else NVFP4_MFMA_LAUNCH(false, false, true);
+  const int num_m = (M + kBM - 1) / kBM;
+  const int n_full = N / kBN * kBN;                    // columns covered by whole tiles
+  const int tiles = (K + kTileK - 1) / kTileK;
+  // A ragged last tile column costs a whole extra round of workgroups when the
+  // whole tiles fill their last round (e.g. 16 x 48 = 768 = 3 x 256): then the
+  // whole tiles run alone and the ragged column runs split along K, each part
+  // adding into the zeroed output with atomics.
+  int ksplit = 1;
+  if (n_full > 0 && n_full < N && rounds((int64_t)num_m * (n_full / kBN)) < rounds((int64_t)num_m * (N / kBN + 1)))
+    ksplit = std::max(1, std::min(tiles, 256 / num_m));
+  const int n_main = (ksplit > 1) ? n_full : N;
+  const int grid = num_m * ((n_main + kBN - 1) / kBN);
+#define NVFP4_MFMA_LAUNCH(A16, A4, T, SPLIT, GRID, NLO, NHI)                                                    \
+  gemm_mfma_kernel<A16, A4, T, SPLIT><<<GRID, kMfThreads, 0, stream>>>(a_codes, a_scales, a_g, M, K, w_codes,   \
+                                                                       w_scales, N, NLO, NHI, st, w_g, out, ldo)
+#define NVFP4_MFMA_DISPATCH(SPLIT, GRID, NLO, NHI)                                                               \
+  if (K % kTileK == 0) NVFP4_MFMA_LAUNCH(true, true, false, SPLIT, GRID, NLO, NHI);                             \
+  else if (K % 64 == 0) NVFP4_MFMA_LAUNCH(true, true, true, SPLIT, GRID, NLO, NHI);                             \
+  else if (K % 32 == 0) NVFP4_MFMA_LAUNCH(true, false, true, SPLIT, GRID, NLO, NHI);                            \
+  else NVFP4_MFMA_LAUNCH(false, false, true, SPLIT, GRID, NLO, NHI)
+  NVFP4_MFMA_DISPATCH(false, grid, 0, n_main);
+  if (ksplit > 1) {
+    const hipError_t e = launch_fill_zero(out + n_full, M, N - n_full, ldo, stream);
+    if (e != hipSuccess) return e;
+    const dim3 g2(num_m, ksplit);
+    NVFP4_MFMA_DISPATCH(true, g2, n_full, N);
+  }
+#undef NVFP4_MFMA_DISPATCH
 #undef NVFP4_MFMA_LAUNCH
   return hipGetLastError();
 }

@@ -86,16 +86,21 @@ __device__ __forceinline__ void decode_a(uint4 v, uint32_t sc, uint32_t amask, h
 
 // Cross-wave sum of the per-wave partial tiles and the epilogue: output element
 // e = (s, i, l) is row 4 * (l / 16) + i, column (strip0 + s) * 16 + l % 16, and is
-// stored as fl(sum * fl(a_g * w_g[seg(n)])).
+// stored as fl(sum * fl(a_g * w_g[seg(n)])).  The per-segment scales were loaded
+// at kernel start (wgv, thread t < nseg holds w_g[t]) so the epilogue does not
+// wait on memory behind the weight stream; they reach the other threads through
+// LDS with the partial tiles.
 template <int S, int NW>
-__device__ __forceinline__ void reduce_store(const float4_t (&acc)[S], float (&red)[NW][S][4][64], int strip0, int M,
-                                             int N, const SegTable& st, float ag, const float* __restrict__ w_g,
-                                             float* __restrict__ out, int64_t ldo) {
+__device__ __forceinline__ void reduce_store(const float4_t (&acc)[S], float (&red)[NW][S][4][64],
+                                             float (&swg)[NVFP4_MAX_SEGMENTS], float wgv, int strip0, int M,
+                                             int N, const SegTable& st, float ag, float* __restrict__ out,
+                                             int64_t ldo) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
   for (int s = 0; s < S; ++s)
 #pragma unroll
     for (int i = 0; i < 4; ++i) red[wave][s][i][lane] = acc[s][i];
+  if (threadIdx.x < (unsigned)st.nseg) swg[threadIdx.x] = wgv;
   __syncthreads();
   for (int e = threadIdx.x; e < S * 256; e += 64 * NW) {
     const int s = e >> 8, i = (e >> 6) & 3, l = e & 63;
@@ -105,8 +110,13 @@ __device__ __forceinline__ void reduce_store(const float4_t (&acc)[S], float (&r
     float v = 0.f;
 #pragma unroll
     for (int w = 0; w < NW; ++w) v += red[w][s][i][l];
-    out[(int64_t)row * ldo + n] = v * (ag * w_g[seg_of(st, n)]);
+    out[(int64_t)row * ldo + n] = v * (ag * swg[seg_of(st, n)]);
   }
+}
+
+// The caller's early load of the per-segment scales (see reduce_store).
+__device__ __forceinline__ float load_segment_scale(const float* __restrict__ w_g, const SegTable& st) {
+  return (threadIdx.x < (unsigned)st.nseg) ? w_g[threadIdx.x] : 0.0f;
 }
 
 // Weight pointers of lane `lane` for the S strips starting at strip0 (clamped;
@@ -133,6 +143,9 @@ __global__ __launch_bounds__(64 * NW) void gemm_skinny_kernel(
     int M, int K, const uint8_t* __restrict__ w_codes, const uint8_t* __restrict__ w_scales, int N,
     SegTable st, const float* __restrict__ w_g, float* __restrict__ out, int64_t ldo) {
   __shared__ float red[NW][S][4][64];
+  __shared__ float swg[NVFP4_MAX_SEGMENTS];
+  const float wgv = load_segment_scale(w_g, st);
+  const float ag = *a_g;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = lane & 15, g = lane >> 4;
@@ -193,7 +206,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_skinny_kernel(
       tile_mfma(A, w, wsv, acc[s]);
     }
   }
-  reduce_store<S, NW>(acc, red, strip0, M, N, st, *a_g, w_g, out, ldo);
+  reduce_store<S, NW>(acc, red, swg, wgv, strip0, M, N, st, ag, out, ldo);
 }
 
 // ---- decode-form linear layer in one launch (M <= 16, K <= 5120).
@@ -246,6 +259,8 @@ __global__ __launch_bounds__(64 * NW) void linear_decode_kernel(
   __shared__ __align__(16) uint8_t lscales[kDecMaxM * kDecScaleStride];
   __shared__ float rtab[128];
   __shared__ uint32_t wmax[NW];
+  __shared__ float swg[NVFP4_MAX_SEGMENTS];
+  const float wgv = load_segment_scale(w_g, st);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nb = K / kBlock;
@@ -363,7 +378,7 @@ __global__ __launch_bounds__(64 * NW) void linear_decode_kernel(
 #pragma unroll
     for (int s = 0; s < S; ++s) tile_mfma(A, wv[u][s], wsc[u][s], acc[s]);
   }
-  reduce_store<S, NW>(acc, red, strip0, M, N, st, g_dec, w_g, out, ldo);
+  reduce_store<S, NW>(acc, red, swg, wgv, strip0, M, N, st, g_dec, out, ldo);
 }
 
 

@@ -130,6 +130,22 @@ def test_gemm_subnormal_block_scales(M):
     check_linear(xb, w, [(0, 40), (40, N)], f"subnormal scales M={M}")
 
 
+@pytest.mark.parametrize("M,N,K", [(300, 32808, 1040), (40, 65584, 512)])
+def test_gemm_ragged_column_split_along_k(M, N, K):
+    """Shapes whose whole 256x256 tiles exactly fill their last round of 256
+    workgroups (2 x 128 and 1 x 256 tiles): the ragged last column then runs as a
+    separate launch split along K with atomic accumulation.  (300, 32808, 1040)
+    also has ragged rows and a k tail (K % 128 == 16)."""
+    rng = np.random.default_rng(M + N + K)
+    segs = [(0, 1000), (1000, N - 20), (N - 20, N)]
+    w = np.concatenate([(0.02 * (1 + 2 * i) * rng.standard_normal((e - b, K))).astype(np.float32)
+                        for i, (b, e) in enumerate(segs)])
+    x = W.random_act(M + K, M, K, "student_t")
+    rows = _sample(M, 12, rng, [0, M - 1])
+    cols = _sample(N, 300, rng, list(range(N - N % 256, N)) + [0, N - N % 256 - 1])
+    check_linear(x, w, segs, f"ragged column split M={M} N={N} K={K}", rows, cols)
+
+
 def test_gemm_k_zero_and_m_zero():
     w = np.zeros((16, 0), np.float32)
     pw = gpu_pack(w, [(0, 16)])

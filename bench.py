@@ -35,7 +35,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=48)
     ap.add_argument("--config", default="decode",
                     choices=["decode", "prefill_gate_up", "gdn_in_proj", "down_proj", "down_proj_quantize", "tiny",
-                             "copy_calibration"])
+                             "copy_calibration", "gdn_repair_compare"])
     ap.add_argument("--copies", type=int, default=16, help="device copies of the packed weight (decode)")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying HIP graphs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -60,6 +60,8 @@ def main():
         res = bench_decode(args, torch, nv, W, dev)
     elif args.config == "copy_calibration":
         res = bench_copy(args, torch, dev)
+    elif args.config == "gdn_repair_compare":
+        res = bench_repair(args, torch, nv, W, dev)
     elif args.config == "down_proj_quantize":
         res = bench_quantize(args, torch, nv, W, dev)
     else:
@@ -114,6 +116,46 @@ def bench_copy(args, torch, dev):
             "ms_per_step": round(sec / args.steps * 1e3, 5), "higher_is_better": True, "scaling": "weak",
             "vs_baseline": None, "dtype": "u8", "data": "synthetic",
             "config": {"workload": "copy_512MiB", "bytes_read_per_launch": n, "bytes_written_per_launch": n}}
+
+
+def bench_repair(args, torch, nv, W, dev):
+    """The two readings of the mismatch repair on the GDN in-projection (six modules,
+    amax ratio ~20): the per-segment epilogue (six FP32 scales, the library's default)
+    against re-encoding all modules with one shared scale (a single-segment GEMM).
+    Times both GEMMs and reports, per module, the relative RMS error of each output
+    against the unquantized float64 product over a sample of rows and columns."""
+    d = W.gdn_in_proj()
+    M, K, N = d.M, d.K, d.N
+    x = to_dev_bf16(torch, d.x_bits, dev)
+    c, s, g = nv.quantize_act(x)
+    w = torch.from_numpy(d.w).to(dev)
+    variants = {"per_segment": nv.pack_weight(w, d.segments), "shared": nv.pack_weight(w, [(0, N)])}
+    del w
+    out = torch.empty((M, N), dtype=torch.float32, device=dev)
+    rng = np.random.default_rng(0)
+    rows = np.sort(rng.choice(M, 64, replace=False))
+    cols = np.concatenate([np.sort(rng.choice(np.arange(b, e), min(e - b, 128), replace=False))
+                           for b, e in d.segments])
+    x32 = (d.x_bits.astype(np.uint32) << 16).view(np.float32)[rows].astype(np.float64)
+    y_ref = x32 @ d.w[cols].astype(np.float64).T
+    steps = max(1, args.steps)
+    res = {"metric": "NVFP4 W4A4 fused-GEMM repair comparison: per-segment epilogue vs shared-scale re-encode",
+           "value": None, "unit": "ms", "n_gpus": 1, "steps": steps, "warmup": min(args.warmup, 5),
+           "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": "f16", "data": "synthetic",
+           "config": {"workload": d.name, "M": M, "K": K, "N": N,
+                      "segments": [[int(b), int(e)] for b, e in d.segments]}}
+    for name, pw in variants.items():
+        sec, _ = time_region(torch, lambda i, pw=pw: nv.gemm(c, s, g, pw, out=out), steps, min(args.warmup, 5))
+        y = out.cpu().numpy().astype(np.float64)[rows][:, cols]
+        errs = []
+        for b, e in d.segments:
+            sel = (cols >= b) & (cols < e)
+            ref = y_ref[:, sel]
+            errs.append(round(float(np.sqrt(np.mean((y[:, sel] - ref) ** 2)) / np.sqrt(np.mean(ref ** 2))), 6))
+        res["config"][name] = {"gemm_ms": round(sec / steps * 1e3, 4), "rel_rms_error_per_module": errs}
+    res["value"] = res["config"]["per_segment"]["gemm_ms"]
+    res["ms_per_step"] = res["value"]
+    return res
 
 
 def to_dev_bf16(torch, bits, dev):

@@ -35,7 +35,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=48)
     ap.add_argument("--config", default="decode",
                     choices=["decode", "prefill_gate_up", "gdn_in_proj", "down_proj", "down_proj_quantize", "tiny",
-                             "copy_calibration", "gdn_repair_compare"])
+                             "copy_calibration", "gdn_repair_compare", "gate_up_swiglu"])
     ap.add_argument("--copies", type=int, default=16, help="device copies of the packed weight (decode)")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying HIP graphs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -62,6 +62,8 @@ def main():
         res = bench_copy(args, torch, dev)
     elif args.config == "gdn_repair_compare":
         res = bench_repair(args, torch, nv, W, dev)
+    elif args.config == "gate_up_swiglu":
+        res = bench_swiglu(args, torch, nv, W, dev)
     elif args.config == "down_proj_quantize":
         res = bench_quantize(args, torch, nv, W, dev)
     else:
@@ -156,6 +158,58 @@ def bench_repair(args, torch, nv, W, dev):
     res["value"] = res["config"]["per_segment"]["gemm_ms"]
     res["ms_per_step"] = res["value"]
     return res
+
+
+def bench_swiglu(args, torch, nv, W, dev):
+    """Gate+up projection of the prefill MLP (M = 8192, K = 5120, I = 17408) up to the
+    down projection's NVFP4 input, two ways: unfused (GEMM to fp32, SwiGLU to bf16,
+    activation quantizer with a calibrated maximum) and fused (the GEMM's epilogue emits
+    the NVFP4 codes directly).  The calibrated maximum is that of this batch's h, taken
+    from one unfused run before timing.  TFLOP/s counts the GEMM's 2 M N K."""
+    d = W.prefill_gate_up()
+    M, K, N = d.M, d.K, d.N
+    I = N // 2
+    x = to_dev_bf16(torch, d.x_bits, dev)
+    c, s, g = nv.quantize_act(x)
+    w = torch.from_numpy(d.w).to(dev)
+    pw = nv.pack_weight(w, d.segments)
+    pwi = nv.pack_weight_gate_up(w)
+    del w
+    gu = torch.empty((M, N), dtype=torch.float32, device=dev)
+    h = torch.empty((M, I), dtype=torch.bfloat16, device=dev)
+    hq = (torch.empty((M, I // 2), dtype=torch.uint8, device=dev), torch.empty((M, I // 16), dtype=torch.uint8,
+          device=dev), torch.empty(1, dtype=torch.float32, device=dev))
+    fq = (torch.empty_like(hq[0]), torch.empty_like(hq[1]), torch.empty_like(hq[2]))
+    nv.gemm(c, s, g, pw, out=gu)
+    nv.nvfp4_swiglu(gu, M, I, gu.stride(0), h, h.stride(0))
+    amax_h = h.float().abs().max().reshape(1).contiguous()
+    ws = nv.Workspace(dev)
+
+    def unfused(i):
+        nv.gemm(c, s, g, pw, out=gu)
+        nv.nvfp4_swiglu(gu, M, I, gu.stride(0), h, h.stride(0))
+        nv.quantize_act(h, amax_h, ws, out=hq)
+
+    def fused(i):
+        nv.gemm_swiglu_quantize(c, s, g, pwi, amax_h, out=fq)
+
+    steps = max(1, args.steps)
+    t_un, _ = time_region(torch, unfused, steps, min(args.warmup, 5))
+    t_fu, _ = time_region(torch, fused, steps, min(args.warmup, 5))
+    same = bool(torch.equal(fq[0], hq[0]) and torch.equal(fq[1], hq[1]) and torch.equal(fq[2], hq[2]))
+    flops = 2.0 * M * N * K
+    value = flops * steps / t_fu / 1e12
+    return {"metric": "NVFP4 W4A4 gate+up GEMM with fused SwiGLU -> NVFP4 epilogue TFLOP/s, % of MI355X fp16 MFMA roofline",
+            "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": steps, "warmup": min(args.warmup, 5),
+            "ms_per_step": round(t_fu / steps * 1e3, 4), "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "f16", "data": "synthetic",
+            "config": {"workload": "gate_up_swiglu_m8192_k5120_i17408", "M": M, "K": K, "I": I,
+                       "unfused_ms": round(t_un / steps * 1e3, 4), "fused_ms": round(t_fu / steps * 1e3, 4),
+                       "fused_equals_unfused": same,
+                       "hbm_bytes_avoided": M * N * 4 * 2 + M * I * 2 * 2},
+            "roofline": {"bound": "mfma", "achieved": round(value, 2), "peak": F16_MFMA_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(value / F16_MFMA_PEAK_TFLOPS, 4), "traffic": None,
+                         "kernel": "gemm_mfma_kernel (SwiGLU epilogue)"}}
 
 
 def to_dev_bf16(torch, bits, dev):

@@ -174,6 +174,51 @@ nvfp4_status nvfp4_linear(const void* x_bf16, int64_t M, int64_t K, int64_t ldx,
                           const nvfp4_segment* segs, const float* w_g_dec, int32_t nseg,
                           float* out, int64_t ldo, void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * Fused gate+up projection with the SwiGLU -> NVFP4 epilogue.
+ *
+ * Every linear layer is W4A4 (paper abstract), so the down projection's input
+ * h = silu(g) * u, formed from the gate (g) and up (u) projections of the MLP,
+ * is quantized on the fly too (Glonce article, "How to use it").  With a
+ * calibrated maximum of h (static mode; calibration-only PTQ, aiany page,
+ * "Who it's for") that quantization can run in the gate+up GEMM's epilogue,
+ * which then never writes the fp32 gate/up output:
+ *
+ *   g, u  = the two modules' outputs exactly as nvfp4_gemm computes them
+ *           (gate and up keep their own FP32 scales: the per-module repair);
+ *   h     = bf16(silu(g) * u), silu(z) = z / (1 + e^-z), evaluated in fp32
+ *           (round to nearest even to bf16);
+ *   codes, scales, g_dec = nvfp4_quantize_act(h, amax_in = amax_h).
+ * The result is bit-identical to nvfp4_gemm (unfused packing), nvfp4_swiglu
+ * and nvfp4_quantize_act run one after another.
+ * ------------------------------------------------------------------------- */
+
+/* Pack a gate+up weight pair for nvfp4_gemm_swiglu_quantize.  w is fp32
+ * [2I][K] (row stride ldw): rows [0, I) the gate module, [I, 2I) the up module,
+ * each encoded with its own maximum (w_g_dec[0] gate, w_g_dec[1] up, device).
+ * The packed layout is the tiled one of nvfp4_pack_weight for 2I rows taken in
+ * interleaved order (packed row n = module (n / 128) % 2, row (n / 256) * 128 +
+ * n % 128); sizes from nvfp4_packed_weight_bytes(2I, K).  Requires I % 128 == 0
+ * and K >= 16; workspace of nvfp4_pack_weight_workspace_bytes(2I, K, 2). */
+nvfp4_status nvfp4_pack_weight_gate_up(const float* w, int64_t I, int64_t K, int64_t ldw,
+                                       uint8_t* w_codes, uint8_t* w_scales, float* w_g_dec,
+                                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* h's NVFP4 codes [M][I/2], scales [M][I/16] (canonical layout) and g_dec
+ * (amax_h / 2688) from activations a (as for nvfp4_gemm) and a weight from
+ * nvfp4_pack_weight_gate_up.  amax_h: device pointer to the calibrated maximum
+ * of |h| (finite, >= 0; larger |h| saturate).  Requires I % 128 == 0, K >= 16. */
+nvfp4_status nvfp4_gemm_swiglu_quantize(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_g_dec,
+                                        int64_t M, int64_t K, const uint8_t* w_codes, const uint8_t* w_scales,
+                                        int64_t I, const float* w_g_dec, const float* amax_h,
+                                        uint8_t* h_codes, uint8_t* h_scales, float* h_g_dec, void* stream);
+
+/* The unfused SwiGLU step: h_bf16[m][j] = bf16(silu(gu[m][j]) * gu[m][I + j])
+ * for a gate+up output gu (fp32, row stride ldgu >= 2I; h row stride ldh >= I),
+ * with the arithmetic of the fused epilogue. */
+nvfp4_status nvfp4_swiglu(const float* gu, int64_t M, int64_t I, int64_t ldgu, void* h_bf16, int64_t ldh,
+                          void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -69,6 +69,13 @@ def _lib():
         lib.nvfp4_linear.restype = ctypes.c_int
         lib.nvfp4_linear.argtypes = [_vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _i64,
                                      ctypes.POINTER(Segment), _vp, ctypes.c_int32, _vp, _i64, _vp, _sz, _vp]
+        lib.nvfp4_pack_weight_gate_up.restype = ctypes.c_int
+        lib.nvfp4_pack_weight_gate_up.argtypes = [_vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _sz, _vp]
+        lib.nvfp4_gemm_swiglu_quantize.restype = ctypes.c_int
+        lib.nvfp4_gemm_swiglu_quantize.argtypes = [_vp, _vp, _vp, _i64, _i64, _vp, _vp, _i64, _vp, _vp, _vp, _vp,
+                                                   _vp, _vp]
+        lib.nvfp4_swiglu.restype = ctypes.c_int
+        lib.nvfp4_swiglu.argtypes = [_vp, _i64, _i64, _i64, _vp, _i64, _vp]
         _LIB = lib
     return _LIB
 
@@ -159,6 +166,24 @@ def nvfp4_linear(x, M, K, ldx, amax_in, a_codes, a_scales, a_g_dec, w_codes, w_s
     _check(_lib().nvfp4_linear(_ptr(x), M, K, ldx, _ptr(amax_in), _ptr(a_codes), _ptr(a_scales), _ptr(a_g_dec),
                                _ptr(w_codes), _ptr(w_scales), N, arr, _ptr(w_g_dec), n, _ptr(out), ldo,
                                _ptr(workspace), workspace_bytes, _stream(stream)), "nvfp4_linear")
+
+
+def nvfp4_pack_weight_gate_up(w, I, K, ldw, w_codes, w_scales, w_g_dec, workspace, workspace_bytes, stream=None):
+    _check(_lib().nvfp4_pack_weight_gate_up(_ptr(w), I, K, ldw, _ptr(w_codes), _ptr(w_scales), _ptr(w_g_dec),
+                                            _ptr(workspace), workspace_bytes, _stream(stream)),
+           "nvfp4_pack_weight_gate_up")
+
+
+def nvfp4_gemm_swiglu_quantize(a_codes, a_scales, a_g_dec, M, K, w_codes, w_scales, I, w_g_dec, amax_h,
+                               h_codes, h_scales, h_g_dec, stream=None):
+    _check(_lib().nvfp4_gemm_swiglu_quantize(_ptr(a_codes), _ptr(a_scales), _ptr(a_g_dec), M, K, _ptr(w_codes),
+                                             _ptr(w_scales), I, _ptr(w_g_dec), _ptr(amax_h), _ptr(h_codes),
+                                             _ptr(h_scales), _ptr(h_g_dec), _stream(stream)),
+           "nvfp4_gemm_swiglu_quantize")
+
+
+def nvfp4_swiglu(gu, M, I, ldgu, h, ldh, stream=None):
+    _check(_lib().nvfp4_swiglu(_ptr(gu), M, I, ldgu, _ptr(h), ldh, _stream(stream)), "nvfp4_swiglu")
 
 
 # ---- convenience layer: allocate with torch, call the C ABI --------------------------
@@ -270,3 +295,44 @@ def linear(x, pw, amax=None, workspace=None, out=None, act_out=None, stream=None
     nvfp4_linear(x, M, K, max(x.stride(0), K), amax, codes, scales, g, pw.codes, pw.scales, pw.N, pw.segments,
                  pw.g_dec, out, out.stride(0), buf, nbytes, stream)
     return out, (codes, scales, g)
+
+
+def pack_weight_gate_up(w, stream=None):
+    """fp32 [2I, K] (gate rows, then up rows) -> PackedWeight in the interleaved
+    gate/up layout, with the two modules' own scales (segments (0, I), (I, 2I))."""
+    assert w.dtype == torch.float32 and w.dim() == 2 and w.is_cuda and w.stride(1) == 1
+    N2, K = w.shape
+    I = N2 // 2
+    cb, sb = nvfp4_packed_weight_bytes(N2, K)
+    codes = _empty(cb, torch.uint8, w.device)
+    scales = _empty(sb, torch.uint8, w.device)
+    g = torch.empty(2, dtype=torch.float32, device=w.device)
+    need = nvfp4_pack_weight_workspace_bytes(N2, K, 2)
+    ws = torch.empty(max(need, 16), dtype=torch.uint8, device=w.device)
+    nvfp4_pack_weight_gate_up(w, I, K, w.stride(0), codes, scales, g, ws, ws.numel(), stream)
+    return PackedWeight(codes, scales, g, N2, K, [(0, I), (I, N2)])
+
+
+def gemm_swiglu_quantize(a_codes, a_scales, a_g_dec, pw, amax_h, out=None, stream=None):
+    """NVFP4 activations x interleaved gate/up weight -> NVFP4 of bf16(silu(g) * u):
+    (codes uint8 [M, I/2], scales uint8 [M, I/16], g_dec float32 [1])."""
+    M = a_codes.shape[0]
+    I = pw.N // 2
+    dev = a_codes.device
+    if out is None:
+        out = (torch.empty((M, I // 2), dtype=torch.uint8, device=dev),
+               torch.empty((M, I // 16), dtype=torch.uint8, device=dev),
+               torch.empty(1, dtype=torch.float32, device=dev))
+    c, s, g = out
+    nvfp4_gemm_swiglu_quantize(a_codes, a_scales, a_g_dec, M, pw.K, pw.codes, pw.scales, I, pw.g_dec, amax_h,
+                               c, s, g, stream)
+    return out
+
+
+def swiglu(gu, stream=None):
+    """fp32 [M, 2I] gate+up output -> bf16 [M, I] = bf16(silu(g) * u)."""
+    assert gu.dtype == torch.float32 and gu.dim() == 2 and gu.stride(1) == 1
+    M, N2 = gu.shape
+    h = torch.empty((M, N2 // 2), dtype=torch.bfloat16, device=gu.device)
+    nvfp4_swiglu(gu, M, N2 // 2, gu.stride(0), h, h.stride(0), stream)
+    return h

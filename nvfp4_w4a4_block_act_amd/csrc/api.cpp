@@ -226,4 +226,70 @@ nvfp4_status nvfp4_linear(const void* x_bf16, int64_t M, int64_t K, int64_t ldx,
                                           st, w_g_dec, out, ldo, s));
 }
 
+// ---- fused gate+up GEMM with the SwiGLU -> NVFP4 epilogue
+nvfp4_status nvfp4_pack_weight_gate_up(const float* w, int64_t I, int64_t K, int64_t ldw, uint8_t* w_codes,
+                                       uint8_t* w_scales, float* w_g_dec, void* workspace, size_t workspace_bytes,
+                                       void* stream) {
+  if (I < 1 || K < 0) return NVFP4_EINVAL;
+  if (I % 128 != 0 || K % 16 != 0 || K < 16 || 2 * I >= kMaxDim || K >= kMaxDim || ldw < K) return NVFP4_ESHAPE;
+  if (!w || !w_codes || !w_scales || !w_g_dec) return NVFP4_EINVAL;
+  if (!aligned16(w) || !aligned16(w_codes) || !aligned16(w_scales)) return NVFP4_EALIGN;
+  const size_t need = nvfp4::pack_weight_workspace(2 * I, K, 2);
+  if (!workspace || workspace_bytes < need) return NVFP4_EWORKSPACE;
+  size_t cb = 0, sb = 0;
+  nvfp4_packed_weight_bytes(2 * I, K, &cb, &sb);
+  const size_t wb = (size_t)((2 * I - 1) * ldw + K) * 4;
+  if (overlap(w, wb, w_codes, cb) || overlap(w, wb, w_scales, sb) || overlap(w_codes, cb, w_scales, sb) ||
+      overlap(workspace, need, w_codes, cb) || overlap(workspace, need, w_scales, sb) ||
+      overlap(w_g_dec, 8, w_codes, cb) || overlap(w_g_dec, 8, w_scales, sb) || overlap(w_g_dec, 8, w, wb))
+    return NVFP4_EINVAL;
+  return launched(nvfp4::launch_pack_weight_gate_up(w, I, K, ldw, w_codes, w_scales, w_g_dec, workspace,
+                                                    static_cast<hipStream_t>(stream)));
+}
+
+nvfp4_status nvfp4_gemm_swiglu_quantize(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_g_dec,
+                                        int64_t M, int64_t K, const uint8_t* w_codes, const uint8_t* w_scales,
+                                        int64_t I, const float* w_g_dec, const float* amax_h, uint8_t* h_codes,
+                                        uint8_t* h_scales, float* h_g_dec, void* stream) {
+  if (M < 0 || K < 0 || I < 1) return NVFP4_EINVAL;
+  if (I % 128 != 0 || K % 16 != 0 || K < 16 || M >= kMaxDim || K >= kMaxDim || 2 * I >= kMaxDim)
+    return NVFP4_ESHAPE;
+  if (!amax_h || !h_g_dec) return NVFP4_EINVAL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (M == 0) return launched(nvfp4::launch_quantize_act(nullptr, 0, 0, 0, amax_h, nullptr, nullptr, h_g_dec,
+                                                         nullptr, s));
+  if (!a_codes || !a_scales || !a_g_dec || !w_codes || !w_scales || !w_g_dec || !h_codes || !h_scales)
+    return NVFP4_EINVAL;
+  if (!aligned16(a_codes) || !aligned16(a_scales) || !aligned16(w_codes) || !aligned16(w_scales) ||
+      !aligned16(h_codes) || !aligned16(h_scales))
+    return NVFP4_EALIGN;
+  size_t cb = 0, sb = 0;
+  nvfp4_packed_weight_bytes(2 * I, K, &cb, &sb);
+  const size_t hcb = (size_t)(M * I / 2), hsb = (size_t)(M * I / 16);
+  const void* outs[3] = {h_codes, h_scales, h_g_dec};
+  const size_t osz[3] = {hcb, hsb, 4};
+  const void* ins[7] = {a_codes, a_scales, a_g_dec, w_codes, w_scales, w_g_dec, amax_h};
+  const size_t isz[7] = {(size_t)(M * K / 2), (size_t)(M * K / 16), 4, cb, sb, 8, 4};
+  for (int i = 0; i < 3; ++i) {
+    for (int j = 0; j < 7; ++j)
+      if (overlap(outs[i], osz[i], ins[j], isz[j])) return NVFP4_EINVAL;
+    for (int j = i + 1; j < 3; ++j)
+      if (overlap(outs[i], osz[i], outs[j], osz[j])) return NVFP4_EINVAL;
+  }
+  return launched(nvfp4::launch_gemm_swiglu_quantize(a_codes, a_scales, a_g_dec, (int)M, (int)K, w_codes, w_scales,
+                                                     (int)I, w_g_dec, amax_h, h_codes, h_scales, h_g_dec, s));
+}
+
+nvfp4_status nvfp4_swiglu(const float* gu, int64_t M, int64_t I, int64_t ldgu, void* h_bf16, int64_t ldh,
+                          void* stream) {
+  if (M < 0 || I < 0) return NVFP4_EINVAL;
+  if (M >= kMaxDim || I >= kMaxDim || ldgu < 2 * I || ldh < I) return NVFP4_ESHAPE;
+  if (M == 0 || I == 0) return NVFP4_OK;
+  if (!gu || !h_bf16) return NVFP4_EINVAL;
+  const size_t gb = (size_t)((M - 1) * ldgu + 2 * I) * 4, hb = (size_t)((M - 1) * ldh + I) * 2;
+  if (overlap(gu, gb, h_bf16, hb)) return NVFP4_EINVAL;
+  return launched(nvfp4::launch_swiglu(gu, M, I, ldgu, static_cast<uint16_t*>(h_bf16), ldh,
+                                       static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -143,4 +143,12 @@ hipError_t launch_gemm_mfma(const uint8_t* a_codes, const uint8_t* a_scales, con
                             int M, int K, const uint8_t* w_codes, const uint8_t* w_scales, int N,
                             const SegTable& st, const float* w_g, float* out, int64_t ldo,
                             hipStream_t stream);
+hipError_t launch_pack_weight_gate_up(const float* w, int64_t I, int64_t K, int64_t ldw, uint8_t* w_codes,
+                                      uint8_t* w_scales, float* w_g_dec, void* workspace, hipStream_t stream);
+hipError_t launch_gemm_swiglu_quantize(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_g, int M,
+                                       int K, const uint8_t* w_codes, const uint8_t* w_scales, int I,
+                                       const float* w_g, const float* amax_h, uint8_t* h_codes,
+                                       uint8_t* h_scales, float* h_g_dec, hipStream_t stream);
+hipError_t launch_swiglu(const float* gu, int64_t M, int64_t I, int64_t ldgu, uint16_t* h, int64_t ldh,
+                         hipStream_t stream);
 }  // namespace nvfp4

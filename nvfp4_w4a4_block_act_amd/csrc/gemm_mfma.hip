@@ -38,6 +38,7 @@
 #include <algorithm>
 
 #include "common.hpp"
+#include "quant_device.hpp"
 
 namespace nvfp4 {
 
@@ -134,10 +135,17 @@ __device__ __forceinline__ void store_w_piece(const WSlots& ws, const RawW& r, i
   stage[ws.lds + d] = __builtin_bit_cast(uint4, decode8(w, scale_pair(sc)));
 }
 
+// Column offset (inside the wave's column base) of the wave's MFMA column tile c.
+// Plain: four adjacent 32-column tiles.  Gate/up (SW): tiles 0, 1 are 64 gate
+// columns and tiles 2, 3 the 64 up columns 128 further on, so each lane holds the
+// gate and up values of the same output element.
+template <bool SW>
+__device__ __forceinline__ constexpr int wtile_col(int c) { return SW ? (c >> 1) * 128 + (c & 1) * 32 : 32 * c; }
+
 // Four MFMA steps (one half-tile, global steps 4 * HALF .. 4 * HALF + 3) on the
 // activation codes of LDS stage `sa` and the decoded weights of half-stage `sw`,
 // while one weight piece per step of the next half-tile is decoded into `sw_next`.
-template <int HALF>
+template <int HALF, bool SW>
 __device__ __forceinline__ void mfma_half(const uint4* sa, const uint4* sw, const uint32_t (&asc)[2],
                                           const uint32_t (&amask)[2], int arow0, int bbase, int h,
                                           const WSlots& ws, const RawW& wstore, int wslot, uint4* sw_next,
@@ -159,7 +167,7 @@ __device__ __forceinline__ void mfma_half(const uint4* sa, const uint4* sw, cons
     }
 #pragma unroll
     for (int c = 0; c < 4; ++c)
-      bf[c] = __builtin_bit_cast(half8_t, sw[bbase + 32 * c * kHalfRow + jj]);
+      bf[c] = __builtin_bit_cast(half8_t, sw[bbase + wtile_col<SW>(c) * kHalfRow + jj]);
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
@@ -169,15 +177,47 @@ __device__ __forceinline__ void mfma_half(const uint4* sa, const uint4* sw, cons
   }
 }
 
+// Epilogues of the MFMA GEMM.
+enum MfmaEpilogue : int {
+  kEpiStore = 0,     // out[m][n] = acc * fl(a_g * w_g[seg(n)])
+  kEpiSplitK = 1,    // same value, added into `out` with fp32 atomics (K split across launches' y)
+  kEpiSwiglu = 2,    // gate/up weights interleaved; emit NVFP4(bf16(silu(g) * u)) instead of fp32
+};
+
+// Outputs of the SwiGLU -> NVFP4 epilogue: the down projection's activations.
+struct SwigluOut {
+  const float* amax;   // calibrated maximum of h (device scalar)
+  uint8_t* codes;      // [M][I/2] canonical
+  uint8_t* scales;     // [M][I/16]
+  float* g_dec;        // amax / 2688
+  int I;               // intermediate size (gate rows = up rows = I)
+};
+
+// bf16 bits of a finite float (round to nearest even).
+__device__ __forceinline__ uint16_t bf16_rne(float f) {
+  const uint32_t b = __float_as_uint(f);
+  return (uint16_t)((b + 0x7FFFu + ((b >> 16) & 1u)) >> 16);
+}
+
+// The MLP's gate nonlinearity on fp32 values: h = silu(g) * u, silu(z) = z / (1 + e^-z).
+__device__ __forceinline__ float swiglu_f32(float g, float u) { return g / (1.0f + expf(-g)) * u; }
+
+constexpr int kHRow = 128 + 8;   // bf16 per LDS row of the SwiGLU tile (16-byte pad)
+
 // One launch covers output columns [n_lo, n_hi) (n_lo a multiple of 256).  With
-// SPLIT, blockIdx.y selects one of gridDim.y contiguous slices of the k tiles and
-// the workgroup adds its scaled partial sums into `out` (zeroed beforehand) with
-// fp32 atomics; otherwise it stores them.
-template <bool AL16, bool AL4, bool TAIL, bool SPLIT>
+// kEpiSplitK, blockIdx.y selects one of gridDim.y contiguous slices of the k
+// tiles and the workgroup adds its scaled partial sums into `out` (zeroed
+// beforehand) with fp32 atomics.  With kEpiSwiglu the weight is the interleaved
+// gate/up packing (columns 256 t .. 256 t + 127 are gate rows 128 t .., the next
+// 128 the matching up rows), and the workgroup writes the NVFP4 encoding of
+// h[m][j] = bf16(silu(g) * u) for its 128 j instead of fp32 output.
+template <bool AL16, bool AL4, bool TAIL, int EPI>
 __global__ __launch_bounds__(kMfThreads, 1) void gemm_mfma_kernel(
     const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales, const float* __restrict__ a_g,
     int M, int K, const uint8_t* __restrict__ w_codes, const uint8_t* __restrict__ w_scales, int N, int n_lo,
-    int n_hi, SegTable st, const float* __restrict__ w_g, float* __restrict__ out, int64_t ldo) {
+    int n_hi, SegTable st, const float* __restrict__ w_g, float* __restrict__ out, int64_t ldo, SwigluOut so) {
+  constexpr bool SPLIT = EPI == kEpiSplitK;
+  constexpr bool SW = EPI == kEpiSwiglu;
   __shared__ uint4 sW[2][kBN * kHalfRow];              // decoded weight half-tiles, 2 x 36 KB
   __shared__ uint4 sA[2][kBM * 4];                     // activation codes, 2 x 16 KB
 
@@ -247,7 +287,7 @@ __global__ __launch_bounds__(kMfThreads, 1) void gemm_mfma_kernel(
   const int last = te - 1;
   const int kb = 64 * h;
   const int arow0 = wm * 64 + i;
-  const int bbase = (wn * 128 + i) * kHalfRow + 4 * h;
+  const int bbase = (wn * (SW ? 64 : 128) + i) * kHalfRow + 4 * h;
   uint4 an[2];                                          // activation codes in flight (next tile)
   uint32_t sc0[2];                                      // activation scales of tile 0
   RawW rw0, rw1;                                        // weights of tiles 0 and 1
@@ -281,12 +321,12 @@ __global__ __launch_bounds__(kMfThreads, 1) void gemm_mfma_kernel(
     uint4* sa_next = sA[(t - tb + 1) & 1];
     uint32_t scn[2];
     load_a_scales<AL4, TAIL>(asp, min(t + 1, last), full, min(t + 1, last) * kTileK + kb, K, scn);
-    mfma_half<0>(sa, sW[0], scc, amask, arow0, bbase, h, ws, rwc, 1, sW[1], acc);
+    mfma_half<0, SW>(sa, sW[0], scc, amask, arow0, bbase, h, ws, rwc, 1, sW[1], acc);
     sa_next[as.lds[0]] = an[0];
     sa_next[as.lds[1]] = an[1];
     load_a_codes<AL16, TAIL>(as, min(t + 2, last), full, K, an);
     __syncthreads();
-    mfma_half<1>(sa, sW[1], scc, amask, arow0, bbase, h, ws, rwn, 0, sW[0], acc);
+    mfma_half<1, SW>(sa, sW[1], scc, amask, arow0, bbase, h, ws, rwn, 0, sW[0], acc);
     rwc = rwn;
     load_w_tile(ws, min(t + 2, last), rwn);
     scc[0] = scn[0];
@@ -296,6 +336,45 @@ __global__ __launch_bounds__(kMfThreads, 1) void gemm_mfma_kernel(
 
   // ---- epilogue: lane holds rows 8*(r/4) + 4*h + r%4, column i of each 32x32 tile
   const float ag = *a_g;
+  if constexpr (SW) {
+    // h = bf16(silu(g) * u) for the tile's 256 rows x 128 j, staged in LDS (the
+    // weight stages are free once every wave has left the loop), then encoded
+    // block by block exactly as the activation quantizer encodes a bf16 tensor.
+    uint16_t* hs = reinterpret_cast<uint16_t*>(&sW[0][0]);
+    float* rtab = reinterpret_cast<float*>(&sA[0][0]);
+    const float alpha_g = ag * w_g[0], alpha_u = ag * w_g[1];
+    __syncthreads();
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int ml = wm * 64 + rt * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+          const int jl = wn * 64 + 32 * c + i;
+          hs[ml * kHRow + jl] = bf16_rne(swiglu_f32(acc[rt][c][r] * alpha_g, acc[rt][c + 2][r] * alpha_u));
+        }
+    fill_rcp_table(rtab);
+    __syncthreads();
+    const float amax = *so.amax;
+    const EncCtx cx = make_ctx(amax, rtab);
+    if (blockIdx.x == 0 && tid == 0) *so.g_dec = amax / kGMax;
+    const int j0 = n0 / 2;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int b = tid + kMfThreads * q;          // 256 rows x 8 blocks of 16 j
+      const int row = b >> 3, jb = b & 7;
+      const int m = m0 + row;
+      if (m >= M) continue;
+      const uint4* src = reinterpret_cast<const uint4*>(hs + row * kHRow + jb * 16);
+      uint2 cw;
+      const uint32_t sc = encode_bf16_block(src[0], src[1], cx, cw);
+      const int64_t j = j0 + jb * 16;
+      *reinterpret_cast<uint2*>(so.codes + (int64_t)m * (so.I / 2) + j / 2) = cw;
+      so.scales[(int64_t)m * (so.I / kBlock) + j / kBlock] = (uint8_t)sc;
+    }
+    return;
+  }
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
     const int n = n0 + wn * 128 + 32 * c + i;
@@ -316,6 +395,27 @@ __global__ __launch_bounds__(kMfThreads, 1) void gemm_mfma_kernel(
   }
 }
 
+// ---- unfused SwiGLU of a gate+up output (columns [0, I) gate, [I, 2I) up) to bf16,
+// with the same fp32 arithmetic as the fused epilogue.
+__global__ void swiglu_kernel(const float* __restrict__ gu, int64_t M, int I, int64_t ldgu,
+                              uint16_t* __restrict__ hout, int64_t ldh) {
+  const int64_t total = M * I;
+  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total; e += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t m = e / I;
+    const int j = (int)(e - m * I);
+    hout[m * ldh + j] = bf16_rne(swiglu_f32(gu[m * ldgu + j], gu[m * ldgu + I + j]));
+  }
+}
+
+hipError_t launch_swiglu(const float* gu, int64_t M, int64_t I, int64_t ldgu, uint16_t* h, int64_t ldh,
+                         hipStream_t stream) {
+  const int64_t total = M * I;
+  if (total == 0) return hipSuccess;
+  const int grid = (int)std::min<int64_t>((total + 255) / 256, 256 * 16);
+  swiglu_kernel<<<grid, 256, 0, stream>>>(gu, M, (int)I, ldgu, h, ldh);
+  return hipGetLastError();
+}
+
 // Number of waves of 256 workgroups a launch of `tiles` workgroups takes.
 static int rounds(int64_t tiles) { return (int)((tiles + 255) / 256); }
 
@@ -334,23 +434,47 @@ hipError_t launch_gemm_mfma(const uint8_t* a_codes, const uint8_t* a_scales, con
     ksplit = std::max(1, std::min(tiles, 256 / num_m));
   const int n_main = (ksplit > 1) ? n_full : N;
   const int grid = num_m * ((n_main + kBN - 1) / kBN);
-#define NVFP4_MFMA_LAUNCH(A16, A4, T, SPLIT, GRID, NLO, NHI)                                                    \
-  gemm_mfma_kernel<A16, A4, T, SPLIT><<<GRID, kMfThreads, 0, stream>>>(a_codes, a_scales, a_g, M, K, w_codes,   \
-                                                                       w_scales, N, NLO, NHI, st, w_g, out, ldo)
-#define NVFP4_MFMA_DISPATCH(SPLIT, GRID, NLO, NHI)                                                               \
-  if (K % kTileK == 0) NVFP4_MFMA_LAUNCH(true, true, false, SPLIT, GRID, NLO, NHI);                             \
-  else if (K % 64 == 0) NVFP4_MFMA_LAUNCH(true, true, true, SPLIT, GRID, NLO, NHI);                             \
-  else if (K % 32 == 0) NVFP4_MFMA_LAUNCH(true, false, true, SPLIT, GRID, NLO, NHI);                            \
-  else NVFP4_MFMA_LAUNCH(false, false, true, SPLIT, GRID, NLO, NHI)
-  NVFP4_MFMA_DISPATCH(false, grid, 0, n_main);
+#define NVFP4_MFMA_LAUNCH(A16, A4, T, EPI, GRID, NLO, NHI)                                                      \
+  gemm_mfma_kernel<A16, A4, T, EPI><<<GRID, kMfThreads, 0, stream>>>(a_codes, a_scales, a_g, M, K, w_codes,     \
+                                                                     w_scales, N, NLO, NHI, st, w_g, out, ldo,  \
+                                                                     SwigluOut{})
+#define NVFP4_MFMA_DISPATCH(EPI, GRID, NLO, NHI)                                                                 \
+  if (K % kTileK == 0) NVFP4_MFMA_LAUNCH(true, true, false, EPI, GRID, NLO, NHI);                               \
+  else if (K % 64 == 0) NVFP4_MFMA_LAUNCH(true, true, true, EPI, GRID, NLO, NHI);                               \
+  else if (K % 32 == 0) NVFP4_MFMA_LAUNCH(true, false, true, EPI, GRID, NLO, NHI);                              \
+  else NVFP4_MFMA_LAUNCH(false, false, true, EPI, GRID, NLO, NHI)
+  NVFP4_MFMA_DISPATCH(kEpiStore, grid, 0, n_main);
   if (ksplit > 1) {
     const hipError_t e = launch_fill_zero(out + n_full, M, N - n_full, ldo, stream);
     if (e != hipSuccess) return e;
     const dim3 g2(num_m, ksplit);
-    NVFP4_MFMA_DISPATCH(true, g2, n_full, N);
+    NVFP4_MFMA_DISPATCH(kEpiSplitK, g2, n_full, N);
   }
 #undef NVFP4_MFMA_DISPATCH
 #undef NVFP4_MFMA_LAUNCH
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_swiglu_quantize(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_g, int M,
+                                       int K, const uint8_t* w_codes, const uint8_t* w_scales, int I,
+                                       const float* w_g, const float* amax_h, uint8_t* h_codes,
+                                       uint8_t* h_scales, float* h_g_dec, hipStream_t stream) {
+  const int N = 2 * I;
+  const int grid = ((M + kBM - 1) / kBM) * (N / kBN);
+  SegTable st{};
+  st.nseg = 2;
+  st.end[0] = I;
+  st.end[1] = N;
+  const SwigluOut so{amax_h, h_codes, h_scales, h_g_dec, I};
+#define NVFP4_SWIGLU_LAUNCH(A16, A4, T)                                                                          \
+  gemm_mfma_kernel<A16, A4, T, kEpiSwiglu><<<grid, kMfThreads, 0, stream>>>(a_codes, a_scales, a_g, M, K,        \
+                                                                            w_codes, w_scales, N, 0, N, st, w_g, \
+                                                                            nullptr, 0, so)
+  if (K % kTileK == 0) NVFP4_SWIGLU_LAUNCH(true, true, false);
+  else if (K % 64 == 0) NVFP4_SWIGLU_LAUNCH(true, true, true);
+  else if (K % 32 == 0) NVFP4_SWIGLU_LAUNCH(true, false, true);
+  else NVFP4_SWIGLU_LAUNCH(false, false, true);
+#undef NVFP4_SWIGLU_LAUNCH
   return hipGetLastError();
 }
 

@@ -217,9 +217,13 @@ __global__ __launch_bounds__(kQThreads) void seg_amax_kernel(const float* __rest
   if (threadIdx.x == 0) partial[s * kSegParts + blockIdx.x] = r;
 }
 
-// One thread per 16-element block of the padded Np x Kp weight.
+// One thread per 16-element block of the padded Np x Kp weight.  With ilv = I > 0
+// the weight is a fused gate+up pair (rows [0, I) gate, [I, 2I) up, segments 0
+// and 1) packed interleaved: packed row n holds module (n / 128) % 2, row
+// (n / 256) * 128 + n % 128 of it, so every 256-row tile pairs 128 gate rows
+// with the matching 128 up rows.
 __global__ __launch_bounds__(kQThreads) void pack_weight_kernel(
-    const float* __restrict__ w, int N, int K, int64_t ldw, int Np, int Kp, SegTable st,
+    const float* __restrict__ w, int N, int K, int64_t ldw, int Np, int Kp, SegTable st, int ilv,
     const uint32_t* __restrict__ partial, uint8_t* __restrict__ w_codes, uint8_t* __restrict__ w_scales,
     float* __restrict__ w_g_dec) {
   __shared__ float s_genc[NVFP4_MAX_SEGMENTS];
@@ -240,8 +244,10 @@ __global__ __launch_bounds__(kQThreads) void pack_weight_kernel(
     const int b = (int)(i - (int64_t)n * nbk);
     uint2 c = make_uint2(0u, 0u);
     uint32_t sc = 0;
+    const int mod = (n >> 7) & 1;
+    const int src = ilv ? mod * ilv + ((n >> 8) << 7) + (n & 127) : n;
     if (n < N && b * kBlock < K) {
-      const float* p = w + (int64_t)n * ldw + (int64_t)b * kBlock;
+      const float* p = w + (int64_t)src * ldw + (int64_t)b * kBlock;
       float xf[16];
       float bmax = 0.0f;
 #pragma unroll
@@ -249,7 +255,7 @@ __global__ __launch_bounds__(kQThreads) void pack_weight_kernel(
         xf[j] = p[j];
         bmax = fmaxf(bmax, fabsf(xf[j]));
       }
-      sc = encode_block(xf, bmax, s_genc[seg_of(st, n)], c);
+      sc = encode_block(xf, bmax, s_genc[ilv ? mod : seg_of(st, n)], c);
     }
     const int64_t chunk = (int64_t)(n / kStrip) * tiles + b / (kTileK / kBlock);
     const int r = n % kStrip, bb = b % (kTileK / kBlock);   // block bb of the chunk: group bb / 2
@@ -281,6 +287,19 @@ size_t pack_weight_workspace(int64_t, int64_t, int nseg) {
   return (size_t)nseg * kSegParts * sizeof(uint32_t);
 }
 
+static hipError_t pack_weight_impl(const float* w, int64_t N, int64_t K, int64_t ldw, const SegTable& st,
+                                   int ilv, uint8_t* w_codes, uint8_t* w_scales, float* w_g_dec, void* workspace,
+                                   hipStream_t stream) {
+  uint32_t* partial = static_cast<uint32_t*>(workspace);
+  seg_amax_kernel<<<dim3(kSegParts, st.nseg), kQThreads, 0, stream>>>(w, (int)K, ldw, st, partial);
+  const int64_t Np = round_up(N, kStrip), Kp = round_up(K, kTileK);
+  const int64_t total = Np * (Kp / kBlock);
+  const int grid = (int)std::max<int64_t>(1, std::min<int64_t>((total + kQThreads - 1) / kQThreads, 256 * 16));
+  pack_weight_kernel<<<grid, kQThreads, 0, stream>>>(w, (int)N, (int)K, ldw, (int)Np, (int)Kp, st, ilv, partial,
+                                                     w_codes, w_scales, w_g_dec);
+  return hipGetLastError();
+}
+
 hipError_t launch_pack_weight(const float* w, int64_t N, int64_t K, int64_t ldw,
                               const nvfp4_segment* segs, int nseg, uint8_t* w_codes,
                               uint8_t* w_scales, float* w_g_dec, void* workspace,
@@ -288,14 +307,16 @@ hipError_t launch_pack_weight(const float* w, int64_t N, int64_t K, int64_t ldw,
   SegTable st{};
   st.nseg = nseg;
   for (int i = 0; i < nseg; ++i) st.end[i] = segs[i].n_end;
-  uint32_t* partial = static_cast<uint32_t*>(workspace);
-  seg_amax_kernel<<<dim3(kSegParts, nseg), kQThreads, 0, stream>>>(w, (int)K, ldw, st, partial);
-  const int64_t Np = round_up(N, kStrip), Kp = round_up(K, kTileK);
-  const int64_t total = Np * (Kp / kBlock);
-  const int grid = (int)std::max<int64_t>(1, std::min<int64_t>((total + kQThreads - 1) / kQThreads, 256 * 16));
-  pack_weight_kernel<<<grid, kQThreads, 0, stream>>>(w, (int)N, (int)K, ldw, (int)Np, (int)Kp, st, partial,
-                                                     w_codes, w_scales, w_g_dec);
-  return hipGetLastError();
+  return pack_weight_impl(w, N, K, ldw, st, 0, w_codes, w_scales, w_g_dec, workspace, stream);
+}
+
+hipError_t launch_pack_weight_gate_up(const float* w, int64_t I, int64_t K, int64_t ldw, uint8_t* w_codes,
+                                      uint8_t* w_scales, float* w_g_dec, void* workspace, hipStream_t stream) {
+  SegTable st{};
+  st.nseg = 2;
+  st.end[0] = (int32_t)I;
+  st.end[1] = (int32_t)(2 * I);
+  return pack_weight_impl(w, 2 * I, K, ldw, st, (int)I, w_codes, w_scales, w_g_dec, workspace, stream);
 }
 
 hipError_t launch_weight_to_canonical(const uint8_t* w_codes, const uint8_t* w_scales, int64_t N,

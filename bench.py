@@ -35,7 +35,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=48)
     ap.add_argument("--config", default="decode",
                     choices=["decode", "prefill_gate_up", "gdn_in_proj", "down_proj", "down_proj_quantize", "tiny",
-                             "copy_calibration", "gdn_repair_compare", "gate_up_swiglu"])
+                             "copy_calibration", "gdn_repair_compare", "gate_up_swiglu", "kv_fp8"])
     ap.add_argument("--copies", type=int, default=16, help="device copies of the packed weight (decode)")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying HIP graphs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -64,6 +64,8 @@ def main():
         res = bench_repair(args, torch, nv, W, dev)
     elif args.config == "gate_up_swiglu":
         res = bench_swiglu(args, torch, nv, W, dev)
+    elif args.config == "kv_fp8":
+        res = bench_kv_fp8(args, torch, nv, W, dev)
     elif args.config == "down_proj_quantize":
         res = bench_quantize(args, torch, nv, W, dev)
     else:
@@ -210,6 +212,55 @@ def bench_swiglu(args, torch, nv, W, dev):
             "roofline": {"bound": "mfma", "achieved": round(value, 2), "peak": F16_MFMA_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(value / F16_MFMA_PEAK_TFLOPS, 4), "traffic": None,
                          "kernel": "gemm_mfma_kernel (SwiGLU epilogue)"}}
+
+
+def bench_kv_fp8(args, torch, nv, W, dev):
+    """FP8 KV-cache codec on one layer's keys and values for a 32768-token context with
+    8 KV heads of 128 (2 x 32768 x 1024 bf16, 128 MB), N(0, 1) with 8 outlier channels
+    x20; amax calibrated on a different draw of the same distribution.  One step =
+    encode K and V, then decode both; GB/s counts bf16 read + fp8 written (encode) and
+    fp8 read + bf16 written (decode)."""
+    rng = np.random.default_rng(0)
+    T, C = 32768, 1024
+    outl = rng.choice(C, 8, replace=False)
+
+    def draw():
+        x = rng.standard_normal((T, C)).astype(np.float32)
+        x[:, outl] *= 20.0
+        return torch.from_numpy(x).to(dev).to(torch.bfloat16)
+
+    kv = [draw(), draw()]
+    cal = draw()
+    amax = cal.float().abs().max().reshape(1).contiguous()
+    del cal
+    codes = [torch.empty((T, C), dtype=torch.uint8, device=dev) for _ in kv]
+    outs = [torch.empty((T, C), dtype=torch.bfloat16, device=dev) for _ in kv]
+
+    def step(i):
+        for x, c in zip(kv, codes):
+            nv.kv_fp8_encode(x, amax, out=c)
+        for c, y in zip(codes, outs):
+            nv.kv_fp8_decode(c, amax, out=y)
+
+    steps = max(1, args.steps)
+    sec, _ = time_region(torch, step, steps, min(args.warmup, 5))
+    n = 2 * T * C
+    step_bytes = 2 * (n * 3)
+    enc_t = kernel_time_pairs(torch, lambda i: nv.kv_fp8_encode(kv[0], amax, out=codes[0]), 50)[0]
+    dec_t = kernel_time_pairs(torch, lambda i: nv.kv_fp8_decode(codes[0], amax, out=outs[0]), 50)[0]
+    per = T * C * 3
+    sat = float((codes[0] & 0x7F).eq(0x7E).float().mean().item())
+    value = step_bytes * steps / sec / 1e9
+    achieved = per / ((enc_t + dec_t) / 2) / 1e9
+    return {"metric": "FP8 KV-cache codec GB/s (encode + decode), % of MI355X HBM roofline", "value": round(value, 1),
+            "unit": "GB/s", "n_gpus": 1, "steps": steps, "warmup": min(args.warmup, 5),
+            "ms_per_step": round(sec / steps * 1e3, 4), "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "fp8", "data": "synthetic",
+            "config": {"workload": "kv_fp8_t32768_c1024_k_and_v", "encode_us": round(enc_t * 1e6, 2),
+                       "decode_us": round(dec_t * 1e6, 2), "saturated_fraction": sat},
+            "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                         "kernel": "kv_fp8_encode_kernel / kv_fp8_decode_kernel"}}
 
 
 def to_dev_bf16(torch, bits, dev):

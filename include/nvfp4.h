@@ -219,6 +219,23 @@ nvfp4_status nvfp4_gemm_swiglu_quantize(const uint8_t* a_codes, const uint8_t* a
 nvfp4_status nvfp4_swiglu(const float* gu, int64_t M, int64_t I, int64_t ldgu, void* h_bf16, int64_t ldh,
                           void* stream);
 
+/* ---------------------------------------------------------------------------
+ * Calibrated FP8 (E4M3FN) KV-cache codec, one scale per tensor.
+ *
+ * The quantized model is served with an FP8 KV cache under calibrated
+ * per-tensor scales (paper abstract; Glonce article, "How to use it"; aiany
+ * page, "Mechanistic notes").  Reading, built like the NVFP4 per-tensor scale:
+ *   g_enc = fl(448 / amax), g_dec = fl(amax / 448)   (amax == 0: g = 0);
+ *   code  = sign(x) << 7 | E4M3 RNE of fl(|x| * g_enc), saturating at 448;
+ *   decode = bf16 (RNE) of fl(E4M3(code) * g_dec).
+ * n elements, contiguous; amax is a device pointer to the calibrated maximum
+ * (finite, >= 0).  Pointers 16-byte aligned; any n.  Non-finite x are outside
+ * the contract.
+ * ------------------------------------------------------------------------- */
+nvfp4_status nvfp4_kv_fp8_encode(const void* x_bf16, int64_t n, const float* amax, uint8_t* codes, void* stream);
+
+nvfp4_status nvfp4_kv_fp8_decode(const uint8_t* codes, int64_t n, const float* amax, void* out_bf16, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

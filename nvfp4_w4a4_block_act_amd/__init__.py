@@ -74,6 +74,10 @@ def _lib():
         lib.nvfp4_gemm_swiglu_quantize.restype = ctypes.c_int
         lib.nvfp4_gemm_swiglu_quantize.argtypes = [_vp, _vp, _vp, _i64, _i64, _vp, _vp, _i64, _vp, _vp, _vp, _vp,
                                                    _vp, _vp]
+        lib.nvfp4_kv_fp8_encode.restype = ctypes.c_int
+        lib.nvfp4_kv_fp8_encode.argtypes = [_vp, _i64, _vp, _vp, _vp]
+        lib.nvfp4_kv_fp8_decode.restype = ctypes.c_int
+        lib.nvfp4_kv_fp8_decode.argtypes = [_vp, _i64, _vp, _vp, _vp]
         lib.nvfp4_swiglu.restype = ctypes.c_int
         lib.nvfp4_swiglu.argtypes = [_vp, _i64, _i64, _i64, _vp, _i64, _vp]
         _LIB = lib
@@ -180,6 +184,14 @@ def nvfp4_gemm_swiglu_quantize(a_codes, a_scales, a_g_dec, M, K, w_codes, w_scal
                                              _ptr(w_scales), I, _ptr(w_g_dec), _ptr(amax_h), _ptr(h_codes),
                                              _ptr(h_scales), _ptr(h_g_dec), _stream(stream)),
            "nvfp4_gemm_swiglu_quantize")
+
+
+def nvfp4_kv_fp8_encode(x, n, amax, codes, stream=None):
+    _check(_lib().nvfp4_kv_fp8_encode(_ptr(x), n, _ptr(amax), _ptr(codes), _stream(stream)), "nvfp4_kv_fp8_encode")
+
+
+def nvfp4_kv_fp8_decode(codes, n, amax, out, stream=None):
+    _check(_lib().nvfp4_kv_fp8_decode(_ptr(codes), n, _ptr(amax), _ptr(out), _stream(stream)), "nvfp4_kv_fp8_decode")
 
 
 def nvfp4_swiglu(gu, M, I, ldgu, h, ldh, stream=None):
@@ -336,3 +348,19 @@ def swiglu(gu, stream=None):
     h = torch.empty((M, N2 // 2), dtype=torch.bfloat16, device=gu.device)
     nvfp4_swiglu(gu, M, N2 // 2, gu.stride(0), h, h.stride(0), stream)
     return h
+
+
+def kv_fp8_encode(x, amax, out=None, stream=None):
+    """Contiguous bf16 cuda tensor + device amax [1] -> uint8 E4M3FN codes of the same shape."""
+    assert x.dtype == torch.bfloat16 and x.is_contiguous()
+    codes = torch.empty(x.shape, dtype=torch.uint8, device=x.device) if out is None else out
+    nvfp4_kv_fp8_encode(x, x.numel(), amax, codes, stream)
+    return codes
+
+
+def kv_fp8_decode(codes, amax, out=None, stream=None):
+    """uint8 E4M3FN codes + device amax [1] -> bf16 tensor of the same shape."""
+    assert codes.dtype == torch.uint8 and codes.is_contiguous()
+    y = torch.empty(codes.shape, dtype=torch.bfloat16, device=codes.device) if out is None else out
+    nvfp4_kv_fp8_decode(codes, codes.numel(), amax, y, stream)
+    return y

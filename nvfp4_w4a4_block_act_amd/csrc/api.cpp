@@ -292,4 +292,26 @@ nvfp4_status nvfp4_swiglu(const float* gu, int64_t M, int64_t I, int64_t ldgu, v
                                        static_cast<hipStream_t>(stream)));
 }
 
+// ---- calibrated FP8 KV-cache codec
+nvfp4_status nvfp4_kv_fp8_encode(const void* x_bf16, int64_t n, const float* amax, uint8_t* codes, void* stream) {
+  if (n < 0) return NVFP4_EINVAL;
+  if (n == 0) return NVFP4_OK;
+  if (!x_bf16 || !amax || !codes) return NVFP4_EINVAL;
+  if (!aligned16(x_bf16) || !aligned16(codes)) return NVFP4_EALIGN;
+  if (overlap(x_bf16, (size_t)n * 2, codes, (size_t)n) || overlap(amax, 4, codes, (size_t)n)) return NVFP4_EINVAL;
+  return launched(nvfp4::launch_kv_fp8_encode(static_cast<const uint16_t*>(x_bf16), n, amax, codes,
+                                              static_cast<hipStream_t>(stream)));
+}
+
+nvfp4_status nvfp4_kv_fp8_decode(const uint8_t* codes, int64_t n, const float* amax, void* out_bf16, void* stream) {
+  if (n < 0) return NVFP4_EINVAL;
+  if (n == 0) return NVFP4_OK;
+  if (!codes || !amax || !out_bf16) return NVFP4_EINVAL;
+  if (!aligned16(codes) || !aligned16(out_bf16)) return NVFP4_EALIGN;
+  if (overlap(codes, (size_t)n, out_bf16, (size_t)n * 2) || overlap(amax, 4, out_bf16, (size_t)n * 2))
+    return NVFP4_EINVAL;
+  return launched(nvfp4::launch_kv_fp8_decode(codes, n, amax, static_cast<uint16_t*>(out_bf16),
+                                              static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -1,0 +1,99 @@
+// Calibrated FP8 (E4M3FN) KV-cache codec with one scale per tensor.
+//
+// The pages serve the quantized model with an FP8 KV cache scaled by
+// calibrated per-tensor scales (paper abstract; Glonce article, "How to use
+// it"; aiany page, "Mechanistic notes").  Rule (the plain reading, built like
+// the NVFP4 per-tensor scale): a calibrated maximum amax of |x| maps onto 448,
+// g_enc = fl(448 / amax), g_dec = fl(amax / 448); code = sign(x) << 7 | E4M3
+// round-to-nearest-even of fl(|x| * g_enc), saturating at 448 (amax == 0
+// gives sign-only codes); decode = bf16 RNE of fl(E4M3(code) * g_dec).
+//
+// gfx950's v_cvt_pk_fp8_f32 rounds to nearest even on OCP E4M3FN; clamped to
+// 448 first it equals the saturating rule for every binary32 input (checked
+// exhaustively on the device for all values in [0, 448]), and v_cvt_f32_fp8
+// decodes every code exactly.  Both kernels are HBM-bound streams: 2 B read
+// and 1 B written per element (encode), the reverse for decode; each thread
+// moves 16 elements per trip with 16-byte loads and stores.
+#include <algorithm>
+
+#include "common.hpp"
+
+namespace nvfp4 {
+
+__device__ __forceinline__ float kv_g_enc(float amax) { return (amax == 0.0f) ? 0.0f : 448.0f / amax; }
+
+// Codes of one bf16 word pair (elements lo, hi of `w`), as bits 0-15 of the result.
+__device__ __forceinline__ uint32_t kv_encode_pair(uint32_t w, float g) {
+  const float y0 = fminf(__uint_as_float((w << 16) & 0x7FFF0000u) * g, 448.0f);
+  const float y1 = fminf(__uint_as_float(w & 0x7FFF0000u) * g, 448.0f);
+  const uint32_t m = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y0, y1, 0, false) & 0xFFFFu;
+  const uint32_t sign = ((w >> 8) & 0x80u) | ((w >> 16) & 0x8000u);   // bf16 sign bits 15, 31 -> 7, 15
+  return m | sign;
+}
+
+__global__ void kv_fp8_encode_kernel(const uint16_t* __restrict__ x, int64_t n, const float* __restrict__ amax,
+                                     uint8_t* __restrict__ codes) {
+  const float g = kv_g_enc(*amax);
+  const int64_t chunks = n / 16;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < chunks; c += stride) {
+    const uint4* p = reinterpret_cast<const uint4*>(x + c * 16);
+    const uint4 a = p[0], b = p[1];
+    uint4 o;
+    o.x = kv_encode_pair(a.x, g) | (kv_encode_pair(a.y, g) << 16);
+    o.y = kv_encode_pair(a.z, g) | (kv_encode_pair(a.w, g) << 16);
+    o.z = kv_encode_pair(b.x, g) | (kv_encode_pair(b.y, g) << 16);
+    o.w = kv_encode_pair(b.z, g) | (kv_encode_pair(b.w, g) << 16);
+    *reinterpret_cast<uint4*>(codes + c * 16) = o;
+  }
+  // tail (n % 16 elements): one element per thread of the first workgroup
+  const int64_t t = chunks * 16 + threadIdx.x;
+  if (blockIdx.x == 0 && t < n) codes[t] = (uint8_t)kv_encode_pair(x[t], g);
+}
+
+// bf16 RNE bits of E4M3(code) * g (g >= 0), sign taken from the code.
+__device__ __forceinline__ uint32_t kv_decode_one(uint32_t code, float g) {
+  const float v = __builtin_amdgcn_cvt_f32_fp8((int)code, 0) * g;
+  const uint32_t b = __float_as_uint(v);
+  return (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
+}
+
+__global__ void kv_fp8_decode_kernel(const uint8_t* __restrict__ codes, int64_t n, const float* __restrict__ amax,
+                                     uint16_t* __restrict__ out) {
+  const float g = *amax / 448.0f;
+  const int64_t chunks = n / 16;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < chunks; c += stride) {
+    const uint4 q = *reinterpret_cast<const uint4*>(codes + c * 16);
+    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+    uint32_t o[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      o[2 * i] = kv_decode_one(w[i] & 0xFFu, g) | (kv_decode_one((w[i] >> 8) & 0xFFu, g) << 16);
+      o[2 * i + 1] = kv_decode_one((w[i] >> 16) & 0xFFu, g) | (kv_decode_one(w[i] >> 24, g) << 16);
+    }
+    uint4* d = reinterpret_cast<uint4*>(out + c * 16);
+    d[0] = make_uint4(o[0], o[1], o[2], o[3]);
+    d[1] = make_uint4(o[4], o[5], o[6], o[7]);
+  }
+  const int64_t t = chunks * 16 + threadIdx.x;
+  if (blockIdx.x == 0 && t < n) out[t] = (uint16_t)kv_decode_one(codes[t], g);
+}
+
+static int kv_grid(int64_t n) {
+  return (int)std::max<int64_t>(1, std::min<int64_t>((n / 16 + 255) / 256, 256 * 8));
+}
+
+hipError_t launch_kv_fp8_encode(const uint16_t* x, int64_t n, const float* amax, uint8_t* codes,
+                                hipStream_t stream) {
+  kv_fp8_encode_kernel<<<kv_grid(n), 256, 0, stream>>>(x, n, amax, codes);
+  return hipGetLastError();
+}
+
+hipError_t launch_kv_fp8_decode(const uint8_t* codes, int64_t n, const float* amax, uint16_t* out,
+                                hipStream_t stream) {
+  kv_fp8_decode_kernel<<<kv_grid(n), 256, 0, stream>>>(codes, n, amax, out);
+  return hipGetLastError();
+}
+
+}  // namespace nvfp4

@@ -35,7 +35,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=48)
     ap.add_argument("--config", default="decode",
                     choices=["decode", "prefill_gate_up", "gdn_in_proj", "down_proj", "down_proj_quantize", "tiny",
-                             "copy_calibration", "gdn_repair_compare", "gate_up_swiglu", "kv_fp8"])
+                             "copy_calibration", "gdn_repair_compare", "gate_up_swiglu", "kv_fp8", "static_calibration"])
     ap.add_argument("--copies", type=int, default=16, help="device copies of the packed weight (decode)")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying HIP graphs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -66,6 +66,8 @@ def main():
         res = bench_swiglu(args, torch, nv, W, dev)
     elif args.config == "kv_fp8":
         res = bench_kv_fp8(args, torch, nv, W, dev)
+    elif args.config == "static_calibration":
+        res = bench_calibration(args, torch, nv, W, dev)
     elif args.config == "down_proj_quantize":
         res = bench_quantize(args, torch, nv, W, dev)
     else:
@@ -261,6 +263,55 @@ def bench_kv_fp8(args, torch, nv, W, dev):
             "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
                          "kernel": "kv_fp8_encode_kernel / kv_fp8_decode_kernel"}}
+
+
+def bench_calibration(args, torch, nv, W, dev):
+    """Static activation scales as calibration-only PTQ ships them, on the decode
+    linear layer (K = 5120, N = 12288): observe the running maximum over 16
+    calibration batches of 16 tokens (Student-t(3) activations with outlier
+    channels, the decode distribution), then on 16 held-out batches compare the
+    static scale with the dynamic one: saturated block scales, clipped elements, and
+    the layer output's relative RMS error against the unquantized float64 product
+    (512 sampled output columns).  Times the observer and the static linear call."""
+    d = W.decode(M=16)
+    K, N = d.K, d.N
+    w = torch.from_numpy(d.w).to(dev)
+    pw = nv.pack_weight(w, d.segments)
+    del w
+    obs = nv.AmaxObserver(dev)
+    cal = [to_dev_bf16(torch, W.random_act(1000 + i, 16, K, "student_t"), dev) for i in range(16)]
+    for x in cal:
+        obs.observe(x)
+    amax = obs.amax.clone()
+    rng = np.random.default_rng(0)
+    cols = np.sort(rng.choice(N, 512, replace=False))
+    wsub = d.w[cols].astype(np.float64)
+    sat = clip = blocks = elems = 0
+    err = {"static": [], "dynamic": []}
+    for i in range(16):
+        bits = W.random_act(5000 + i, 16, K, "student_t")
+        x = to_dev_bf16(torch, bits, dev)
+        cnt = nv.quantize_stats(x, amax).cpu().numpy()
+        sat, clip = sat + int(cnt[0]), clip + int(cnt[1])
+        blocks, elems = blocks + 16 * K // 16, elems + 16 * K
+        ref = (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64) @ wsub.T
+        for name, a in (("static", amax), ("dynamic", None)):
+            y = nv.linear(x, pw, a)[0].cpu().numpy().astype(np.float64)[:, cols]
+            err[name].append(float(np.sqrt(np.mean((y - ref) ** 2)) / np.sqrt(np.mean(ref ** 2))))
+    x0 = cal[0]
+    t_obs = kernel_time_pairs(torch, lambda i: obs.observe(x0), 50)[0]
+    out = torch.empty((16, N), dtype=torch.float32, device=dev)
+    t_lin = kernel_time_pairs(torch, lambda i: nv.linear(x0, pw, amax, out=out), 50)[0]
+    return {"metric": "NVFP4 static activation scale: calibration observer and held-out saturation / error",
+            "value": round(float(np.mean(err["static"])), 6), "unit": "relative RMS error (static scale)",
+            "n_gpus": 1, "steps": 16, "warmup": 0, "ms_per_step": round(t_lin * 1e3, 5), "higher_is_better": False,
+            "scaling": "weak", "vs_baseline": None, "dtype": "f16", "data": "synthetic",
+            "config": {"workload": "decode_static_calibration_m16_k5120_n12288", "calibration_batches": 16,
+                       "heldout_batches": 16, "calibrated_amax": float(amax.item()),
+                       "saturated_block_fraction": sat / blocks, "clipped_element_fraction": clip / elems,
+                       "rel_rms_error_static": round(float(np.mean(err["static"])), 6),
+                       "rel_rms_error_dynamic": round(float(np.mean(err["dynamic"])), 6),
+                       "observer_us": round(t_obs * 1e6, 2), "static_linear_us": round(t_lin * 1e6, 2)}}
 
 
 def to_dev_bf16(torch, bits, dev):

@@ -220,6 +220,33 @@ nvfp4_status nvfp4_swiglu(const float* gu, int64_t M, int64_t I, int64_t ldgu, v
                           void* stream);
 
 /* ---------------------------------------------------------------------------
+ * Static (calibrated) activation scales.
+ *
+ * The pages' recipe is calibration-only post-training quantization (aiany
+ * page, "Who it's for"): an activation's per-tensor maximum may be observed
+ * over calibration batches and then passed as amax_in (static mode).
+ *
+ * nvfp4_amax_observe: *running_amax = max(*running_amax, max |x|) over the
+ * bf16 tensor x[M][K] (row stride ldx); running_amax is a device float the
+ * caller initializes (e.g. to 0).  Workspace: nvfp4_amax_observe_workspace_bytes.
+ *
+ * nvfp4_quantize_stats: with the static maximum *amax_in, counts (device
+ * uint32[2], overwritten) receive the number of blocks whose unrounded scale
+ * fl(fl(bmax / 6) * g_enc) exceeds 448 (the E4M3 encode saturates) and the
+ * number of elements with y = fl(|x| * fl(g_enc / s_dec)) >= 7 (cut to the
+ * largest E2M1 magnitude 6 rather than rounded to it: in saturated blocks or
+ * under E4M3 subnormal scales), in the encoder's own binary32 steps.
+ * amax == 0 counts nothing.
+ * ------------------------------------------------------------------------- */
+size_t nvfp4_amax_observe_workspace_bytes(int64_t M, int64_t K);
+
+nvfp4_status nvfp4_amax_observe(const void* x_bf16, int64_t M, int64_t K, int64_t ldx, float* running_amax,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
+nvfp4_status nvfp4_quantize_stats(const void* x_bf16, int64_t M, int64_t K, int64_t ldx, const float* amax_in,
+                                  uint32_t* counts, void* stream);
+
+/* ---------------------------------------------------------------------------
  * Calibrated FP8 (E4M3FN) KV-cache codec, one scale per tensor.
  *
  * The quantized model is served with an FP8 KV cache under calibrated

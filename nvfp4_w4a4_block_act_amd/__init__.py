@@ -74,6 +74,12 @@ def _lib():
         lib.nvfp4_gemm_swiglu_quantize.restype = ctypes.c_int
         lib.nvfp4_gemm_swiglu_quantize.argtypes = [_vp, _vp, _vp, _i64, _i64, _vp, _vp, _i64, _vp, _vp, _vp, _vp,
                                                    _vp, _vp]
+        lib.nvfp4_amax_observe_workspace_bytes.restype = _sz
+        lib.nvfp4_amax_observe_workspace_bytes.argtypes = [_i64, _i64]
+        lib.nvfp4_amax_observe.restype = ctypes.c_int
+        lib.nvfp4_amax_observe.argtypes = [_vp, _i64, _i64, _i64, _vp, _vp, _sz, _vp]
+        lib.nvfp4_quantize_stats.restype = ctypes.c_int
+        lib.nvfp4_quantize_stats.argtypes = [_vp, _i64, _i64, _i64, _vp, _vp, _vp]
         lib.nvfp4_kv_fp8_encode.restype = ctypes.c_int
         lib.nvfp4_kv_fp8_encode.argtypes = [_vp, _i64, _vp, _vp, _vp]
         lib.nvfp4_kv_fp8_decode.restype = ctypes.c_int
@@ -184,6 +190,20 @@ def nvfp4_gemm_swiglu_quantize(a_codes, a_scales, a_g_dec, M, K, w_codes, w_scal
                                              _ptr(w_scales), I, _ptr(w_g_dec), _ptr(amax_h), _ptr(h_codes),
                                              _ptr(h_scales), _ptr(h_g_dec), _stream(stream)),
            "nvfp4_gemm_swiglu_quantize")
+
+
+def nvfp4_amax_observe_workspace_bytes(M, K):
+    return _lib().nvfp4_amax_observe_workspace_bytes(int(M), int(K))
+
+
+def nvfp4_amax_observe(x, M, K, ldx, running_amax, workspace, workspace_bytes, stream=None):
+    _check(_lib().nvfp4_amax_observe(_ptr(x), M, K, ldx, _ptr(running_amax), _ptr(workspace), workspace_bytes,
+                                     _stream(stream)), "nvfp4_amax_observe")
+
+
+def nvfp4_quantize_stats(x, M, K, ldx, amax_in, counts, stream=None):
+    _check(_lib().nvfp4_quantize_stats(_ptr(x), M, K, ldx, _ptr(amax_in), _ptr(counts), _stream(stream)),
+           "nvfp4_quantize_stats")
 
 
 def nvfp4_kv_fp8_encode(x, n, amax, codes, stream=None):
@@ -364,3 +384,25 @@ def kv_fp8_decode(codes, amax, out=None, stream=None):
     y = torch.empty(codes.shape, dtype=torch.bfloat16, device=codes.device) if out is None else out
     nvfp4_kv_fp8_decode(codes, codes.numel(), amax, y, stream)
     return y
+
+
+class AmaxObserver:
+    """Running maximum of |x| over calibration batches, kept on the device."""
+
+    def __init__(self, device):
+        self.amax = torch.zeros(1, dtype=torch.float32, device=device)
+        self.ws = torch.empty(max(nvfp4_amax_observe_workspace_bytes(0, 0), 16), dtype=torch.uint8, device=device)
+
+    def observe(self, x, stream=None):
+        assert x.dtype == torch.bfloat16 and x.dim() == 2 and (x.stride(1) == 1 or x.shape[1] <= 1)
+        M, K = x.shape
+        nvfp4_amax_observe(x, M, K, max(x.stride(0), K), self.amax, self.ws, self.ws.numel(), stream)
+        return self.amax
+
+
+def quantize_stats(x, amax, stream=None):
+    """(saturated-scale blocks, clipped elements) of bf16 x under the static maximum amax [1]."""
+    M, K = x.shape
+    counts = torch.empty(2, dtype=torch.int32, device=x.device)
+    nvfp4_quantize_stats(x, M, K, max(x.stride(0), K), amax, counts, stream)
+    return counts

@@ -292,6 +292,45 @@ nvfp4_status nvfp4_swiglu(const float* gu, int64_t M, int64_t I, int64_t ldgu, v
                                        static_cast<hipStream_t>(stream)));
 }
 
+// ---- static-scale calibration
+size_t nvfp4_amax_observe_workspace_bytes(int64_t M, int64_t K) {
+  (void)M;
+  (void)K;
+  return nvfp4::amax_observe_workspace();
+}
+
+nvfp4_status nvfp4_amax_observe(const void* x_bf16, int64_t M, int64_t K, int64_t ldx, float* running_amax,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  if (M < 0 || K < 0) return NVFP4_EINVAL;
+  if (K % 16 != 0 || M >= kMaxDim || K >= kMaxDim || ldx < K) return NVFP4_ESHAPE;
+  if (!running_amax) return NVFP4_EINVAL;
+  if (M == 0 || K == 0) return NVFP4_OK;
+  if (!x_bf16) return NVFP4_EINVAL;
+  if (!aligned16(x_bf16) || ldx % 8 != 0) return NVFP4_EALIGN;
+  const size_t need = nvfp4::amax_observe_workspace();
+  if (!workspace || workspace_bytes < need) return NVFP4_EWORKSPACE;
+  const size_t xb = (size_t)((M - 1) * ldx + K) * 2;
+  if (overlap(x_bf16, xb, running_amax, 4) || overlap(workspace, need, running_amax, 4) ||
+      overlap(workspace, need, x_bf16, xb))
+    return NVFP4_EINVAL;
+  return launched(nvfp4::launch_amax_observe(static_cast<const uint16_t*>(x_bf16), M, K, ldx, running_amax,
+                                             workspace, static_cast<hipStream_t>(stream)));
+}
+
+nvfp4_status nvfp4_quantize_stats(const void* x_bf16, int64_t M, int64_t K, int64_t ldx, const float* amax_in,
+                                  uint32_t* counts, void* stream) {
+  if (M < 0 || K < 0) return NVFP4_EINVAL;
+  if (K % 16 != 0 || M >= kMaxDim || K >= kMaxDim || ldx < K) return NVFP4_ESHAPE;
+  if (!amax_in || !counts) return NVFP4_EINVAL;
+  const bool empty = (M == 0 || K == 0);
+  if (!empty && !x_bf16) return NVFP4_EINVAL;
+  if (!empty && (!aligned16(x_bf16) || ldx % 8 != 0)) return NVFP4_EALIGN;
+  if (!empty && overlap(x_bf16, (size_t)((M - 1) * ldx + K) * 2, counts, 8)) return NVFP4_EINVAL;
+  if (overlap(amax_in, 4, counts, 8)) return NVFP4_EINVAL;
+  return launched(nvfp4::launch_quantize_stats(static_cast<const uint16_t*>(x_bf16), M, K, ldx, amax_in, counts,
+                                               static_cast<hipStream_t>(stream)));
+}
+
 // ---- calibrated FP8 KV-cache codec
 nvfp4_status nvfp4_kv_fp8_encode(const void* x_bf16, int64_t n, const float* amax, uint8_t* codes, void* stream) {
   if (n < 0) return NVFP4_EINVAL;

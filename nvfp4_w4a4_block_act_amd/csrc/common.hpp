@@ -151,6 +151,11 @@ hipError_t launch_gemm_swiglu_quantize(const uint8_t* a_codes, const uint8_t* a_
                                        uint8_t* h_scales, float* h_g_dec, hipStream_t stream);
 hipError_t launch_swiglu(const float* gu, int64_t M, int64_t I, int64_t ldgu, uint16_t* h, int64_t ldh,
                          hipStream_t stream);
+size_t amax_observe_workspace();
+hipError_t launch_amax_observe(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, float* running,
+                               void* workspace, hipStream_t stream);
+hipError_t launch_quantize_stats(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, const float* amax_in,
+                                 uint32_t* counts, hipStream_t stream);
 hipError_t launch_kv_fp8_encode(const uint16_t* x, int64_t n, const float* amax, uint8_t* codes,
                                 hipStream_t stream);
 hipError_t launch_kv_fp8_decode(const uint8_t* codes, int64_t n, const float* amax, uint16_t* out,

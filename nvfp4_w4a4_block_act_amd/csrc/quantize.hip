@@ -195,6 +195,84 @@ hipError_t launch_quantize_act(const uint16_t* x, int64_t M, int64_t K, int64_t 
   return hipGetLastError();
 }
 
+// ---- static-scale calibration -------------------------------------------------------
+// Observer: running = max(running, max |x|), from the partial maxima above.
+__global__ __launch_bounds__(kQThreads) void amax_observe_finalize_kernel(const uint32_t* __restrict__ partial,
+                                                                          int nparts, float* __restrict__ running) {
+  __shared__ uint32_t red[kQThreads / 64];
+  uint32_t m = 0;
+  for (int i = threadIdx.x; i < nparts; i += blockDim.x) m = max(m, partial[i]);
+  m = block_reduce_max(m, red);
+  if (threadIdx.x == 0) *running = fmaxf(*running, __uint_as_float(m << 16));
+}
+
+size_t amax_observe_workspace() { return kPartials * sizeof(uint32_t); }
+
+hipError_t launch_amax_observe(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, float* running,
+                               void* workspace, hipStream_t stream) {
+  if (M * K == 0) return hipSuccess;
+  uint32_t* partial = static_cast<uint32_t*>(workspace);
+  const int64_t chunks = M * (K / 8);
+  const int pgrid = (int)std::max<int64_t>(1, std::min<int64_t>(kPartials, chunks / (kQThreads * 16)));
+  amax_partial_kernel<<<pgrid, kQThreads, 0, stream>>>(x, M, (int)K, ldx, partial);
+  amax_observe_finalize_kernel<<<1, kQThreads, 0, stream>>>(partial, pgrid, running);
+  return hipGetLastError();
+}
+
+// Saturation statistics under a static maximum, in the encoder's own binary32
+// steps: counts[0] += blocks whose unrounded scale fl(fl(bmax / 6) * g_enc)
+// exceeds 448, counts[1] += elements with y = fl(|x| * fl(g_enc / s_dec)) >= 7
+// (past the midpoint from 6 to the next grid value 8: cut rather than rounded to
+// 6, which happens in saturated blocks and in blocks with E4M3 subnormal scales).
+__global__ __launch_bounds__(kQThreads) void quantize_stats_kernel(const uint16_t* __restrict__ x, int64_t M,
+                                                                   int K, int64_t ldx,
+                                                                   const float* __restrict__ amax_in,
+                                                                   uint32_t* __restrict__ counts) {
+  const float g_enc = g_enc_of(*amax_in);
+  const int nb = K / kBlock;
+  const int64_t total = M * nb;
+  uint32_t sat = 0, clip = 0;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t m = i / nb;
+    const int b = (int)(i - m * nb);
+    const uint4* p = reinterpret_cast<const uint4*>(x + m * ldx + (int64_t)b * kBlock);
+    const uint4 v0 = p[0], v1 = p[1];
+    const uint32_t d[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+    const float bmax = __uint_as_float(absmax_bits(v0, absmax_bits(v1, 0u)) << 16);
+    const float t = bmax / 6.0f;
+    const float s = t * g_enc;
+    sat += (s > 448.0f) ? 1u : 0u;
+    const uint32_t sc = (t != 0.0f) ? e4m3_encode_rne_sat(s) : 0u;
+    const float sdec = e4m3_value(sc);
+    const float rb = (sdec != 0.0f) ? g_enc / sdec : 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      clip += (__uint_as_float((d[e] << 16) & 0x7FFF0000u) * rb >= 7.0f) ? 1u : 0u;
+      clip += (__uint_as_float(d[e] & 0x7FFF0000u) * rb >= 7.0f) ? 1u : 0u;
+    }
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    sat += (uint32_t)__shfl_xor((int)sat, o, 64);
+    clip += (uint32_t)__shfl_xor((int)clip, o, 64);
+  }
+  if ((threadIdx.x & 63) == 0 && (sat | clip)) {
+    atomicAdd(&counts[0], sat);
+    atomicAdd(&counts[1], clip);
+  }
+}
+
+hipError_t launch_quantize_stats(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, const float* amax_in,
+                                 uint32_t* counts, hipStream_t stream) {
+  const hipError_t e = launch_fill_zero(reinterpret_cast<float*>(counts), 1, 2, 2, stream);
+  if (e != hipSuccess) return e;
+  const int64_t blocks = M * (K / kBlock);
+  if (blocks == 0) return hipSuccess;
+  const int grid = (int)std::min<int64_t>((blocks + kQThreads - 1) / kQThreads, 256 * 8);
+  quantize_stats_kernel<<<grid, kQThreads, 0, stream>>>(x, M, (int)K, ldx, amax_in, counts);
+  return hipGetLastError();
+}
+
 // ---- weights: per-module encode into the tiled layout ----------------------------
 constexpr int kSegParts = 64;   // amax workgroups per segment
 

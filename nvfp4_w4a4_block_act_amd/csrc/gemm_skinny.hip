@@ -224,10 +224,11 @@ __global__ __launch_bounds__(64 * NW) void gemm_skinny_kernel(
 //     publishes the reciprocal table of the fast encoder);
 //  4. every thread encodes its blocks into LDS in the canonical layout (rows
 //     padded by 16 bytes against bank conflicts); workgroup 0 also writes the
-//     canonical codes, scales and g_dec to memory;
-//  5. the remaining weight batches are requested (a wave that has requested
-//     its weights stalls at issue while the memory system back-pressures the
-//     loads, so they go out only once the encode is done), then a barrier;
+//     canonical codes, scales and g_dec to memory.  The remaining weight
+//     batches are requested between encode steps: a wave that has requested
+//     weights stalls at issue while the memory system back-pressures the
+//     loads, and meanwhile the other wave on its SIMD encodes;
+//  5. a barrier publishes the activations;
 //  6. the skinny-GEMM tiles read their activation operand from LDS.
 // The results are bit-identical to the activation quantizer followed by the
 // skinny GEMM.
@@ -341,19 +342,21 @@ __global__ __launch_bounds__(64 * NW) void linear_decode_kernel(
         a_scales[(int64_t)row * nb + col] = (uint8_t)sc;
       }
     }
+    // the remaining weight batches go out spread over the encode loop: a wave
+    // stalled on issuing them yields its SIMD to the other wave's encode work
+#pragma unroll
+    for (int u = PRE; u < U; ++u)
+      if (j == (u - PRE) * kPer / (U - PRE)) {
+        const int t = min(wave + NW * u, tiles - 1);
+#pragma unroll
+        for (int s = 0; s < S; ++s) {
+          wv[u][s] = *reinterpret_cast<const uint4*>(wc[s] + (int64_t)t * kChunkCodes);
+          wsc[u][s] = *reinterpret_cast<const uint16_t*>(ws[s] + (int64_t)t * kChunkScales);
+        }
+      }
   }
 
-  // 5. remaining weight batches, then publish the LDS activations
-  __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-  for (int u = PRE; u < U; ++u) {
-    const int t = min(wave + NW * u, tiles - 1);
-#pragma unroll
-    for (int s = 0; s < S; ++s) {
-      wv[u][s] = *reinterpret_cast<const uint4*>(wc[s] + (int64_t)t * kChunkCodes);
-      wsc[u][s] = *reinterpret_cast<const uint16_t*>(ws[s] + (int64_t)t * kChunkScales);
-    }
-  }
+  // 5. publish the LDS activations
   __syncthreads();
 
   // 6. MFMAs: lane (r, g) of tile t takes row r, k in [t * 128 + 32 g, + 32)
@@ -412,7 +415,9 @@ hipError_t launch_gemm_skinny(const uint8_t* a_codes, const uint8_t* a_scales, c
   return hipGetLastError();
 }
 
-constexpr int kDecPre = 2;
+// first weight batches requested before the activation work: two for up to 4
+// rows (little encode work to hide), one for more rows (measured best)
+constexpr int kDecPreSmallM = 2, kDecPreLargeM = 1;
 
 bool linear_decode_fits(int64_t M, int64_t K) {
   return M >= 1 && M <= kDecMaxM && K >= kBlock && K <= kDecMaxK;
@@ -424,9 +429,14 @@ hipError_t launch_linear_decode(const uint16_t* x, int64_t ldx, const float* ama
                                 int64_t ldo, hipStream_t stream) {
   const int nstrips = (N + kStrip - 1) / kStrip;
   const int grid = (nstrips + kSkS - 1) / kSkS;
-  linear_decode_kernel<kSkS, kSkNW, kSkU, kDecPre><<<grid, 64 * kSkNW, 0, stream>>>(
-      x, ldx, amax_in, a_codes, a_scales, a_g, M, K, 1.0f / (float)(K / kBlock), w_codes, w_scales, N, st, w_g, out,
-      ldo);
+  if (M <= 4)
+    linear_decode_kernel<kSkS, kSkNW, kSkU, kDecPreSmallM><<<grid, 64 * kSkNW, 0, stream>>>(
+        x, ldx, amax_in, a_codes, a_scales, a_g, M, K, 1.0f / (float)(K / kBlock), w_codes, w_scales, N, st, w_g,
+        out, ldo);
+  else
+    linear_decode_kernel<kSkS, kSkNW, kSkU, kDecPreLargeM><<<grid, 64 * kSkNW, 0, stream>>>(
+        x, ldx, amax_in, a_codes, a_scales, a_g, M, K, 1.0f / (float)(K / kBlock), w_codes, w_scales, N, st, w_g,
+        out, ldo);
   return hipGetLastError();
 }
 

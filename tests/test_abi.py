@@ -109,6 +109,85 @@ def test_pack_validation(kw, status):
     assert p(**kw) == status
 
 
+def lin(x=A, M=4, K=32, ldx=32, amax=None, ac=A + (1 << 20), as_=A + (2 << 20), ag=A + (3 << 20),
+        wc=A + (4 << 20), ws=A + (5 << 20), N=32, sg=((0, 32),), wg=A + (6 << 20), out=A + (7 << 20), ldo=32,
+        work=None, workb=0):
+    s = segs(list(sg))
+    return nv.lib().nvfp4_linear(x, M, K, ldx, amax, ac, as_, ag, wc, ws, N, s, wg, len(sg), out, ldo, work, workb,
+                                 None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(M=-1), 1), (dict(K=24), 2), (dict(ldo=16), 2), (dict(sg=((0, 16),)), 4), (dict(ag=None), 1),
+    (dict(x=None), 1), (dict(out=A + 4), 3), (dict(ldx=36), 3), (dict(out=A + (4 << 20) + 128), 1),
+    (dict(M=4096, K=4096, ldx=4096, ac=A + (64 << 20), as_=A + (80 << 20), ag=A + (96 << 20), wc=A + (128 << 20),
+          ws=A + (160 << 20), wg=A + (192 << 20), out=A + (256 << 20)), 5),
+])
+def test_linear_validation(kw, status):
+    assert lin(**kw) == status
+
+
+def gu_pack(w=A, I=128, K=32, ldw=32, wc=A + (1 << 20), ws=A + (2 << 20), wg=A + (3 << 20), work=A + (4 << 20),
+            workb=4096):
+    return nv.lib().nvfp4_pack_weight_gate_up(w, I, K, ldw, wc, ws, wg, work, workb, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(I=0), 1), (dict(I=96), 2), (dict(K=40), 2), (dict(K=0), 2), (dict(ldw=16), 2), (dict(w=A + 4), 3),
+    (dict(workb=0), 5), (dict(wg=None), 1), (dict(wc=A + 64), 1),
+])
+def test_pack_gate_up_validation(kw, status):
+    assert gu_pack(**kw) == status
+
+
+def swq(a=A, sa=A + (1 << 20), ag=A + (2 << 20), M=32, K=32, wc=A + (3 << 20), ws=A + (4 << 20), I=128,
+        wg=A + (5 << 20), amax=A + (6 << 20), hc=A + (7 << 20), hs=A + (8 << 20), hg=A + (9 << 20)):
+    return nv.lib().nvfp4_gemm_swiglu_quantize(a, sa, ag, M, K, wc, ws, I, wg, amax, hc, hs, hg, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(M=-1), 1), (dict(I=64), 2), (dict(K=8), 2), (dict(amax=None), 1), (dict(hg=None), 1),
+    (dict(a=None), 1), (dict(hc=A + 8), 3), (dict(hc=A + (3 << 20) + 256), 1),
+])
+def test_gemm_swiglu_quantize_validation(kw, status):
+    assert swq(**kw) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(M=-1), 1), (dict(ldgu=100), 2), (dict(ldh=10), 2), (dict(gu=None), 1), (dict(h=A + 64), 1),
+    (dict(M=0), 0),
+])
+def test_swiglu_validation(kw, status):
+    a = dict(gu=A, M=4, I=64, ldgu=128, h=A + (1 << 20), ldh=64)
+    a.update(kw)
+    assert nv.lib().nvfp4_swiglu(a["gu"], a["M"], a["I"], a["ldgu"], a["h"], a["ldh"], None) == status
+
+
+@pytest.mark.parametrize("fn", ["encode", "decode"])
+def test_kv_fp8_validation(fn):
+    f = nv.lib().nvfp4_kv_fp8_encode if fn == "encode" else nv.lib().nvfp4_kv_fp8_decode
+    assert f(A, -1, A + (1 << 20), A + (2 << 20), None) == 1
+    assert f(A, 0, None, None, None) == 0                          # empty: nothing to do
+    assert f(None, 16, A + (1 << 20), A + (2 << 20), None) == 1
+    assert f(A, 16, None, A + (2 << 20), None) == 1
+    assert f(A + 4, 16, A + (1 << 20), A + (2 << 20), None) == 3
+    assert f(A, 64, A + (1 << 20), A + 16, None) == 1               # output overlaps input
+
+
+def test_observe_and_stats_validation():
+    lib = nv.lib()
+    wsb = nv.nvfp4_amax_observe_workspace_bytes(4, 32)
+    assert wsb > 0
+    assert lib.nvfp4_amax_observe(A, 4, 24, 32, A + (1 << 20), A + (2 << 20), wsb, None) == 2
+    assert lib.nvfp4_amax_observe(A, 4, 32, 32, None, A + (2 << 20), wsb, None) == 1
+    assert lib.nvfp4_amax_observe(A, 4, 32, 32, A + (1 << 20), A + (2 << 20), 0, None) == 5
+    assert lib.nvfp4_amax_observe(A + 8, 4, 32, 32, A + (1 << 20), A + (2 << 20), wsb, None) == 3
+    assert lib.nvfp4_amax_observe(A, 0, 32, 32, A + (1 << 20), None, 0, None) == 0
+    assert lib.nvfp4_quantize_stats(A, 4, 24, 32, A + (1 << 20), A + (2 << 20), None) == 2
+    assert lib.nvfp4_quantize_stats(A, 4, 32, 32, None, A + (2 << 20), None) == 1
+    assert lib.nvfp4_quantize_stats(A, 4, 32, 32, A + (1 << 20), A + 64, None) == 1   # counts overlap x
+
+
 def test_binding_has_no_cpu_fallback(monkeypatch):
     """With the library path pointing nowhere, the binding raises instead of computing."""
     monkeypatch.setattr(nv, "_LIB", None)

@@ -118,8 +118,6 @@ hipError_t launch_gemm_skinny(const uint8_t* a_codes, const uint8_t* a_scales, c
                               const SegTable& st, const float* w_g, float* out, int64_t ldo,
                               hipStream_t stream);
 hipError_t launch_fill_zero(float* out, int M, int N, int64_t ldo, hipStream_t stream);
-// Fused decode-form linear layer (quantize + skinny GEMM in one launch); `sync`
-// points at 16 zero-initialised bytes of the caller's workspace.
 // One-launch decode-form linear layer (activation quantization fused into the
 // skinny GEMM); valid when linear_decode_fits(M, K).
 bool linear_decode_fits(int64_t M, int64_t K);

@@ -305,7 +305,7 @@ __global__ __launch_bounds__(kQThreads) void pack_weight_kernel(
     const uint32_t* __restrict__ partial, uint8_t* __restrict__ w_codes, uint8_t* __restrict__ w_scales,
     float* __restrict__ w_g_dec) {
   __shared__ float s_genc[NVFP4_MAX_SEGMENTS];
-  if (threadIdx.x < st.nseg) {
+  if ((int)threadIdx.x < st.nseg) {
     uint32_t m = 0;
     for (int p = 0; p < kSegParts; ++p) m = max(m, partial[threadIdx.x * kSegParts + p]);
     const float amax = __uint_as_float(m);

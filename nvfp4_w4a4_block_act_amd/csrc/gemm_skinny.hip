@@ -114,9 +114,12 @@ __device__ __forceinline__ void reduce_store(const float4_t (&acc)[S], float (&r
   }
 }
 
-// The caller's early load of the per-segment scales (see reduce_store).
+// The caller's early load of the per-segment scales (see reduce_store): thread
+// t < nseg keeps w_g[t].  Branch-free (every thread reads a valid entry), so the
+// kernel's argument loads are not split around a branch at kernel start; issue
+// it after the first activation and weight loads.
 __device__ __forceinline__ float load_segment_scale(const float* __restrict__ w_g, const SegTable& st) {
-  return (threadIdx.x < (unsigned)st.nseg) ? w_g[threadIdx.x] : 0.0f;
+  return w_g[min((int)threadIdx.x, st.nseg - 1)];
 }
 
 // Weight pointers of lane `lane` for the S strips starting at strip0 (clamped;
@@ -168,6 +171,12 @@ __global__ __launch_bounds__(64 * NW) void gemm_skinny_kernel(
   for (int s = 0; s < S; ++s) acc[s] = float4_t{0.f, 0.f, 0.f, 0.f};
 
   for (int t0 = wave; t0 < full; t0 += NW * U) {
+    // activation fragments first (a few hundred bytes, L2-resident after the
+    // first workgroups), so the first tile's wait does not cover the weights
+    uint4 av[U];
+    uint32_t asc[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) load_a_full<AL16>(ac, as, min(t0 + u * NW, full - 1), av[u], asc[u]);
     uint4 wv[U][S];
     uint32_t wsc[U][S];
 #pragma unroll
@@ -179,10 +188,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_skinny_kernel(
         wsc[u][s] = *reinterpret_cast<const uint16_t*>(ws[s] + (int64_t)t * kChunkScales);
       }
     }
-    uint4 av[U];
-    uint32_t asc[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) load_a_full<AL16>(ac, as, min(t0 + u * NW, full - 1), av[u], asc[u]);
+    __builtin_amdgcn_sched_barrier(0);   // keep the whole batch in flight before any MFMA
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const uint32_t live = (t0 + u * NW < full) ? amask : 0u;
@@ -210,77 +216,76 @@ __global__ __launch_bounds__(64 * NW) void gemm_skinny_kernel(
 }
 
 // ---- decode-form linear layer in one launch (M <= 16, K <= 5120).
-// Every workgroup quantizes the whole activation tensor itself: it is at most
-// 16 x 5120 bf16 (160 KB, L2-resident once the first workgroups have read it),
-// and encoding it redundantly costs less than the alternatives measured on this
-// chip: a separate quantizer launch (about 5 us of launch and latency for a few
-// KB of work), or producer workgroups handing codes to the GEMM workgroups
-// (which needs a device-scope release/acquire, an L2 write-back and invalidate,
-// and whose loads queue behind the 35 MB weight stream).  Steps:
-//  1. every thread loads the bf16 blocks tid, tid + 64 NW, ... (coalesced);
-//  2. each wave requests its first PRE weight batches, so the weight stream
-//     starts before the activation work;
-//  3. amax: per-thread maximum, wave reduction, one barrier (which also
+// The activation quantizer and the skinny GEMM above in a single kernel: the
+// tensor is at most 16 x 5120 bf16, and a separate quantizer launch costs about
+// 5 us of launch and latency for a few KB of work on this chip.  Wave w of a
+// workgroup multiplies only k tiles w, w + NW, ..., so it needs the quantized
+// activations of those tiles alone: each wave loads and encodes exactly those
+// blocks (all rows) itself, spread over its 64 lanes, and hands them to the
+// MFMA lane layout through a wave-private LDS area.  The only workgroup barrier
+// before the MFMAs is the tensor-amax reduction (the scale rule needs the amax
+// of the whole tensor, which the waves hold between them); no wave waits for
+// another wave's encode, so its weight decode and MFMAs overlap the rest of the
+// weight stream.  Every workgroup encodes the tensor's blocks (redundantly;
+// the bf16 input is L2-resident after the first reads) and workgroup 0 also
+// writes the canonical codes, scales and g_dec.  Steps:
+//  1. each lane loads its bf16 blocks: slot i = lane + 64 q is row i / (8 U),
+//     tile u = (i / 8) % U, block j = i % 8 of that tile, i.e. block column
+//     (w + NW u) * 8 + j; groups of eight lanes read 256 contiguous bytes;
+//  2. the wave requests its first PRE weight batches;
+//  3. amax: per-lane maximum, wave reduction, one barrier (which also
 //     publishes the reciprocal table of the fast encoder);
-//  4. every thread encodes its blocks into LDS in the canonical layout (rows
-//     padded by 16 bytes against bank conflicts); workgroup 0 also writes the
-//     canonical codes, scales and g_dec to memory.  The remaining weight
-//     batches are requested between encode steps: a wave that has requested
-//     weights stalls at issue while the memory system back-pressures the
-//     loads, and meanwhile the other wave on its SIMD encodes;
-//  5. a barrier publishes the activations;
-//  6. the skinny-GEMM tiles read their activation operand from LDS.
-// The results are bit-identical to the activation quantizer followed by the
-// skinny GEMM.
+//  4. each lane encodes its blocks into the wave's LDS area; the remaining
+//     weight batches are requested between encode steps (a wave stalled on
+//     issuing loads under memory back-pressure yields its SIMD to the other
+//     wave's encode work);
+//  5. the MFMA tiles read their activation operand from the wave's LDS area.
+// MAXM bounds the rows a launch may have: the encode steps are unrolled over
+// MAXM rows' slots, and smaller instantiations (less code to fetch at each
+// launch) are measurably faster for small M.  The results are bit-identical to
+// the activation quantizer followed by the skinny GEMM.
 constexpr int kDecMaxM = 16;
 constexpr int kDecMaxK = 5120;
-constexpr int kDecCodeStride = kDecMaxK / 2 + 16;       // LDS bytes per activation row
-constexpr int kDecScaleStride = kDecMaxK / kBlock + 4;
+constexpr int kDecRowBytes = kTileK / 2 + 16;   // LDS bytes per row of one tile (padded)
 
-// b = r * nb + c with 0 <= c < nb, via a float reciprocal corrected to exact (b < 2^24).
-__device__ __forceinline__ void split_block(int b, int nb, float inv_nb, int& r, int& c) {
-  r = (int)((float)b * inv_nb);
-  c = b - r * nb;
-  if (c < 0) { --r; c += nb; }
-  if (c >= nb) { ++r; c -= nb; }
-}
-
-template <int S, int NW, int U, int PRE>
+template <int S, int NW, int U, int MAXM, int PRE, int SPREAD>
 __global__ __launch_bounds__(64 * NW) void linear_decode_kernel(
     const uint16_t* __restrict__ x, int64_t ldx, const float* __restrict__ amax_in, uint8_t* __restrict__ a_codes,
-    uint8_t* __restrict__ a_scales, float* __restrict__ a_g, int M, int K, float inv_nb,
-    const uint8_t* __restrict__ w_codes, const uint8_t* __restrict__ w_scales, int N, SegTable st,
-    const float* __restrict__ w_g, float* __restrict__ out, int64_t ldo) {
-  constexpr int kThreads = 64 * NW;
-  constexpr int kPer = kDecMaxM * kDecMaxK / kBlock / kThreads;   // blocks per thread at most
-  static_assert(kPer * kThreads == kDecMaxM * kDecMaxK / kBlock, "block split");
+    uint8_t* __restrict__ a_scales, float* __restrict__ a_g, int M, int K, const uint8_t* __restrict__ w_codes,
+    const uint8_t* __restrict__ w_scales, int N, SegTable st, const float* __restrict__ w_g,
+    float* __restrict__ out, int64_t ldo) {
+  constexpr int kSlots = MAXM * U * (kTileK / kBlock);   // block slots of one wave
+  constexpr int kQ = (kSlots + 63) / 64;
   static_assert(NW * U * kTileK >= kDecMaxK, "one batch set covers K");
   __shared__ float red[NW][S][4][64];
-  __shared__ __align__(16) uint8_t lcodes[kDecMaxM * kDecCodeStride];
-  __shared__ __align__(16) uint8_t lscales[kDecMaxM * kDecScaleStride];
+  __shared__ __align__(16) uint8_t lcodes[NW][U][MAXM][kDecRowBytes];
+  __shared__ uint8_t lscales[NW][U][MAXM][kTileK / kBlock];
   __shared__ float rtab[128];
   __shared__ uint32_t wmax[NW];
   __shared__ float swg[NVFP4_MAX_SEGMENTS];
-  const float wgv = load_segment_scale(w_g, st);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nb = K / kBlock;
-  const int B = M * nb;
+  const int nslot = M * U * (kTileK / kBlock);   // live slots: rows < M
   const int tiles = (K + kTileK - 1) / kTileK;
   const int nstrips = (N + kStrip - 1) / kStrip;
   const int strip0 = blockIdx.x * S;
 
-  // 1. activations: block b = tid + kThreads j is row b / nb, block column b % nb
-  uint4 xv[kPer][2];
+  // 1. this wave's activation blocks
+  uint4 xv[kQ][2];
 #pragma unroll
-  for (int j = 0; j < kPer; ++j) {
-    const int b = tid + kThreads * j;
-    int r, c;
-    split_block(b, nb, inv_nb, r, c);
-    const bool ok = b < B;
-    const uint4* q = reinterpret_cast<const uint4*>(x + (ok ? (int64_t)r * ldx + (int64_t)c * kBlock : 0));
-    xv[j][0] = ok ? q[0] : make_uint4(0u, 0u, 0u, 0u);
-    xv[j][1] = ok ? q[1] : make_uint4(0u, 0u, 0u, 0u);
+  for (int q = 0; q < kQ; ++q) {
+    xv[q][0] = xv[q][1] = make_uint4(0u, 0u, 0u, 0u);
+    if (64 * q < nslot) {                          // uniform
+      const int i = lane + 64 * q;
+      const int row = i / (8 * U), u = (i >> 3) % U;
+      const int c = (wave + NW * u) * 8 + (i & 7);
+      if (i < nslot && c < nb) {
+        const uint4* p = reinterpret_cast<const uint4*>(x + (int64_t)row * ldx + (int64_t)c * kBlock);
+        xv[q][0] = p[0];
+        xv[q][1] = p[1];
+      }
+    }
   }
   __builtin_amdgcn_sched_barrier(0);
 
@@ -300,8 +305,10 @@ __global__ __launch_bounds__(64 * NW) void linear_decode_kernel(
     }
   }
   __builtin_amdgcn_sched_barrier(0);
+  const float wgv = load_segment_scale(w_g, st);
 
-  // 3. reciprocal table and tensor amax (max of |x| as bf16 bit patterns)
+  // 3. reciprocal table and tensor amax (max of |x| as bf16 bit patterns); the
+  //    waves together hold every block of the tensor
   fill_rcp_table(rtab);
   float amax;
   if (amax_in) {
@@ -310,7 +317,7 @@ __global__ __launch_bounds__(64 * NW) void linear_decode_kernel(
   } else {
     u16x2_t mp = {0, 0};
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) mp = absmax_pk(xv[j][1], absmax_pk(xv[j][0], mp));
+    for (int q = 0; q < kQ; ++q) mp = absmax_pk(xv[q][1], absmax_pk(xv[q][0], mp));
     uint32_t m = max(mp.x, mp.y);
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o, 64));
@@ -326,27 +333,29 @@ __global__ __launch_bounds__(64 * NW) void linear_decode_kernel(
   const bool writer = blockIdx.x == 0;
   if (writer && tid == 0) *a_g = g_dec;
 
-  // 4. encode into LDS (and, in workgroup 0, to the canonical output buffers)
+  // 4. encode this wave's blocks into its LDS area (workgroup 0 also writes the
+  //    canonical codes and scales); the remaining weight batches go out between
+  //    encode steps
 #pragma unroll
-  for (int j = 0; j < kPer; ++j) {
-    const int b = tid + kThreads * j;
-    if (b < B) {
-      int row, col;
-      split_block(b, nb, inv_nb, row, col);
-      uint2 c;
-      const uint32_t sc = encode_bf16_block(xv[j][0], xv[j][1], cx, c);
-      *reinterpret_cast<uint2*>(lcodes + row * kDecCodeStride + col * 8) = c;
-      lscales[row * kDecScaleStride + col] = (uint8_t)sc;
-      if (writer) {
-        *reinterpret_cast<uint2*>(a_codes + (int64_t)row * (K / 2) + col * 8) = c;
-        a_scales[(int64_t)row * nb + col] = (uint8_t)sc;
+  for (int q = 0; q < kQ; ++q) {
+    if (64 * q < nslot) {                          // uniform
+      const int i = lane + 64 * q;
+      const int row = i / (8 * U), u = (i >> 3) % U, j = i & 7;
+      const int c = (wave + NW * u) * 8 + j;
+      if (i < nslot && c < nb) {
+        uint2 cd;
+        const uint32_t sc = encode_bf16_block(xv[q][0], xv[q][1], cx, cd);
+        *reinterpret_cast<uint2*>(&lcodes[wave][u][row][j * 8]) = cd;
+        lscales[wave][u][row][j] = (uint8_t)sc;
+        if (writer) {
+          *reinterpret_cast<uint2*>(a_codes + (int64_t)row * (K / 2) + c * 8) = cd;
+          a_scales[(int64_t)row * nb + c] = (uint8_t)sc;
+        }
       }
     }
-    // the remaining weight batches go out spread over the encode loop: a wave
-    // stalled on issuing them yields its SIMD to the other wave's encode work
 #pragma unroll
     for (int u = PRE; u < U; ++u)
-      if (j == (u - PRE) * kPer / (U - PRE)) {
+      if (q == (u - PRE) * SPREAD / (U > PRE ? U - PRE : 1)) {
         const int t = min(wave + NW * u, tiles - 1);
 #pragma unroll
         for (int s = 0; s < S; ++s) {
@@ -355,15 +364,14 @@ __global__ __launch_bounds__(64 * NW) void linear_decode_kernel(
         }
       }
   }
+  // the lanes of this wave read each other's LDS writes
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-  // 5. publish the LDS activations
-  __syncthreads();
-
-  // 6. MFMAs: lane (r, g) of tile t takes row r, k in [t * 128 + 32 g, + 32)
+  // 5. MFMAs: lane (r, g) of tile t takes row r, k in [t * 128 + 32 g, + 32)
   const int r = lane & 15, g = lane >> 4;
   const int arow = min(r, M - 1);
-  const uint8_t* lc = lcodes + arow * kDecCodeStride + g * 16;
-  const uint8_t* ls = lscales + arow * kDecScaleStride + g * 2;
   float4_t acc[S];
 #pragma unroll
   for (int s = 0; s < S; ++s) acc[s] = float4_t{0.f, 0.f, 0.f, 0.f};
@@ -373,17 +381,16 @@ __global__ __launch_bounds__(64 * NW) void linear_decode_kernel(
     const int k0 = t * kTileK + 32 * g;
     const bool live0 = (wave + NW * u < tiles) && (r < M) && (k0 < K);
     const bool live1 = live0 && (k0 + kBlock < K);
-    const uint2 c0 = *reinterpret_cast<const uint2*>(lc + t * 64);
-    const uint2 c1 = *reinterpret_cast<const uint2*>(lc + t * 64 + 8);
-    const uint32_t sc = (live0 ? (uint32_t)ls[t * 8] : 0u) | (live1 ? (uint32_t)ls[t * 8 + 1] << 8 : 0u);
+    const uint4 cv = *reinterpret_cast<const uint4*>(&lcodes[wave][u][arow][16 * g]);
+    const uint32_t sc = (live0 ? (uint32_t)lscales[wave][u][arow][2 * g] : 0u) |
+                        (live1 ? (uint32_t)lscales[wave][u][arow][2 * g + 1] << 8 : 0u);
     half8_t A[4];
-    decode_a(make_uint4(c0.x, c0.y, c1.x, c1.y), sc, 0xFFFFu, A);
+    decode_a(cv, sc, 0xFFFFu, A);
 #pragma unroll
     for (int s = 0; s < S; ++s) tile_mfma(A, wv[u][s], wsc[u][s], acc[s]);
   }
   reduce_store<S, NW>(acc, red, swg, wgv, strip0, M, N, st, g_dec, out, ldo);
 }
-
 
 __global__ void fill_zero_kernel(float* __restrict__ out, int M, int N, int64_t ldo) {
   const int64_t total = (int64_t)M * N;
@@ -415,12 +422,20 @@ hipError_t launch_gemm_skinny(const uint8_t* a_codes, const uint8_t* a_scales, c
   return hipGetLastError();
 }
 
-// first weight batches requested before the activation work: two for up to 4
-// rows (little encode work to hide), one for more rows (measured best)
-constexpr int kDecPreSmallM = 2, kDecPreLargeM = 1;
-
 bool linear_decode_fits(int64_t M, int64_t K) {
   return M >= 1 && M <= kDecMaxM && K >= kBlock && K <= kDecMaxK;
+}
+
+// One instantiation per row bound: one weight batch requested before the
+// activation work (more delays the amax barrier), the other batches spread over
+// the first SPREAD encode steps (measured best for each bound).
+template <int MAXM, int SPREAD>
+static void launch_decode(int grid, hipStream_t stream, const uint16_t* x, int64_t ldx, const float* amax_in,
+                          uint8_t* a_codes, uint8_t* a_scales, float* a_g, int M, int K, const uint8_t* w_codes,
+                          const uint8_t* w_scales, int N, const SegTable& st, const float* w_g, float* out,
+                          int64_t ldo) {
+  linear_decode_kernel<kSkS, kSkNW, kSkU, MAXM, 1, SPREAD><<<grid, 64 * kSkNW, 0, stream>>>(
+      x, ldx, amax_in, a_codes, a_scales, a_g, M, K, w_codes, w_scales, N, st, w_g, out, ldo);
 }
 
 hipError_t launch_linear_decode(const uint16_t* x, int64_t ldx, const float* amax_in, uint8_t* a_codes,
@@ -429,14 +444,18 @@ hipError_t launch_linear_decode(const uint16_t* x, int64_t ldx, const float* ama
                                 int64_t ldo, hipStream_t stream) {
   const int nstrips = (N + kStrip - 1) / kStrip;
   const int grid = (nstrips + kSkS - 1) / kSkS;
-  if (M <= 4)
-    linear_decode_kernel<kSkS, kSkNW, kSkU, kDecPreSmallM><<<grid, 64 * kSkNW, 0, stream>>>(
-        x, ldx, amax_in, a_codes, a_scales, a_g, M, K, 1.0f / (float)(K / kBlock), w_codes, w_scales, N, st, w_g,
-        out, ldo);
+  if (M == 1)
+    launch_decode<1, 1>(grid, stream, x, ldx, amax_in, a_codes, a_scales, a_g, M, K, w_codes, w_scales, N, st, w_g,
+                        out, ldo);
+  else if (M <= 4)
+    launch_decode<4, 3>(grid, stream, x, ldx, amax_in, a_codes, a_scales, a_g, M, K, w_codes, w_scales, N, st, w_g,
+                        out, ldo);
+  else if (M <= 8)
+    launch_decode<8, 5>(grid, stream, x, ldx, amax_in, a_codes, a_scales, a_g, M, K, w_codes, w_scales, N, st, w_g,
+                        out, ldo);
   else
-    linear_decode_kernel<kSkS, kSkNW, kSkU, kDecPreLargeM><<<grid, 64 * kSkNW, 0, stream>>>(
-        x, ldx, amax_in, a_codes, a_scales, a_g, M, K, 1.0f / (float)(K / kBlock), w_codes, w_scales, N, st, w_g,
-        out, ldo);
+    launch_decode<kDecMaxM, 10>(grid, stream, x, ldx, amax_in, a_codes, a_scales, a_g, M, K, w_codes, w_scales, N,
+                                st, w_g, out, ldo);
   return hipGetLastError();
 }
 

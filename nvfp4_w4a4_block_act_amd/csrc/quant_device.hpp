@@ -130,7 +130,7 @@ __device__ __forceinline__ uint32_t encode_bf16_block(uint4 v0, uint4 v1, const 
   const uint32_t d[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
   const float bmax = __uint_as_float(absmax_bits(v0, absmax_bits(v1, 0u)) << 16);
   uint32_t lo = 0, hi = 0, sc;
-  if (cx.fast) {
+  if (__builtin_expect(cx.fast, 1)) {   // keeps the rare exact-division path out of line
     const float t = div_rn(bmax, 6.0f, kRcp6);
     sc = e4m3_encode_rne_sat(t * cx.g_enc);   // t == 0 gives code 0
     const float rb = div_rn(cx.g_enc, e4m3_value(sc), cx.rtab[sc]);

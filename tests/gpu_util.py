@@ -40,13 +40,15 @@ def gpu_pack(w, segments):
     return pw
 
 
-def oracle_linear_rows(x_bits, w, segments, rows=None, cols=None):
+def oracle_linear_rows(x_bits, w, segments, rows=None, cols=None, amax=None):
     """Oracle output (fp64) and error bound for output rows x cols of the linear layer.
 
-    The activation scale uses the whole tensor's maximum; each weight row is
-    encoded with its segment's maximum over the whole segment."""
+    The activation scale uses the whole tensor's maximum (or the calibrated
+    `amax` when given); each weight row is encoded with its segment's maximum
+    over the whole segment."""
     x32 = bf16_to_f32(x_bits)
-    amax = np.float32(np.max(np.abs(x32))) if x32.size else np.float32(0)
+    if amax is None:
+        amax = np.float32(np.max(np.abs(x32))) if x32.size else np.float32(0)
     rows = np.arange(x32.shape[0]) if rows is None else np.asarray(rows)
     cols = np.arange(w.shape[0]) if cols is None else np.asarray(cols)
     ac, as_, ag, _ = Q.quantize(x32[rows], amax)

@@ -45,7 +45,7 @@ def test_linear_decode_full(M):
 
 @pytest.mark.parametrize("M,N,K,nseg", [
     (1, 16, 16, 1), (3, 37, 48, 2), (7, 200, 272, 3), (16, 129, 144, 2), (16, 520, 5136, 4), (5, 64, 4112, 1),
-    (16, 300, 17408, 2),
+    (16, 300, 17408, 2), (2, 40, 160, 1), (8, 100, 5120, 2), (9, 64, 1040, 3), (4, 1000, 5104, 2),
 ])
 def test_linear_ragged(M, N, K, nseg):
     rng = np.random.default_rng(M * 7 + N + K)
@@ -60,6 +60,25 @@ def test_linear_ragged(M, N, K, nseg):
     out, _, _ = run_both(x, pw)
     ref, bnd = oracle_linear_rows(x, w, segs)
     assert_within_tol(out.cpu().numpy().astype(np.float64), ref, bnd, f"linear ragged {M}x{K}x{N}")
+
+
+@pytest.mark.parametrize("M", [1, 2, 4, 5, 8, 9, 16])
+def test_linear_static_amax_each_row_bound(M):
+    """The one-launch kernel has one instantiation per row bound (1, 4, 8, 16):
+    a calibrated amax below the tensor's (saturating blocks) at each of them."""
+    rng = np.random.default_rng(100 + M)
+    N, K = 96, 1296
+    w = (0.05 * rng.standard_normal((N, K))).astype(np.float32)
+    segs = [(0, 40), (40, N)]
+    x = W.random_act(200 + M, M, K, "student_t")
+    amax = np.float32(float(np.max(np.abs(W.bf16_to_f32(x)))) / 3)
+    say(f"[linear] static amax M={M}")
+    pw = gpu_pack(w, segs)
+    out, c, s = run_both(x, pw, amax=amax)
+    oc, os_, _, _ = Q.quantize(W.bf16_to_f32(x), amax)
+    assert np.array_equal(c, oc) and np.array_equal(s, os_)
+    ref, bnd = oracle_linear_rows(x, w, segs, amax=amax)
+    assert_within_tol(out.cpu().numpy().astype(np.float64), ref, bnd, f"linear static M={M}")
 
 
 def test_linear_static_amax_and_prefill_path():

@@ -136,18 +136,24 @@ __device__ __forceinline__ void strip_pointers(const uint8_t* w_codes, const uin
 }
 
 // The skinny GEMM of one workgroup: S strips of 16 columns, NW waves splitting
-// the k tiles (wave w takes tiles w, w + NW, ...), U tiles per load batch.  Every
-// load of a batch is issued before any decode and batches have no branches
-// (tiles past the end are clamped and their activation scales zeroed), so the
-// waits before each tile's MFMAs stay progressive.
+// the k tiles (wave w takes tiles w, w + NW, ...), U tiles per outer iteration.
+// Software pipeline: a batch is one tile of the S strips, and a wave keeps two
+// batches in flight (batch u + 2 is requested after the MFMAs of batch u).
+// Requesting every batch up front instead lets the memory system accept the
+// loads first come, first served: the first waves of a workgroup get all their
+// data early, the last wave gets all of it at the end of the stream and then
+// has its whole decode and MFMA work left (about 1 us of tail).  Batches have no
+// branches (tiles past the end are clamped and their activation scales zeroed),
+// so the waits before each batch's MFMAs stay progressive.
 template <int S, int NW, int U, bool AL16>
 __global__ __launch_bounds__(64 * NW) void gemm_skinny_kernel(
     const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales, const float* __restrict__ a_g,
     int M, int K, const uint8_t* __restrict__ w_codes, const uint8_t* __restrict__ w_scales, int N,
     SegTable st, const float* __restrict__ w_g, float* __restrict__ out, int64_t ldo) {
+  constexpr int kDepth = 2;
+  static_assert(U >= kDepth, "pipeline depth");
   __shared__ float red[NW][S][4][64];
   __shared__ float swg[NVFP4_MAX_SEGMENTS];
-  const float wgv = load_segment_scale(w_g, st);
   const float ag = *a_g;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -165,6 +171,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_skinny_kernel(
   const uint8_t* wc[S];
   const uint8_t* ws[S];
   strip_pointers<S>(w_codes, w_scales, strip0, nstrips, tiles, lane, wc, ws);
+  const float wgv = load_segment_scale(w_g, st);
 
   float4_t acc[S];
 #pragma unroll
@@ -172,23 +179,24 @@ __global__ __launch_bounds__(64 * NW) void gemm_skinny_kernel(
 
   for (int t0 = wave; t0 < full; t0 += NW * U) {
     // activation fragments first (a few hundred bytes, L2-resident after the
-    // first workgroups), so the first tile's wait does not cover the weights
+    // first workgroups), then the first two weight batches
     uint4 av[U];
     uint32_t asc[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) load_a_full<AL16>(ac, as, min(t0 + u * NW, full - 1), av[u], asc[u]);
     uint4 wv[U][S];
     uint32_t wsc[U][S];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
+    auto request = [&](int u) {
       const int t = min(t0 + u * NW, full - 1);
 #pragma unroll
       for (int s = 0; s < S; ++s) {
         wv[u][s] = *reinterpret_cast<const uint4*>(wc[s] + (int64_t)t * kChunkCodes);
         wsc[u][s] = *reinterpret_cast<const uint16_t*>(ws[s] + (int64_t)t * kChunkScales);
       }
-    }
-    __builtin_amdgcn_sched_barrier(0);   // keep the whole batch in flight before any MFMA
+    };
+#pragma unroll
+    for (int u = 0; u < kDepth; ++u) request(u);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const uint32_t live = (t0 + u * NW < full) ? amask : 0u;
@@ -196,6 +204,9 @@ __global__ __launch_bounds__(64 * NW) void gemm_skinny_kernel(
       decode_a(av[u], asc[u], live, A);
 #pragma unroll
       for (int s = 0; s < S; ++s) tile_mfma(A, wv[u][s], wsc[u][s], acc[s]);
+      __builtin_amdgcn_sched_barrier(0);
+      if (u + kDepth < U) request(u + kDepth);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
   if (full < tiles && wave == full % NW) {           // ragged last tile
@@ -232,14 +243,14 @@ __global__ __launch_bounds__(64 * NW) void gemm_skinny_kernel(
 //  1. each lane loads its bf16 blocks: slot i = lane + 64 q is row i / (8 U),
 //     tile u = (i / 8) % U, block j = i % 8 of that tile, i.e. block column
 //     (w + NW u) * 8 + j; groups of eight lanes read 256 contiguous bytes;
-//  2. the wave requests its first PRE weight batches;
+//  2. the wave requests its first weight batch (one k tile of its S strips);
 //  3. amax: per-lane maximum, wave reduction, one barrier (which also
 //     publishes the reciprocal table of the fast encoder);
-//  4. each lane encodes its blocks into the wave's LDS area; the remaining
-//     weight batches are requested between encode steps (a wave stalled on
-//     issuing loads under memory back-pressure yields its SIMD to the other
-//     wave's encode work);
-//  5. the MFMA tiles read their activation operand from the wave's LDS area.
+//  4. each lane encodes its blocks into the wave's LDS area; the second weight
+//     batch is requested after the first encode step;
+//  5. the MFMA tiles read their activation operand from the wave's LDS area,
+//     software-pipelined with two weight batches in flight (batch u + 2 is
+//     requested after the MFMAs of batch u; see the skinny GEMM above).
 // MAXM bounds the rows a launch may have: the encode steps are unrolled over
 // MAXM rows' slots, and smaller instantiations (less code to fetch at each
 // launch) are measurably faster for small M.  The results are bit-identical to
@@ -248,7 +259,7 @@ constexpr int kDecMaxM = 16;
 constexpr int kDecMaxK = 5120;
 constexpr int kDecRowBytes = kTileK / 2 + 16;   // LDS bytes per row of one tile (padded)
 
-template <int S, int NW, int U, int MAXM, int PRE, int SPREAD>
+template <int S, int NW, int U, int MAXM>
 __global__ __launch_bounds__(64 * NW) void linear_decode_kernel(
     const uint16_t* __restrict__ x, int64_t ldx, const float* __restrict__ amax_in, uint8_t* __restrict__ a_codes,
     uint8_t* __restrict__ a_scales, float* __restrict__ a_g, int M, int K, const uint8_t* __restrict__ w_codes,
@@ -289,21 +300,22 @@ __global__ __launch_bounds__(64 * NW) void linear_decode_kernel(
   }
   __builtin_amdgcn_sched_barrier(0);
 
-  // 2. first weight batches: tile t = wave + NW u (clamped past the end)
+  // 2. the first weight batch: batch u is tile t = wave + NW u of the S strips
+  //    (clamped past the end; its activation scales are zeroed then)
   const uint8_t* wc[S];
   const uint8_t* ws[S];
   strip_pointers<S>(w_codes, w_scales, strip0, nstrips, tiles, lane, wc, ws);
   uint4 wv[U][S];
   uint32_t wsc[U][S];
-#pragma unroll
-  for (int u = 0; u < PRE; ++u) {
+  auto request = [&](int u) {
     const int t = min(wave + NW * u, tiles - 1);
 #pragma unroll
     for (int s = 0; s < S; ++s) {
       wv[u][s] = *reinterpret_cast<const uint4*>(wc[s] + (int64_t)t * kChunkCodes);
       wsc[u][s] = *reinterpret_cast<const uint16_t*>(ws[s] + (int64_t)t * kChunkScales);
     }
-  }
+  };
+  request(0);
   __builtin_amdgcn_sched_barrier(0);
   const float wgv = load_segment_scale(w_g, st);
 
@@ -334,8 +346,8 @@ __global__ __launch_bounds__(64 * NW) void linear_decode_kernel(
   if (writer && tid == 0) *a_g = g_dec;
 
   // 4. encode this wave's blocks into its LDS area (workgroup 0 also writes the
-  //    canonical codes and scales); the remaining weight batches go out between
-  //    encode steps
+  //    canonical codes and scales); the second weight batch goes out after the
+  //    first encode step
 #pragma unroll
   for (int q = 0; q < kQ; ++q) {
     if (64 * q < nslot) {                          // uniform
@@ -353,23 +365,15 @@ __global__ __launch_bounds__(64 * NW) void linear_decode_kernel(
         }
       }
     }
-#pragma unroll
-    for (int u = PRE; u < U; ++u)
-      if (q == (u - PRE) * SPREAD / (U > PRE ? U - PRE : 1)) {
-        const int t = min(wave + NW * u, tiles - 1);
-#pragma unroll
-        for (int s = 0; s < S; ++s) {
-          wv[u][s] = *reinterpret_cast<const uint4*>(wc[s] + (int64_t)t * kChunkCodes);
-          wsc[u][s] = *reinterpret_cast<const uint16_t*>(ws[s] + (int64_t)t * kChunkScales);
-        }
-      }
+    if (q == 0) request(1);
   }
   // the lanes of this wave read each other's LDS writes
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-  // 5. MFMAs: lane (r, g) of tile t takes row r, k in [t * 128 + 32 g, + 32)
+  // 5. MFMAs, software-pipelined: batch u + 2 is requested after the MFMAs of
+  //    batch u.  Lane (r, g) of tile t takes row r, k in [t * 128 + 32 g, + 32)
   const int r = lane & 15, g = lane >> 4;
   const int arow = min(r, M - 1);
   float4_t acc[S];
@@ -388,6 +392,9 @@ __global__ __launch_bounds__(64 * NW) void linear_decode_kernel(
     decode_a(cv, sc, 0xFFFFu, A);
 #pragma unroll
     for (int s = 0; s < S; ++s) tile_mfma(A, wv[u][s], wsc[u][s], acc[s]);
+    __builtin_amdgcn_sched_barrier(0);
+    if (u + 2 < U) request(u + 2);             // two batches in flight
+    __builtin_amdgcn_sched_barrier(0);
   }
   reduce_store<S, NW>(acc, red, swg, wgv, strip0, M, N, st, g_dec, out, ldo);
 }
@@ -426,15 +433,13 @@ bool linear_decode_fits(int64_t M, int64_t K) {
   return M >= 1 && M <= kDecMaxM && K >= kBlock && K <= kDecMaxK;
 }
 
-// One instantiation per row bound: one weight batch requested before the
-// activation work (more delays the amax barrier), the other batches spread over
-// the first SPREAD encode steps (measured best for each bound).
-template <int MAXM, int SPREAD>
+// One instantiation per row bound.
+template <int MAXM>
 static void launch_decode(int grid, hipStream_t stream, const uint16_t* x, int64_t ldx, const float* amax_in,
                           uint8_t* a_codes, uint8_t* a_scales, float* a_g, int M, int K, const uint8_t* w_codes,
                           const uint8_t* w_scales, int N, const SegTable& st, const float* w_g, float* out,
                           int64_t ldo) {
-  linear_decode_kernel<kSkS, kSkNW, kSkU, MAXM, 1, SPREAD><<<grid, 64 * kSkNW, 0, stream>>>(
+  linear_decode_kernel<kSkS, kSkNW, kSkU, MAXM><<<grid, 64 * kSkNW, 0, stream>>>(
       x, ldx, amax_in, a_codes, a_scales, a_g, M, K, w_codes, w_scales, N, st, w_g, out, ldo);
 }
 
@@ -445,17 +450,17 @@ hipError_t launch_linear_decode(const uint16_t* x, int64_t ldx, const float* ama
   const int nstrips = (N + kStrip - 1) / kStrip;
   const int grid = (nstrips + kSkS - 1) / kSkS;
   if (M == 1)
-    launch_decode<1, 1>(grid, stream, x, ldx, amax_in, a_codes, a_scales, a_g, M, K, w_codes, w_scales, N, st, w_g,
-                        out, ldo);
+    launch_decode<1>(grid, stream, x, ldx, amax_in, a_codes, a_scales, a_g, M, K, w_codes, w_scales, N, st, w_g, out,
+                     ldo);
   else if (M <= 4)
-    launch_decode<4, 3>(grid, stream, x, ldx, amax_in, a_codes, a_scales, a_g, M, K, w_codes, w_scales, N, st, w_g,
-                        out, ldo);
+    launch_decode<4>(grid, stream, x, ldx, amax_in, a_codes, a_scales, a_g, M, K, w_codes, w_scales, N, st, w_g, out,
+                     ldo);
   else if (M <= 8)
-    launch_decode<8, 5>(grid, stream, x, ldx, amax_in, a_codes, a_scales, a_g, M, K, w_codes, w_scales, N, st, w_g,
-                        out, ldo);
+    launch_decode<8>(grid, stream, x, ldx, amax_in, a_codes, a_scales, a_g, M, K, w_codes, w_scales, N, st, w_g, out,
+                     ldo);
   else
-    launch_decode<kDecMaxM, 10>(grid, stream, x, ldx, amax_in, a_codes, a_scales, a_g, M, K, w_codes, w_scales, N,
-                                st, w_g, out, ldo);
+    launch_decode<kDecMaxM>(grid, stream, x, ldx, amax_in, a_codes, a_scales, a_g, M, K, w_codes, w_scales, N, st,
+                            w_g, out, ldo);
   return hipGetLastError();
 }
 

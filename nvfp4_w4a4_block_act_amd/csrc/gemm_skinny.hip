@@ -319,18 +319,20 @@ __global__ __launch_bounds__(64 * NW) void linear_decode_kernel(
   __builtin_amdgcn_sched_barrier(0);
   const float wgv = load_segment_scale(w_g, st);
 
-  // 3. reciprocal table and tensor amax (max of |x| as bf16 bit patterns); the
-  //    waves together hold every block of the tensor
+  // 3. reciprocal table, block maxima (kept for the encode) and tensor amax
+  //    (max of |x| as bf16 bit patterns); the waves together hold every block
   fill_rcp_table(rtab);
+  uint32_t bm[kQ];
+#pragma unroll
+  for (int q = 0; q < kQ; ++q) bm[q] = absmax_bits(xv[q][0], absmax_bits(xv[q][1], 0u));
   float amax;
   if (amax_in) {
     amax = *amax_in;
     __syncthreads();
   } else {
-    u16x2_t mp = {0, 0};
+    uint32_t m = 0;
 #pragma unroll
-    for (int q = 0; q < kQ; ++q) mp = absmax_pk(xv[q][1], absmax_pk(xv[q][0], mp));
-    uint32_t m = max(mp.x, mp.y);
+    for (int q = 0; q < kQ; ++q) m = max(m, bm[q]);
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o, 64));
     if (lane == 0) wmax[wave] = m;
@@ -356,7 +358,7 @@ __global__ __launch_bounds__(64 * NW) void linear_decode_kernel(
       const int c = (wave + NW * u) * 8 + j;
       if (i < nslot && c < nb) {
         uint2 cd;
-        const uint32_t sc = encode_bf16_block(xv[q][0], xv[q][1], cx, cd);
+        const uint32_t sc = encode_bf16_block_max(xv[q][0], xv[q][1], bm[q], cx, cd);
         *reinterpret_cast<uint2*>(&lcodes[wave][u][row][j * 8]) = cd;
         lscales[wave][u][row][j] = (uint8_t)sc;
         if (writer) {

@@ -126,9 +126,12 @@ __device__ __forceinline__ EncCtx make_ctx(float amax, const float* rtab) {
 #define NVFP4_MUL(v) ((v) * rb)
 #define NVFP4_MUL_KEEP_ZERO(v) (((v) == 0.0f) ? (v) : (v) * rb)
 
-__device__ __forceinline__ uint32_t encode_bf16_block(uint4 v0, uint4 v1, const EncCtx& cx, uint2& c) {
+// Same, given the block's |x| maximum as a bf16 bit pattern (absmax_bits of the
+// two chunks), for callers that already have it.
+__device__ __forceinline__ uint32_t encode_bf16_block_max(uint4 v0, uint4 v1, uint32_t bmax_bits, const EncCtx& cx,
+                                                          uint2& c) {
   const uint32_t d[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-  const float bmax = __uint_as_float(absmax_bits(v0, absmax_bits(v1, 0u)) << 16);
+  const float bmax = __uint_as_float(bmax_bits << 16);
   uint32_t lo = 0, hi = 0, sc;
   if (__builtin_expect(cx.fast, 1)) {   // keeps the rare exact-division path out of line
     const float t = div_rn(bmax, 6.0f, kRcp6);
@@ -149,6 +152,10 @@ __device__ __forceinline__ uint32_t encode_bf16_block(uint4 v0, uint4 v1, const 
   }
   c = make_uint2(lo, hi);
   return sc;
+}
+
+__device__ __forceinline__ uint32_t encode_bf16_block(uint4 v0, uint4 v1, const EncCtx& cx, uint2& c) {
+  return encode_bf16_block_max(v0, v1, absmax_bits(v0, absmax_bits(v1, 0u)), cx, c);
 }
 #undef NVFP4_MUL_KEEP_ZERO
 #undef NVFP4_MUL

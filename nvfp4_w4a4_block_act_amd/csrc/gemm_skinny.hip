@@ -269,8 +269,10 @@ __global__ __launch_bounds__(64 * NW) void linear_decode_kernel(
   constexpr int kQ = (kSlots + 63) / 64;
   static_assert(NW * U * kTileK >= kDecMaxK, "one batch set covers K");
   __shared__ float red[NW][S][4][64];
-  __shared__ __align__(16) uint8_t lcodes[NW][U][MAXM][kDecRowBytes];
-  __shared__ uint8_t lscales[NW][U][MAXM][kTileK / kBlock];
+  // wave-private activation tiles, row-major over (row, tile): slot group
+  // v = row * U + u holds the 8 blocks of row `row` in the wave's tile u
+  __shared__ __align__(16) uint8_t lcodes[NW][MAXM * U][kDecRowBytes];
+  __shared__ __align__(4) uint8_t lscales[NW][MAXM * U][kTileK / kBlock];
   __shared__ float rtab[128];
   __shared__ uint32_t wmax[NW];
   __shared__ float swg[NVFP4_MAX_SEGMENTS];
@@ -282,8 +284,9 @@ __global__ __launch_bounds__(64 * NW) void linear_decode_kernel(
   const int nstrips = (N + kStrip - 1) / kStrip;
   const int strip0 = blockIdx.x * S;
 
-  // 1. this wave's activation blocks
+  // 1. this wave's activation blocks; bit q of `live` marks a block to encode
   uint4 xv[kQ][2];
+  uint32_t live = 0;
 #pragma unroll
   for (int q = 0; q < kQ; ++q) {
     xv[q][0] = xv[q][1] = make_uint4(0u, 0u, 0u, 0u);
@@ -295,6 +298,7 @@ __global__ __launch_bounds__(64 * NW) void linear_decode_kernel(
         const uint4* p = reinterpret_cast<const uint4*>(x + (int64_t)row * ldx + (int64_t)c * kBlock);
         xv[q][0] = p[0];
         xv[q][1] = p[1];
+        live |= 1u << q;
       }
     }
   }
@@ -350,18 +354,19 @@ __global__ __launch_bounds__(64 * NW) void linear_decode_kernel(
   // 4. encode this wave's blocks into its LDS area (workgroup 0 also writes the
   //    canonical codes and scales); the second weight batch goes out after the
   //    first encode step
+  uint8_t* const lc = &lcodes[wave][lane >> 3][(lane & 7) * 8];   // slot group (lane >> 3) + 8 q
+  uint8_t* const ls = &lscales[wave][lane >> 3][lane & 7];
 #pragma unroll
   for (int q = 0; q < kQ; ++q) {
     if (64 * q < nslot) {                          // uniform
-      const int i = lane + 64 * q;
-      const int row = i / (8 * U), u = (i >> 3) % U, j = i & 7;
-      const int c = (wave + NW * u) * 8 + j;
-      if (i < nslot && c < nb) {
+      if ((live >> q) & 1u) {
         uint2 cd;
         const uint32_t sc = encode_bf16_block_max(xv[q][0], xv[q][1], bm[q], cx, cd);
-        *reinterpret_cast<uint2*>(&lcodes[wave][u][row][j * 8]) = cd;
-        lscales[wave][u][row][j] = (uint8_t)sc;
+        *reinterpret_cast<uint2*>(lc + q * 8 * kDecRowBytes) = cd;
+        ls[q * 8 * (kTileK / kBlock)] = (uint8_t)sc;
         if (writer) {
+          const int i = lane + 64 * q;
+          const int row = i / (8 * U), c = (wave + NW * ((i >> 3) % U)) * 8 + (i & 7);
           *reinterpret_cast<uint2*>(a_codes + (int64_t)row * (K / 2) + c * 8) = cd;
           a_scales[(int64_t)row * nb + c] = (uint8_t)sc;
         }
@@ -387,9 +392,9 @@ __global__ __launch_bounds__(64 * NW) void linear_decode_kernel(
     const int k0 = t * kTileK + 32 * g;
     const bool live0 = (wave + NW * u < tiles) && (r < M) && (k0 < K);
     const bool live1 = live0 && (k0 + kBlock < K);
-    const uint4 cv = *reinterpret_cast<const uint4*>(&lcodes[wave][u][arow][16 * g]);
-    const uint32_t sc = (live0 ? (uint32_t)lscales[wave][u][arow][2 * g] : 0u) |
-                        (live1 ? (uint32_t)lscales[wave][u][arow][2 * g + 1] << 8 : 0u);
+    const uint4 cv = *reinterpret_cast<const uint4*>(&lcodes[wave][arow * U + u][16 * g]);
+    const uint32_t s2 = *reinterpret_cast<const uint16_t*>(&lscales[wave][arow * U + u][2 * g]);
+    const uint32_t sc = s2 & ((live0 ? 0xFFu : 0u) | (live1 ? 0xFF00u : 0u));
     half8_t A[4];
     decode_a(cv, sc, 0xFFFFu, A);
 #pragma unroll

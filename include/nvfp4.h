@@ -141,7 +141,10 @@ nvfp4_status nvfp4_weight_to_canonical(const uint8_t* w_codes, const uint8_t* w_
  *   segs              HOST array of nseg segments tiling [0, N) in order.
  *   w_g_dec           device array of nseg per-module g_dec values.
  *   out               fp32 [M][ldo], ldo >= N; must not overlap any input.
- * M <= 16 runs the bandwidth-bound skinny path; larger M the MFMA path.
+ * M <= 16 runs the bandwidth-bound skinny path; larger M the MFMA path, which
+ * addresses its operands with 32-bit byte offsets: for M > 16 the activation
+ * codes (M * K / 2 bytes) and the packed weight codes must each be below 4 GiB,
+ * else NVFP4_ESHAPE.
  * ------------------------------------------------------------------------- */
 nvfp4_status nvfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_g_dec,
                         int64_t M, int64_t K,
@@ -160,7 +163,7 @@ nvfp4_status nvfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const f
  * workgroup encodes the (small) activation tensor itself while its weight loads
  * are in flight, so no workspace and no hand-over between workgroups is needed.
  * Other inputs run the quantizer and the GEMM kernels back to back on the
- * stream.
+ * stream (the GEMM's 4 GiB operand limit for M > 16 applies).
  *
  *   workspace  device scratch of nvfp4_linear_workspace_bytes(M, K) bytes
  *              (NULL allowed when that is 0 or amax_in is given); contents
@@ -207,7 +210,8 @@ nvfp4_status nvfp4_pack_weight_gate_up(const float* w, int64_t I, int64_t K, int
 /* h's NVFP4 codes [M][I/2], scales [M][I/16] (canonical layout) and g_dec
  * (amax_h / 2688) from activations a (as for nvfp4_gemm) and a weight from
  * nvfp4_pack_weight_gate_up.  amax_h: device pointer to the calibrated maximum
- * of |h| (finite, >= 0; larger |h| saturate).  Requires I % 128 == 0, K >= 16. */
+ * of |h| (finite, >= 0; larger |h| saturate).  Requires I % 128 == 0, K >= 16,
+ * and activation codes and packed weight codes each below 4 GiB (NVFP4_ESHAPE). */
 nvfp4_status nvfp4_gemm_swiglu_quantize(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_g_dec,
                                         int64_t M, int64_t K, const uint8_t* w_codes, const uint8_t* w_scales,
                                         int64_t I, const float* w_g_dec, const float* amax_h,

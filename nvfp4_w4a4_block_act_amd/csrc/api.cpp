@@ -128,12 +128,22 @@ nvfp4_status nvfp4_weight_to_canonical(const uint8_t* w_codes, const uint8_t* w_
                                                     static_cast<hipStream_t>(stream)));
 }
 
+// The MFMA GEMM (M > 16) addresses each operand buffer with 32-bit byte offsets:
+// the activation codes (M * K / 2 bytes) and the packed weight codes must each
+// stay below 4 GiB (their scales are an eighth of that).
+static bool mfma_operands_fit(int64_t M, int64_t K, int64_t N) {
+  size_t cb = 0, sb = 0;
+  nvfp4_packed_weight_bytes(N, K, &cb, &sb);
+  return (uint64_t)M * (uint64_t)(K / 2) < (1ull << 32) && (uint64_t)cb < (1ull << 32);
+}
+
 nvfp4_status nvfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_g_dec, int64_t M,
                         int64_t K, const uint8_t* w_codes, const uint8_t* w_scales, int64_t N,
                         const nvfp4_segment* segs, const float* w_g_dec, int32_t nseg, float* out, int64_t ldo,
                         void* stream) {
   if (M < 0 || K < 0 || N < 1) return NVFP4_EINVAL;
   if (K % 16 != 0 || M >= kMaxDim || K >= kMaxDim || N >= kMaxDim || ldo < N) return NVFP4_ESHAPE;
+  if (M > 16 && !mfma_operands_fit(M, K, N)) return NVFP4_ESHAPE;
   const nvfp4_status ss = check_segments(segs, nseg, N);
   if (ss != NVFP4_OK) return ss;
   if (M == 0) return NVFP4_OK;
@@ -177,6 +187,7 @@ nvfp4_status nvfp4_linear(const void* x_bf16, int64_t M, int64_t K, int64_t ldx,
                           void* stream) {
   if (M < 0 || K < 0 || N < 1) return NVFP4_EINVAL;
   if (K % 16 != 0 || M >= kMaxDim || K >= kMaxDim || N >= kMaxDim || ldx < K || ldo < N) return NVFP4_ESHAPE;
+  if (M > 16 && !mfma_operands_fit(M, K, N)) return NVFP4_ESHAPE;
   const nvfp4_status ss = check_segments(segs, nseg, N);
   if (ss != NVFP4_OK) return ss;
   if (!a_g_dec) return NVFP4_EINVAL;
@@ -254,6 +265,7 @@ nvfp4_status nvfp4_gemm_swiglu_quantize(const uint8_t* a_codes, const uint8_t* a
   if (M < 0 || K < 0 || I < 1) return NVFP4_EINVAL;
   if (I % 128 != 0 || K % 16 != 0 || K < 16 || M >= kMaxDim || K >= kMaxDim || 2 * I >= kMaxDim)
     return NVFP4_ESHAPE;
+  if (!mfma_operands_fit(M, K, 2 * I)) return NVFP4_ESHAPE;
   if (!amax_h || !h_g_dec) return NVFP4_EINVAL;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (M == 0) return launched(nvfp4::launch_quantize_act(nullptr, 0, 0, 0, amax_h, nullptr, nullptr, h_g_dec,

@@ -49,37 +49,65 @@ constexpr int kHalfRow = 9;                            // uint4 pieces per LDS w
 
 __device__ __forceinline__ int swz_a(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
 
+// Buffer loads: the base address and size live in a resource descriptor (scalar
+// registers), each lane keeps a fixed 32-bit byte offset, and the per-k-tile
+// step is a scalar offset, so advancing to the next tile costs no vector
+// instructions.  Offsets are 32-bit: every operand buffer must be below 4 GiB
+// (checked by the launcher).
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ uint4 buf_u4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+__device__ __forceinline__ uint2 buf_u2(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
+}
+__device__ __forceinline__ uint32_t buf_u32(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+}
+__device__ __forceinline__ uint32_t buf_u16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
+}
+__device__ __forceinline__ uint32_t buf_u8(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(r, voff, soff, 0);
+}
+
 // Per-thread coalesced activation slots: slot q = tid + 512 s covers row q / 4
 // of the tile and its 16-byte piece q % 4.
 struct ASlots {
-  const uint8_t* p[2];
+  uint32_t off[2];                                     // byte offset of the piece in tile 0
   int lds[2];                                          // uint4 index inside an LDS stage
   int koff[2];                                         // k offset of the piece inside a tile
 };
 
 template <bool AL16, bool TAIL>
-__device__ __forceinline__ void load_a_codes(const ASlots& as, int t, int full, int K, uint4 (&r)[2]) {
+__device__ __forceinline__ void load_a_codes(__amdgpu_buffer_rsrc_t ra, const ASlots& as, int t, int full, int K,
+                                             uint4 (&r)[2]) {
+  const uint32_t soff = (uint32_t)t * 64u;
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
-    const uint8_t* p = as.p[s] + (int64_t)t * 64;
     if (TAIL && t == full) {
       const int k0 = t * kTileK + as.koff[s];
       uint4 v = make_uint4(0u, 0u, 0u, 0u);
       if (k0 < K) {
-        const uint2 x0 = reinterpret_cast<const uint2*>(p)[0];
+        const uint2 x0 = buf_u2(ra, as.off[s], soff);
         v.x = x0.x;
         v.y = x0.y;
         if (k0 + 16 < K) {
-          const uint2 x1 = reinterpret_cast<const uint2*>(p)[1];
+          const uint2 x1 = buf_u2(ra, as.off[s] + 8u, soff);
           v.z = x1.x;
           v.w = x1.y;
         }
       }
       r[s] = v;
     } else if (AL16) {
-      r[s] = *reinterpret_cast<const uint4*>(p);
+      r[s] = buf_u4(ra, as.off[s], soff);
     } else {
-      const uint2 x0 = reinterpret_cast<const uint2*>(p)[0], x1 = reinterpret_cast<const uint2*>(p)[1];
+      const uint2 x0 = buf_u2(ra, as.off[s], soff), x1 = buf_u2(ra, as.off[s] + 8u, soff);
       r[s] = make_uint4(x0.x, x0.y, x1.x, x1.y);
     }
   }
@@ -87,21 +115,22 @@ __device__ __forceinline__ void load_a_codes(const ASlots& as, int t, int full, 
 
 // A lane's four scale bytes (blocks 4h .. 4h + 3 of the tile) for each row tile.
 template <bool AL4, bool TAIL>
-__device__ __forceinline__ void load_a_scales(const uint8_t* const (&sp)[2], int t, int full, int kbase, int K,
-                                              uint32_t (&r)[2]) {
+__device__ __forceinline__ void load_a_scales(__amdgpu_buffer_rsrc_t rs, const uint32_t (&so)[2], int t, int full,
+                                              int kbase, int K, uint32_t (&r)[2]) {
+  const uint32_t soff = (uint32_t)t * 8u;
 #pragma unroll
   for (int rt = 0; rt < 2; ++rt) {
-    const uint8_t* q = sp[rt] + (int64_t)t * 8;
     if (TAIL && t == full) {
       uint32_t v = 0;
 #pragma unroll
       for (int b = 0; b < 4; ++b)
-        if (kbase + 16 * b < K) v |= (uint32_t)q[b] << (8 * b);
+        if (kbase + 16 * b < K) v |= buf_u8(rs, so[rt] + b, soff) << (8 * b);
       r[rt] = v;
     } else if (AL4) {
-      r[rt] = *reinterpret_cast<const uint32_t*>(q);
+      r[rt] = buf_u32(rs, so[rt], soff);
     } else {
-      r[rt] = (uint32_t)q[0] | ((uint32_t)q[1] << 8) | ((uint32_t)q[2] << 16) | ((uint32_t)q[3] << 24);
+      r[rt] = buf_u8(rs, so[rt], soff) | (buf_u8(rs, so[rt] + 1, soff) << 8) | (buf_u8(rs, so[rt] + 2, soff) << 16) |
+              (buf_u8(rs, so[rt] + 3, soff) << 24);
     }
   }
 }
@@ -110,8 +139,8 @@ __device__ __forceinline__ void load_a_scales(const uint8_t* const (&sp)[2], int
 // k groups g = 2 * ((tid / 16) % 2) + s for s = 0, 1; slot s is decoded into the
 // half-tile s (groups 0 and 2 feed MFMA steps 0-3, groups 1 and 3 steps 4-7).
 struct WSlots {
-  const uint8_t* wp[2];
-  const uint8_t* wsp[2];
+  uint32_t off[2];                                     // byte offset of the slot's codes in tile 0
+  uint32_t soff[2];                                    // byte offset of its two scales in tile 0
   int lds;                                             // uint4 index of this thread's row + piece 4 * (g / 2)
 };
 
@@ -120,11 +149,12 @@ struct RawW {
   uint32_t s[2];
 };
 
-__device__ __forceinline__ void load_w_tile(const WSlots& ws, int t, RawW& r) {
+__device__ __forceinline__ void load_w_tile(__amdgpu_buffer_rsrc_t rc, __amdgpu_buffer_rsrc_t rs, const WSlots& ws,
+                                            int t, RawW& r) {
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
-    r.c[s] = *reinterpret_cast<const uint4*>(ws.wp[s] + (int64_t)t * kChunkCodes);
-    r.s[s] = *reinterpret_cast<const uint16_t*>(ws.wsp[s] + (int64_t)t * kChunkScales);
+    r.c[s] = buf_u4(rc, ws.off[s], (uint32_t)t * kChunkCodes);
+    r.s[s] = buf_u16(rs, ws.soff[s], (uint32_t)t * kChunkScales);
   }
 }
 
@@ -243,35 +273,39 @@ __global__ __launch_bounds__(kMfThreads, 1) void gemm_mfma_kernel(
   const int m0 = tm * kBM, n0 = n_lo + tn * kBN;
 
   // ---- activation code slots (coalesced loads) and this lane's scale rows
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(a_codes, (uint32_t)((int64_t)M * (K / 2)));
+  const __amdgpu_buffer_rsrc_t ras = make_rsrc(a_scales, (uint32_t)((int64_t)M * (K / kBlock)));
   ASlots as;
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
     const int q = tid + kMfThreads * s;
     const int r = q >> 2, p = q & 3;
     const int rc = min(m0 + r, M - 1);
-    as.p[s] = a_codes + (int64_t)rc * (K / 2) + 16 * p;
+    as.off[s] = (uint32_t)rc * (uint32_t)(K / 2) + 16u * p;
     as.lds[s] = r * 4 + (p ^ swz_a(r));
     as.koff[s] = 32 * p;
   }
   const int i = lane & 31, h = lane >> 5;
-  const uint8_t* asp[2];
+  uint32_t asp[2];
   uint32_t amask[2];
 #pragma unroll
   for (int rt = 0; rt < 2; ++rt) {
     const int row = m0 + wm * 64 + rt * 32 + i;
-    asp[rt] = a_scales + (int64_t)min(row, M - 1) * (K / kBlock) + 4 * h;
+    asp[rt] = (uint32_t)min(row, M - 1) * (uint32_t)(K / kBlock) + 4u * h;
     amask[rt] = row < M ? 0xFFFFFFFFu : 0u;    // padded rows decode to zeros
   }
   // ---- weight slots
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(w_codes, (uint32_t)((int64_t)nstrips * tiles * kChunkCodes));
+  const __amdgpu_buffer_rsrc_t rws = make_rsrc(w_scales, (uint32_t)((int64_t)nstrips * tiles * kChunkScales));
   WSlots ws;
   {
     const int sl = tid >> 5, n = tid & 15, gg = (tid >> 4) & 1;
-    const int64_t strip = min(n0 / kStrip + sl, nstrips - 1);
+    const uint32_t strip = (uint32_t)min(n0 / kStrip + sl, nstrips - 1);
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       const int g = 2 * gg + s;
-      ws.wp[s] = w_codes + strip * tiles * kChunkCodes + chunk_code_off(n, g);
-      ws.wsp[s] = w_scales + strip * tiles * kChunkScales + chunk_scale_off(n, g);
+      ws.off[s] = strip * (uint32_t)tiles * kChunkCodes + (uint32_t)chunk_code_off(n, g);
+      ws.soff[s] = strip * (uint32_t)tiles * kChunkScales + (uint32_t)chunk_scale_off(n, g);
     }
     ws.lds = (sl * kStrip + n) * kHalfRow + 4 * gg;
   }
@@ -293,11 +327,11 @@ __global__ __launch_bounds__(kMfThreads, 1) void gemm_mfma_kernel(
   RawW rw0, rw1;                                        // weights of tiles 0 and 1
   {
     uint4 a0[2];
-    load_a_codes<AL16, TAIL>(as, tb, full, K, a0);
-    load_a_scales<AL4, TAIL>(asp, tb, full, tb * kTileK + kb, K, sc0);
-    load_w_tile(ws, tb, rw0);
-    load_a_codes<AL16, TAIL>(as, min(tb + 1, last), full, K, an);
-    load_w_tile(ws, min(tb + 1, last), rw1);
+    load_a_codes<AL16, TAIL>(ra, as, tb, full, K, a0);
+    load_a_scales<AL4, TAIL>(ras, asp, tb, full, tb * kTileK + kb, K, sc0);
+    load_w_tile(rw, rws, ws, tb, rw0);
+    load_a_codes<AL16, TAIL>(ra, as, min(tb + 1, last), full, K, an);
+    load_w_tile(rw, rws, ws, min(tb + 1, last), rw1);
 #pragma unroll
     for (int d = 0; d < 4; ++d) store_w_piece(ws, rw0, 0, d, sW[0]);
     sA[0][as.lds[0]] = a0[0];
@@ -320,15 +354,15 @@ __global__ __launch_bounds__(kMfThreads, 1) void gemm_mfma_kernel(
     const uint4* sa = sA[(t - tb) & 1];
     uint4* sa_next = sA[(t - tb + 1) & 1];
     uint32_t scn[2];
-    load_a_scales<AL4, TAIL>(asp, min(t + 1, last), full, min(t + 1, last) * kTileK + kb, K, scn);
+    load_a_scales<AL4, TAIL>(ras, asp, min(t + 1, last), full, min(t + 1, last) * kTileK + kb, K, scn);
     mfma_half<0, SW>(sa, sW[0], scc, amask, arow0, bbase, h, ws, rwc, 1, sW[1], acc);
     sa_next[as.lds[0]] = an[0];
     sa_next[as.lds[1]] = an[1];
-    load_a_codes<AL16, TAIL>(as, min(t + 2, last), full, K, an);
+    load_a_codes<AL16, TAIL>(ra, as, min(t + 2, last), full, K, an);
     __syncthreads();
     mfma_half<1, SW>(sa, sW[1], scc, amask, arow0, bbase, h, ws, rwn, 0, sW[0], acc);
     rwc = rwn;
-    load_w_tile(ws, min(t + 2, last), rwn);
+    load_w_tile(rw, rws, ws, min(t + 2, last), rwn);
     scc[0] = scn[0];
     scc[1] = scn[1];
     __syncthreads();

@@ -86,6 +86,8 @@ def g(a=A, sa=A + (1 << 20), ag=A + (2 << 20), M=4, K=32, wc=A + (3 << 20), ws=A
     (dict(sg=tuple((i, i + 1) for i in range(17)), N=17, ldo=17), 4), (dict(sg=()), 4),
     (dict(a=None), 1), (dict(wg=None), 1), (dict(out=A + (6 << 20) + 4), 3), (dict(wc=A + 8), 3),
     (dict(out=A + (3 << 20) + 256), 1),                           # out overlaps the weight codes
+    (dict(M=1 << 20, K=8192), 2),                                 # MFMA path: activation codes reach 4 GiB
+    (dict(M=32, N=1 << 20, K=8192, sg=((0, 1 << 20),), ldo=1 << 20), 2),   # packed weight codes reach 4 GiB
 ])
 def test_gemm_validation(kw, status):
     assert g(**kw) == status
@@ -122,6 +124,7 @@ def lin(x=A, M=4, K=32, ldx=32, amax=None, ac=A + (1 << 20), as_=A + (2 << 20), 
     (dict(x=None), 1), (dict(out=A + 4), 3), (dict(ldx=36), 3), (dict(out=A + (4 << 20) + 128), 1),
     (dict(M=4096, K=4096, ldx=4096, ac=A + (64 << 20), as_=A + (80 << 20), ag=A + (96 << 20), wc=A + (128 << 20),
           ws=A + (160 << 20), wg=A + (192 << 20), out=A + (256 << 20)), 5),
+    (dict(M=1 << 20, K=8192, ldx=8192), 2),                      # MFMA path: activation codes reach 4 GiB
 ])
 def test_linear_validation(kw, status):
     assert lin(**kw) == status
@@ -148,6 +151,7 @@ def swq(a=A, sa=A + (1 << 20), ag=A + (2 << 20), M=32, K=32, wc=A + (3 << 20), w
 @pytest.mark.parametrize("kw,status", [
     (dict(M=-1), 1), (dict(I=64), 2), (dict(K=8), 2), (dict(amax=None), 1), (dict(hg=None), 1),
     (dict(a=None), 1), (dict(hc=A + 8), 3), (dict(hc=A + (3 << 20) + 256), 1),
+    (dict(M=1 << 20, K=8192), 2),                                 # activation codes reach 4 GiB
 ])
 def test_gemm_swiglu_quantize_validation(kw, status):
     assert swq(**kw) == status

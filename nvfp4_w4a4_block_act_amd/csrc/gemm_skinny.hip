@@ -11,8 +11,8 @@
 //    (codes + scales); a workgroup of eight waves owns S = 3 strips of 16
 //    output columns (256 workgroups for N = 12288, one per CU), and its waves
 //    split the K tiles of those strips (split-K inside the workgroup, reduced
-//    through LDS); each wave requests all of its tiles (5 x 3 KB at K = 5120)
-//    before it decodes any, so every CU keeps its whole share in flight;
+//    through LDS); each wave keeps two batches (one k tile of the S strips
+//    each) in flight, requesting batch u + 2 after the MFMAs of batch u;
 //  * the 16 x 16 x 32 fp16 MFMA does the arithmetic with M padded to 16:
 //    lane l holds row/column l % 16 and the 32 k of group g = l / 16 of a
 //    128-k tile.  A K-permutation shared by both operands makes each lane's

@@ -84,42 +84,51 @@ __device__ __forceinline__ void decode_a(uint4 v, uint32_t sc, uint32_t amask, h
   A[3] = decode8(v.w, s1);
 }
 
-// Cross-wave sum of the per-wave partial tiles and the epilogue: output element
-// e = (s, i, l) is row 4 * (l / 16) + i, column (strip0 + s) * 16 + l % 16, and is
-// stored as fl(sum * fl(a_g * w_g[seg(n)])).  The per-segment scales were loaded
-// at kernel start (wgv, thread t < nseg holds w_g[t]) so the epilogue does not
-// wait on memory behind the weight stream; they reach the other threads through
-// LDS with the partial tiles.
+// Cross-wave sum of the per-wave partial tiles and the epilogue.  Only live
+// outputs are visited: e = row * (16 S) + c for row < M, c = 16 s + l % 16, so
+// consecutive threads store consecutive columns of one row.  MFMA lane l holds
+// rows 4 (l / 16) + i in acc[s][i], i.e. output (row, c) is partial
+// red[w][s][row % 4][16 (row / 4) + c % 16] of wave w.  The result is
+// fl(sum * fl(a_g * w_g[seg(n)])).  The per-segment scales were loaded at
+// kernel start (wgv: lane t < nseg of every wave holds w_g[t]) so the epilogue
+// does not wait on memory behind the weight stream; wave 0 turns them into
+// column scales (one cross-lane read per column) before the barrier, while the
+// other waves finish their tiles, and they reach the other threads through LDS
+// with the partial tiles.
 template <int S, int NW>
 __device__ __forceinline__ void reduce_store(const float4_t (&acc)[S], float (&red)[NW][S][4][64],
-                                             float (&swg)[NVFP4_MAX_SEGMENTS], float wgv, int strip0, int M,
-                                             int N, const SegTable& st, float ag, float* __restrict__ out,
-                                             int64_t ldo) {
+                                             float (&scol)[S * kStrip], float wgv, int strip0, int M, int N,
+                                             const SegTable& st, float ag, float* __restrict__ out, int64_t ldo) {
+  static_assert(S * kStrip <= 64, "one lane of wave 0 per column");
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (wave == 0) {
+    const int n = min(strip0 * kStrip + min(lane, S * kStrip - 1), N - 1);
+    const float wc = __shfl(wgv, seg_of(st, n), 64);
+    if (lane < S * kStrip) scol[lane] = wc;
+  }
 #pragma unroll
   for (int s = 0; s < S; ++s)
 #pragma unroll
     for (int i = 0; i < 4; ++i) red[wave][s][i][lane] = acc[s][i];
-  if (threadIdx.x < (unsigned)st.nseg) swg[threadIdx.x] = wgv;
   __syncthreads();
-  for (int e = threadIdx.x; e < S * 256; e += 64 * NW) {
-    const int s = e >> 8, i = (e >> 6) & 3, l = e & 63;
-    const int row = 4 * (l >> 4) + i;
-    const int n = (strip0 + s) * kStrip + (l & 15);
-    if (row >= M || n >= N) continue;
+  for (int e = threadIdx.x; e < M * S * kStrip; e += 64 * NW) {
+    const int row = e / (S * kStrip), c = e % (S * kStrip);
+    const int n = strip0 * kStrip + c;
+    if (n >= N) continue;
+    const int s = c / kStrip, l = (row >> 2) * kStrip + c % kStrip;
     float v = 0.f;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) v += red[w][s][i][l];
-    out[(int64_t)row * ldo + n] = v * (ag * swg[seg_of(st, n)]);
+    for (int w = 0; w < NW; ++w) v += red[w][s][row & 3][l];
+    out[(int64_t)row * ldo + n] = v * (ag * scol[c]);
   }
 }
 
-// The caller's early load of the per-segment scales (see reduce_store): thread
-// t < nseg keeps w_g[t].  Branch-free (every thread reads a valid entry), so the
-// kernel's argument loads are not split around a branch at kernel start; issue
-// it after the first activation and weight loads.
+// The caller's early load of the per-segment scales (see reduce_store): lane
+// t < nseg of each wave keeps w_g[t].  Branch-free (every thread reads a valid
+// entry), so the kernel's argument loads are not split around a branch at
+// kernel start; issue it after the first activation and weight loads.
 __device__ __forceinline__ float load_segment_scale(const float* __restrict__ w_g, const SegTable& st) {
-  return w_g[min((int)threadIdx.x, st.nseg - 1)];
+  return w_g[min((int)(threadIdx.x & 63), st.nseg - 1)];
 }
 
 // Weight pointers of lane `lane` for the S strips starting at strip0 (clamped;
@@ -153,7 +162,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_skinny_kernel(
   constexpr int kDepth = 2;
   static_assert(U >= kDepth, "pipeline depth");
   __shared__ float red[NW][S][4][64];
-  __shared__ float swg[NVFP4_MAX_SEGMENTS];
+  __shared__ float scol[S * kStrip];
   const float ag = *a_g;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -223,7 +232,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_skinny_kernel(
       tile_mfma(A, w, wsv, acc[s]);
     }
   }
-  reduce_store<S, NW>(acc, red, swg, wgv, strip0, M, N, st, ag, out, ldo);
+  reduce_store<S, NW>(acc, red, scol, wgv, strip0, M, N, st, ag, out, ldo);
 }
 
 // ---- decode-form linear layer in one launch (M <= 16, K <= 5120).
@@ -275,7 +284,7 @@ __global__ __launch_bounds__(64 * NW) void linear_decode_kernel(
   __shared__ __align__(4) uint8_t lscales[NW][MAXM * U][kTileK / kBlock];
   __shared__ float rtab[128];
   __shared__ uint32_t wmax[NW];
-  __shared__ float swg[NVFP4_MAX_SEGMENTS];
+  __shared__ float scol[S * kStrip];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nb = K / kBlock;
@@ -403,7 +412,7 @@ __global__ __launch_bounds__(64 * NW) void linear_decode_kernel(
     if (u + 2 < U) request(u + 2);             // two batches in flight
     __builtin_amdgcn_sched_barrier(0);
   }
-  reduce_store<S, NW>(acc, red, swg, wgv, strip0, M, N, st, g_dec, out, ldo);
+  reduce_store<S, NW>(acc, red, scol, wgv, strip0, M, N, st, g_dec, out, ldo);
 }
 
 __global__ void fill_zero_kernel(float* __restrict__ out, int M, int N, int64_t ldo) {

@@ -131,6 +131,20 @@ __device__ __forceinline__ float load_segment_scale(const float* __restrict__ w_
   return w_g[min((int)(threadIdx.x & 63), st.nseg - 1)];
 }
 
+// Issue priority of this wave (s_setprio takes an immediate; p is a constant
+// after unrolling).  The two waves sharing a SIMD otherwise issue oldest first,
+// so the younger one falls behind and its weight batches end the stream alone.
+// With the priority lowered after each batch, a wave that is behind outranks
+// its partner until it catches up; the results do not change.
+__device__ __forceinline__ void set_issue_priority(int p) {
+  switch (p < 0 ? 0 : (p > 3 ? 3 : p)) {
+    case 0: __builtin_amdgcn_s_setprio(0); break;
+    case 1: __builtin_amdgcn_s_setprio(1); break;
+    case 2: __builtin_amdgcn_s_setprio(2); break;
+    default: __builtin_amdgcn_s_setprio(3); break;
+  }
+}
+
 // Weight pointers of lane `lane` for the S strips starting at strip0 (clamped;
 // columns past N are never stored).
 template <int S>
@@ -262,13 +276,14 @@ __global__ __launch_bounds__(64 * NW) void gemm_skinny_kernel(
 //     requested after the MFMAs of batch u; see the skinny GEMM above).
 // MAXM bounds the rows a launch may have: the encode steps are unrolled over
 // MAXM rows' slots, and smaller instantiations (less code to fetch at each
-// launch) are measurably faster for small M.  The results are bit-identical to
-// the activation quantizer followed by the skinny GEMM.
+// launch) are measurably faster for small M.  BAL lowers each wave's issue
+// priority after each batch of step 5 (set_issue_priority).  The results are
+// bit-identical to the activation quantizer followed by the skinny GEMM.
 constexpr int kDecMaxM = 16;
 constexpr int kDecMaxK = 5120;
 constexpr int kDecRowBytes = kTileK / 2 + 16;   // LDS bytes per row of one tile (padded)
 
-template <int S, int NW, int U, int MAXM>
+template <int S, int NW, int U, int MAXM, bool BAL>
 __global__ __launch_bounds__(64 * NW) void linear_decode_kernel(
     const uint16_t* __restrict__ x, int64_t ldx, const float* __restrict__ amax_in, uint8_t* __restrict__ a_codes,
     uint8_t* __restrict__ a_scales, float* __restrict__ a_g, int M, int K, const uint8_t* __restrict__ w_codes,
@@ -383,6 +398,7 @@ __global__ __launch_bounds__(64 * NW) void linear_decode_kernel(
     }
     if (q == 0) request(1);
   }
+  if constexpr (BAL) set_issue_priority(3);
   // the lanes of this wave read each other's LDS writes
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
@@ -410,8 +426,10 @@ __global__ __launch_bounds__(64 * NW) void linear_decode_kernel(
     for (int s = 0; s < S; ++s) tile_mfma(A, wv[u][s], wsc[u][s], acc[s]);
     __builtin_amdgcn_sched_barrier(0);
     if (u + 2 < U) request(u + 2);             // two batches in flight
+    if constexpr (BAL) set_issue_priority(U - 2 - u);
     __builtin_amdgcn_sched_barrier(0);
   }
+  if constexpr (BAL) __builtin_amdgcn_s_setprio(0);
   reduce_store<S, NW>(acc, red, scol, wgv, strip0, M, N, st, g_dec, out, ldo);
 }
 
@@ -449,13 +467,16 @@ bool linear_decode_fits(int64_t M, int64_t K) {
   return M >= 1 && M <= kDecMaxM && K >= kBlock && K <= kDecMaxK;
 }
 
-// One instantiation per row bound.
+// One instantiation per row bound.  The issue-priority balancing of the waves
+// measured about 0.4 us per launch faster for the 1-row instantiation at
+// K = 5120, N = 12288, slower for 2 to 6 rows and no better for 8 or 16 (or in
+// the skinny GEMM).
 template <int MAXM>
 static void launch_decode(int grid, hipStream_t stream, const uint16_t* x, int64_t ldx, const float* amax_in,
                           uint8_t* a_codes, uint8_t* a_scales, float* a_g, int M, int K, const uint8_t* w_codes,
                           const uint8_t* w_scales, int N, const SegTable& st, const float* w_g, float* out,
                           int64_t ldo) {
-  linear_decode_kernel<kSkS, kSkNW, kSkU, MAXM><<<grid, 64 * kSkNW, 0, stream>>>(
+  linear_decode_kernel<kSkS, kSkNW, kSkU, MAXM, MAXM == 1><<<grid, 64 * kSkNW, 0, stream>>>(
       x, ldx, amax_in, a_codes, a_scales, a_g, M, K, w_codes, w_scales, N, st, w_g, out, ldo);
 }
 

@@ -368,6 +368,43 @@ def cpu_threads():
         return os.cpu_count()
 
 
+def host_info():
+    """The host the CPU baseline ran on: CPU model, logical CPUs, the ones this
+    process may use, RAM and the BLAS numpy calls (vendor, threads)."""
+    info = {"cpu_model": None, "os_cpu_count": os.cpu_count(), "affinity": cpu_threads(), "ram_gb": None,
+            "blas": None}
+    try:
+        with open("/proc/cpuinfo") as f:
+            info["cpu_model"] = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), None)
+        with open("/proc/meminfo") as f:
+            kb = next(int(l.split()[1]) for l in f if l.startswith("MemTotal"))
+        info["ram_gb"] = round(kb / 2**20, 1)
+    except Exception:
+        pass
+    try:
+        import threadpoolctl
+        info["blas"] = [{k: d.get(k) for k in ("internal_api", "version", "num_threads")}
+                        for d in threadpoolctl.threadpool_info() if d.get("user_api") == "blas"]
+    except Exception:
+        pass
+    return info
+
+
+def gpu_state():
+    """GPU clocks and power as rocm-smi reports them, read once after the timed
+    region (a snapshot, not an average over it); None where unavailable."""
+    import subprocess
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks", "--showpower", "--json"], capture_output=True,
+                           text=True, timeout=20)
+        card = next(iter(json.loads(r.stdout).values()))
+        keep = {k: v for k, v in card.items() if "sclk" in k.lower() or "mclk" in k.lower()
+                or "power" in k.lower()}
+        return keep or None
+    except Exception:
+        return None
+
+
 # ---------------------------------------------------------------------------------------
 DECODE_COUNTERS = "linear_decode_kernel_decode_k5120_n12288_counters.md"
 DECODE_SOURCES = ("gemm_skinny.hip", "quant_device.hpp", "common.hpp")
@@ -489,7 +526,7 @@ def bench_decode(args, torch, nv, W, dev):
                    "linear_kernel": {str(M): {k: round(v, 3) if isinstance(v, float) else v for k, v in kern[M].items()}
                                    for M in Ms},
                    "call_forms": {str(M): forms[M] for M in Ms},
-                   "device_copy_GBps": round(copy_gbs, 1)},
+                   "device_copy_GBps": round(copy_gbs, 1), "gpu_state_after_run": gpu_state()},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic(DECODE_COUNTERS, DECODE_SOURCES),
@@ -523,7 +560,7 @@ def cpu_baseline_decode(d16, Ms, target_s, step_bytes):
         reps += 1
     per_step = t_all / reps * (N / cols)
     return {"value": round(step_bytes / per_step / 1e9, 4), "unit": "GB/s", "cores": cpu_threads(),
-            "kind": "oracle",
+            "kind": "oracle", "host": host_info(),
             "sample": f"{reps} oracle steps over {cols} of {N} output columns (all three token counts), "
                       f"scaled by {N / cols:.1f} to the full step; {t_all:.1f} s of CPU time"}
 
@@ -559,7 +596,8 @@ def bench_gemm(args, torch, nv, W, dev):
     value = flops * steps / sec / 1e12
     mean, med, p10, p90 = kernel_time_pairs(torch, lambda i: nv.gemm(c, s, g, pw, out=out), max(8, steps // 2), 2)
     achieved = flops / mean / 1e12
-    return {
+    state = gpu_state()
+    res = {
         "metric": "NVFP4 W4A4 prefill GEMM TFLOP/s (quantize + GEMM + epilogue), % of MI355X fp16 MFMA roofline",
         "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": steps, "warmup": min(args.warmup, 5),
         "ms_per_step": round(sec / steps * 1e3, 4), "higher_is_better": True, "scaling": "weak",
@@ -568,11 +606,39 @@ def bench_gemm(args, torch, nv, W, dev):
         "data": "synthetic",
         "config": {"workload": d.name, "M": M, "K": K, "N": N, "segments": len(d.segments),
                    "gemm_kernel_mean_ms": round(mean * 1e3, 4), "gemm_kernel_median_ms": round(med * 1e3, 4),
-                   "gemm_kernel_p10_ms": round(p10 * 1e3, 4), "gemm_kernel_p90_ms": round(p90 * 1e3, 4)},
+                   "gemm_kernel_p10_ms": round(p10 * 1e3, 4), "gemm_kernel_p90_ms": round(p90 * 1e3, 4),
+                   "gpu_state_after_run": state},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": F16_MFMA_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / F16_MFMA_PEAK_TFLOPS, 4), "traffic": None,
                      "kernel": "gemm_mfma_kernel"},
     }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_gemm(d, args.cpu_seconds, flops)
+    return res
+
+
+def cpu_baseline_gemm(d, target_s, flops):
+    """The oracle on the host for one quantize + GEMM step of a prefill workload:
+    quantize and decode a row sample of the activations, fp64 GEMM against a
+    column sample of the pre-decoded weight, scaled to the full M x N."""
+    from oracle import gemm as G
+    from oracle import nvfp4 as Q
+    from workloads import bf16_to_f32
+    rows, cols = min(d.M, 512), min(d.N, 4096)
+    wc, ws, wg, _ = Q.quantize(d.w[:cols], np.float32(np.max(np.abs(d.w[:cols]))))
+    w_hat = Q.dequantize(wc, ws, wg)
+    t_all, reps = 0.0, 0
+    while t_all < target_s and reps < 1000:
+        t0 = time.perf_counter()
+        c, s, g, _ = Q.quantize(bf16_to_f32(d.x_bits[:rows]))
+        G.gemm_f64(Q.dequantize(c, s, g), w_hat)
+        t_all += time.perf_counter() - t0
+        reps += 1
+    per_step = t_all / reps * (d.M / rows) * (d.N / cols)
+    return {"value": round(flops / per_step / 1e12, 6), "unit": "TFLOP/s", "cores": cpu_threads(),
+            "kind": "oracle", "host": host_info(),
+            "sample": f"{reps} oracle steps over {rows} of {d.M} rows and {cols} of {d.N} output columns, "
+                      f"scaled by {d.M * d.N / (rows * cols):.1f} to the full step; {t_all:.1f} s of CPU time"}
 
 
 def bench_quantize(args, torch, nv, W, dev):

@@ -93,3 +93,28 @@ def test_linear_static_amax_and_prefill_path():
     out, _, _ = run_both(x, pw)
     ref, bnd = oracle_linear_rows(x, d.w, d.segments)
     assert_within_tol(out.cpu().numpy().astype(np.float64), ref, bnd, "linear prefill path")
+
+
+@pytest.mark.parametrize("M", [1, 3, 6, 13])
+def test_linear_strided_input_and_output(M):
+    """Row strides beyond K (input) and N (output), for each row-bound instance of
+    the one-launch kernel: the result is bit-identical to quantize + GEMM on
+    contiguous tensors, and the output columns outside the slice are untouched."""
+    rng = np.random.default_rng(400 + M)
+    K, N = 1040, 300
+    segs = [(0, 100), (100, N)]
+    w = (0.02 * rng.standard_normal((N, K))).astype(np.float32)
+    pw = gpu_pack(w, segs)
+    x_bits = W.random_act(500 + M, M, K, "normal")
+    say(f"[strided linear] M={M} K={K} N={N}")
+    x = to_dev_bf16(x_bits)
+    xwide = torch.zeros((M, K + 48), dtype=torch.bfloat16, device=DEV)
+    xwide[:, 16:16 + K] = x
+    big = torch.full((M, N + 40), 7.0, dtype=torch.float32, device=DEV)
+    out, (c, s, g) = nv.linear(xwide[:, 16:16 + K], pw, out=big[:, 8:8 + N])
+    c2, s2, g2 = nv.quantize_act(x)
+    ref = nv.gemm(c2, s2, g2, pw)
+    torch.cuda.synchronize()
+    assert torch.equal(c, c2) and torch.equal(s, s2) and torch.equal(g, g2)
+    assert torch.equal(big[:, 8:8 + N], ref)
+    assert torch.all(big[:, :8] == 7.0) and torch.all(big[:, 8 + N:] == 7.0)

@@ -28,6 +28,8 @@
  *    mag 0..7 = 0, 0.5, 1, 1.5, 2, 3, 4, 6.  Scales are E4M3FN bytes
  *    (0x00..0x7E).  Blocks of 16 run along K.
  *  - Every pointer must be 16-byte aligned; K must be a multiple of 16.
+ *  - Every row count, column count and leading dimension must be below 2^31
+ *    (NVFP4_ESHAPE otherwise).
  */
 #ifndef NVFP4_W4A4_H
 #define NVFP4_W4A4_H
@@ -45,7 +47,7 @@ extern "C" {
 typedef enum {
   NVFP4_OK = 0,
   NVFP4_EINVAL = 1,     /* null pointer, negative size, overlapping input/output buffers */
-  NVFP4_ESHAPE = 2,     /* K % 16 != 0, leading dimension too small, size overflow */
+  NVFP4_ESHAPE = 2,     /* K % 16 != 0, leading dimension too small, a size or leading dimension >= 2^31 */
   NVFP4_EALIGN = 3,     /* pointer not 16-byte aligned, or bf16 leading dimension not a multiple of 8 */
   NVFP4_ESEGMENTS = 4,  /* segments do not tile [0, N) in order, or nseg not in [1, 16] */
   NVFP4_EWORKSPACE = 5, /* workspace missing or smaller than the *_workspace_bytes query */
@@ -260,8 +262,8 @@ nvfp4_status nvfp4_quantize_stats(const void* x_bf16, int64_t M, int64_t K, int6
  *   code  = sign(x) << 7 | E4M3 RNE of fl(|x| * g_enc), saturating at 448;
  *   decode = bf16 (RNE) of fl(E4M3(code) * g_dec).
  * n elements, contiguous; amax is a device pointer to the calibrated maximum
- * (finite, >= 0).  Pointers 16-byte aligned; any n.  Non-finite x are outside
- * the contract.
+ * (finite, >= 0).  Pointers 16-byte aligned; any n below 2^48 (NVFP4_ESHAPE
+ * otherwise).  Non-finite x are outside the contract.
  * ------------------------------------------------------------------------- */
 nvfp4_status nvfp4_kv_fp8_encode(const void* x_bf16, int64_t n, const float* amax, uint8_t* codes, void* stream);
 

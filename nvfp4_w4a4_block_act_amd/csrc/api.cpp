@@ -13,6 +13,10 @@ using nvfp4::round_up;
 
 constexpr int64_t kMaxDim = (int64_t)1 << 31;  // kernel index math is 32-bit per dimension
 
+// Leading dimensions are bounded like the other sizes, so that the extents
+// (rows - 1) * ld + cols computed below stay far inside int64.
+bool ld_ok(int64_t ld, int64_t cols) { return ld >= cols && ld < kMaxDim; }
+
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // [p, p + n) and [q, q + m) overlap (both non-empty)?
@@ -62,7 +66,7 @@ nvfp4_status nvfp4_quantize_act(const void* x_bf16, int64_t M, int64_t K, int64_
                                 uint8_t* codes, uint8_t* scales, float* g_dec_out, void* workspace,
                                 size_t workspace_bytes, void* stream) {
   if (M < 0 || K < 0) return NVFP4_EINVAL;
-  if (K % 16 != 0 || M >= kMaxDim || K >= kMaxDim || ldx < K) return NVFP4_ESHAPE;
+  if (K % 16 != 0 || M >= kMaxDim || K >= kMaxDim || !ld_ok(ldx, K)) return NVFP4_ESHAPE;
   if (!g_dec_out) return NVFP4_EINVAL;
   const bool empty = (M == 0 || K == 0);
   if (!empty && (!x_bf16 || !codes || !scales)) return NVFP4_EINVAL;
@@ -98,7 +102,7 @@ nvfp4_status nvfp4_pack_weight(const float* w, int64_t N, int64_t K, int64_t ldw
                                int32_t nseg, uint8_t* w_codes, uint8_t* w_scales, float* w_g_dec,
                                void* workspace, size_t workspace_bytes, void* stream) {
   if (N < 1 || K < 0) return NVFP4_EINVAL;
-  if (K % 16 != 0 || N >= kMaxDim || K >= kMaxDim || ldw < K) return NVFP4_ESHAPE;
+  if (K % 16 != 0 || N >= kMaxDim || K >= kMaxDim || !ld_ok(ldw, K)) return NVFP4_ESHAPE;
   if ((!w && K > 0) || !w_codes || !w_scales || !w_g_dec) return NVFP4_EINVAL;
   const nvfp4_status ss = check_segments(segs, nseg, N);
   if (ss != NVFP4_OK) return ss;
@@ -142,7 +146,7 @@ nvfp4_status nvfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const f
                         const nvfp4_segment* segs, const float* w_g_dec, int32_t nseg, float* out, int64_t ldo,
                         void* stream) {
   if (M < 0 || K < 0 || N < 1) return NVFP4_EINVAL;
-  if (K % 16 != 0 || M >= kMaxDim || K >= kMaxDim || N >= kMaxDim || ldo < N) return NVFP4_ESHAPE;
+  if (K % 16 != 0 || M >= kMaxDim || K >= kMaxDim || N >= kMaxDim || !ld_ok(ldo, N)) return NVFP4_ESHAPE;
   if (M > 16 && !mfma_operands_fit(M, K, N)) return NVFP4_ESHAPE;
   const nvfp4_status ss = check_segments(segs, nseg, N);
   if (ss != NVFP4_OK) return ss;
@@ -186,7 +190,8 @@ nvfp4_status nvfp4_linear(const void* x_bf16, int64_t M, int64_t K, int64_t ldx,
                           int32_t nseg, float* out, int64_t ldo, void* workspace, size_t workspace_bytes,
                           void* stream) {
   if (M < 0 || K < 0 || N < 1) return NVFP4_EINVAL;
-  if (K % 16 != 0 || M >= kMaxDim || K >= kMaxDim || N >= kMaxDim || ldx < K || ldo < N) return NVFP4_ESHAPE;
+  if (K % 16 != 0 || M >= kMaxDim || K >= kMaxDim || N >= kMaxDim || !ld_ok(ldx, K) || !ld_ok(ldo, N))
+    return NVFP4_ESHAPE;
   if (M > 16 && !mfma_operands_fit(M, K, N)) return NVFP4_ESHAPE;
   const nvfp4_status ss = check_segments(segs, nseg, N);
   if (ss != NVFP4_OK) return ss;
@@ -242,7 +247,8 @@ nvfp4_status nvfp4_pack_weight_gate_up(const float* w, int64_t I, int64_t K, int
                                        uint8_t* w_scales, float* w_g_dec, void* workspace, size_t workspace_bytes,
                                        void* stream) {
   if (I < 1 || K < 0) return NVFP4_EINVAL;
-  if (I % 128 != 0 || K % 16 != 0 || K < 16 || 2 * I >= kMaxDim || K >= kMaxDim || ldw < K) return NVFP4_ESHAPE;
+  if (I % 128 != 0 || K % 16 != 0 || K < 16 || 2 * I >= kMaxDim || K >= kMaxDim || !ld_ok(ldw, K))
+    return NVFP4_ESHAPE;
   if (!w || !w_codes || !w_scales || !w_g_dec) return NVFP4_EINVAL;
   if (!aligned16(w) || !aligned16(w_codes) || !aligned16(w_scales)) return NVFP4_EALIGN;
   const size_t need = nvfp4::pack_weight_workspace(2 * I, K, 2);
@@ -295,7 +301,7 @@ nvfp4_status nvfp4_gemm_swiglu_quantize(const uint8_t* a_codes, const uint8_t* a
 nvfp4_status nvfp4_swiglu(const float* gu, int64_t M, int64_t I, int64_t ldgu, void* h_bf16, int64_t ldh,
                           void* stream) {
   if (M < 0 || I < 0) return NVFP4_EINVAL;
-  if (M >= kMaxDim || I >= kMaxDim || ldgu < 2 * I || ldh < I) return NVFP4_ESHAPE;
+  if (M >= kMaxDim || I >= kMaxDim || !ld_ok(ldgu, 2 * I) || !ld_ok(ldh, I)) return NVFP4_ESHAPE;
   if (M == 0 || I == 0) return NVFP4_OK;
   if (!gu || !h_bf16) return NVFP4_EINVAL;
   const size_t gb = (size_t)((M - 1) * ldgu + 2 * I) * 4, hb = (size_t)((M - 1) * ldh + I) * 2;
@@ -314,7 +320,7 @@ size_t nvfp4_amax_observe_workspace_bytes(int64_t M, int64_t K) {
 nvfp4_status nvfp4_amax_observe(const void* x_bf16, int64_t M, int64_t K, int64_t ldx, float* running_amax,
                                 void* workspace, size_t workspace_bytes, void* stream) {
   if (M < 0 || K < 0) return NVFP4_EINVAL;
-  if (K % 16 != 0 || M >= kMaxDim || K >= kMaxDim || ldx < K) return NVFP4_ESHAPE;
+  if (K % 16 != 0 || M >= kMaxDim || K >= kMaxDim || !ld_ok(ldx, K)) return NVFP4_ESHAPE;
   if (!running_amax) return NVFP4_EINVAL;
   if (M == 0 || K == 0) return NVFP4_OK;
   if (!x_bf16) return NVFP4_EINVAL;
@@ -332,7 +338,7 @@ nvfp4_status nvfp4_amax_observe(const void* x_bf16, int64_t M, int64_t K, int64_
 nvfp4_status nvfp4_quantize_stats(const void* x_bf16, int64_t M, int64_t K, int64_t ldx, const float* amax_in,
                                   uint32_t* counts, void* stream) {
   if (M < 0 || K < 0) return NVFP4_EINVAL;
-  if (K % 16 != 0 || M >= kMaxDim || K >= kMaxDim || ldx < K) return NVFP4_ESHAPE;
+  if (K % 16 != 0 || M >= kMaxDim || K >= kMaxDim || !ld_ok(ldx, K)) return NVFP4_ESHAPE;
   if (!amax_in || !counts) return NVFP4_EINVAL;
   const bool empty = (M == 0 || K == 0);
   if (!empty && !x_bf16) return NVFP4_EINVAL;
@@ -346,6 +352,7 @@ nvfp4_status nvfp4_quantize_stats(const void* x_bf16, int64_t M, int64_t K, int6
 // ---- calibrated FP8 KV-cache codec
 nvfp4_status nvfp4_kv_fp8_encode(const void* x_bf16, int64_t n, const float* amax, uint8_t* codes, void* stream) {
   if (n < 0) return NVFP4_EINVAL;
+  if (n >= ((int64_t)1 << 48)) return NVFP4_ESHAPE;
   if (n == 0) return NVFP4_OK;
   if (!x_bf16 || !amax || !codes) return NVFP4_EINVAL;
   if (!aligned16(x_bf16) || !aligned16(codes)) return NVFP4_EALIGN;
@@ -356,6 +363,7 @@ nvfp4_status nvfp4_kv_fp8_encode(const void* x_bf16, int64_t n, const float* ama
 
 nvfp4_status nvfp4_kv_fp8_decode(const uint8_t* codes, int64_t n, const float* amax, void* out_bf16, void* stream) {
   if (n < 0) return NVFP4_EINVAL;
+  if (n >= ((int64_t)1 << 48)) return NVFP4_ESHAPE;
   if (n == 0) return NVFP4_OK;
   if (!codes || !amax || !out_bf16) return NVFP4_EINVAL;
   if (!aligned16(codes) || !aligned16(out_bf16)) return NVFP4_EALIGN;

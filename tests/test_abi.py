@@ -56,6 +56,7 @@ def q(x=A, M=4, K=32, ldx=32, amax=None, codes=A + (1 << 20), scales=A + (2 << 2
     (dict(M=-1), 1), (dict(K=24), 2), (dict(K=32, ldx=16), 2), (dict(g=None), 1), (dict(x=None), 1),
     (dict(codes=None), 1), (dict(x=A + 8), 3), (dict(scales=A + (2 << 20) + 4), 3), (dict(ldx=36), 3),
     (dict(codes=A + 16), 1),                                      # codes overlap x
+    (dict(ldx=1 << 31), 2), (dict(ldx=1 << 62), 2),               # leading dimension bound (no overflow)
     (dict(M=4096, K=4096, ldx=4096, codes=A + (64 << 20), scales=A + (80 << 20), g=A + (96 << 20)), 5),
 ])
 def test_quantize_act_validation(kw, status):
@@ -88,6 +89,7 @@ def g(a=A, sa=A + (1 << 20), ag=A + (2 << 20), M=4, K=32, wc=A + (3 << 20), ws=A
     (dict(out=A + (3 << 20) + 256), 1),                           # out overlaps the weight codes
     (dict(M=1 << 20, K=8192), 2),                                 # MFMA path: activation codes reach 4 GiB
     (dict(M=32, N=1 << 20, K=8192, sg=((0, 1 << 20),), ldo=1 << 20), 2),   # packed weight codes reach 4 GiB
+    (dict(ldo=1 << 31), 2), (dict(ldo=1 << 62), 2),
 ])
 def test_gemm_validation(kw, status):
     assert g(**kw) == status
@@ -105,7 +107,7 @@ def p(w=A, N=32, K=32, ldw=32, sg=((0, 32),), wc=A + (1 << 20), ws=A + (2 << 20)
 
 @pytest.mark.parametrize("kw,status", [
     (dict(N=0, sg=((0, 1),)), 1), (dict(K=40), 2), (dict(ldw=16), 2), (dict(sg=((0, 31),)), 4),
-    (dict(w=A + 4), 3), (dict(workb=0), 5), (dict(work=None), 5), (dict(wc=A + 64), 1),
+    (dict(w=A + 4), 3), (dict(workb=0), 5), (dict(work=None), 5), (dict(wc=A + 64), 1), (dict(ldw=1 << 31), 2),
 ])
 def test_pack_validation(kw, status):
     assert p(**kw) == status
@@ -125,6 +127,7 @@ def lin(x=A, M=4, K=32, ldx=32, amax=None, ac=A + (1 << 20), as_=A + (2 << 20), 
     (dict(M=4096, K=4096, ldx=4096, ac=A + (64 << 20), as_=A + (80 << 20), ag=A + (96 << 20), wc=A + (128 << 20),
           ws=A + (160 << 20), wg=A + (192 << 20), out=A + (256 << 20)), 5),
     (dict(M=1 << 20, K=8192, ldx=8192), 2),                      # MFMA path: activation codes reach 4 GiB
+    (dict(ldx=1 << 31), 2), (dict(ldo=1 << 62), 2),
 ])
 def test_linear_validation(kw, status):
     assert lin(**kw) == status
@@ -137,7 +140,7 @@ def gu_pack(w=A, I=128, K=32, ldw=32, wc=A + (1 << 20), ws=A + (2 << 20), wg=A +
 
 @pytest.mark.parametrize("kw,status", [
     (dict(I=0), 1), (dict(I=96), 2), (dict(K=40), 2), (dict(K=0), 2), (dict(ldw=16), 2), (dict(w=A + 4), 3),
-    (dict(workb=0), 5), (dict(wg=None), 1), (dict(wc=A + 64), 1),
+    (dict(workb=0), 5), (dict(wg=None), 1), (dict(wc=A + 64), 1), (dict(ldw=1 << 40), 2),
 ])
 def test_pack_gate_up_validation(kw, status):
     assert gu_pack(**kw) == status
@@ -159,7 +162,7 @@ def test_gemm_swiglu_quantize_validation(kw, status):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(M=-1), 1), (dict(ldgu=100), 2), (dict(ldh=10), 2), (dict(gu=None), 1), (dict(h=A + 64), 1),
-    (dict(M=0), 0),
+    (dict(M=0), 0), (dict(ldgu=1 << 31), 2), (dict(ldh=1 << 62), 2),
 ])
 def test_swiglu_validation(kw, status):
     a = dict(gu=A, M=4, I=64, ldgu=128, h=A + (1 << 20), ldh=64)
@@ -176,6 +179,7 @@ def test_kv_fp8_validation(fn):
     assert f(A, 16, None, A + (2 << 20), None) == 1
     assert f(A + 4, 16, A + (1 << 20), A + (2 << 20), None) == 3
     assert f(A, 64, A + (1 << 20), A + 16, None) == 1               # output overlaps input
+    assert f(A, 1 << 48, A + (1 << 20), A + (2 << 20), None) == 2   # size bound
 
 
 def test_observe_and_stats_validation():
@@ -187,9 +191,11 @@ def test_observe_and_stats_validation():
     assert lib.nvfp4_amax_observe(A, 4, 32, 32, A + (1 << 20), A + (2 << 20), 0, None) == 5
     assert lib.nvfp4_amax_observe(A + 8, 4, 32, 32, A + (1 << 20), A + (2 << 20), wsb, None) == 3
     assert lib.nvfp4_amax_observe(A, 0, 32, 32, A + (1 << 20), None, 0, None) == 0
+    assert lib.nvfp4_amax_observe(A, 4, 32, 1 << 31, A + (1 << 20), A + (2 << 20), wsb, None) == 2
     assert lib.nvfp4_quantize_stats(A, 4, 24, 32, A + (1 << 20), A + (2 << 20), None) == 2
     assert lib.nvfp4_quantize_stats(A, 4, 32, 32, None, A + (2 << 20), None) == 1
     assert lib.nvfp4_quantize_stats(A, 4, 32, 32, A + (1 << 20), A + 64, None) == 1   # counts overlap x
+    assert lib.nvfp4_quantize_stats(A, 4, 32, 1 << 62, A + (1 << 20), A + (2 << 20), None) == 2
 
 
 def test_binding_has_no_cpu_fallback(monkeypatch):

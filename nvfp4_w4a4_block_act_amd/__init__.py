@@ -9,8 +9,11 @@ There is no fallback: if the library is not built, importing it raises.
 
 Convenience layer (allocation only): ``quantize_act``, ``pack_weight``,
 ``gemm`` and ``PackedWeight`` allocate outputs with torch and call the C ABI.
+Their ``stream`` is a keyword-only ``torch.cuda.Stream`` (default: torch's
+current stream); the ``nvfp4_*`` wrappers take a raw hipStream_t handle.
 """
 import ctypes
+import functools
 import os
 from dataclasses import dataclass
 
@@ -219,6 +222,23 @@ def nvfp4_swiglu(gu, M, I, ldgu, h, ldh, stream=None):
 
 
 # ---- convenience layer: allocate with torch, call the C ABI --------------------------
+def _on_stream(fn):
+    """Runs a convenience function on ``stream`` (a torch.cuda.Stream, keyword-only):
+    its tensors -- outputs and temporary scratch -- are allocated while that stream
+    is current, so torch's caching allocator hands their memory to no other stream
+    while the enqueued kernels may still use it; the C ABI gets the raw handle."""
+    @functools.wraps(fn)
+    def wrapper(*args, stream=None, **kw):
+        if stream is None:
+            return fn(*args, stream=None, **kw)
+        if not isinstance(stream, torch.cuda.Stream):
+            raise TypeError(f"{fn.__name__}: stream must be a torch.cuda.Stream "
+                            "(the nvfp4_* wrappers take raw handles)")
+        with torch.cuda.stream(stream):
+            return fn(*args, stream=stream.cuda_stream, **kw)
+    return wrapper
+
+
 def _empty(n, dtype, device):
     return torch.empty(max(int(n), 1), dtype=dtype, device=device)
 
@@ -238,7 +258,8 @@ class Workspace:
         return self.buf, self.buf.numel()
 
 
-def quantize_act(x, amax=None, workspace=None, out=None, stream=None):
+@_on_stream
+def quantize_act(x, amax=None, workspace=None, out=None, *, stream=None):
     """bf16 [M, K] cuda tensor -> (codes uint8 [M, K/2], scales uint8 [M, K/16], g_dec float32 [1])."""
     assert x.dtype == torch.bfloat16 and x.dim() == 2 and (x.stride(1) == 1 or x.shape[1] <= 1)
     M, K = x.shape
@@ -269,7 +290,8 @@ class PackedWeight:
         return self.codes.numel() + self.scales.numel()
 
 
-def pack_weight(w, segments=None, stream=None):
+@_on_stream
+def pack_weight(w, segments=None, *, stream=None):
     """fp32 [N, K] cuda tensor + [(n_begin, n_end), ...] -> PackedWeight."""
     assert w.dtype == torch.float32 and w.dim() == 2 and (w.stride(1) == 1 or w.shape[1] <= 1)
     N, K = w.shape
@@ -284,14 +306,16 @@ def pack_weight(w, segments=None, stream=None):
     return PackedWeight(codes, scales, g, N, K, segments)
 
 
-def weight_to_canonical(pw, stream=None):
+@_on_stream
+def weight_to_canonical(pw, *, stream=None):
     codes = torch.empty((pw.N, pw.K // 2), dtype=torch.uint8, device=pw.codes.device)
     scales = torch.empty((pw.N, pw.K // 16), dtype=torch.uint8, device=pw.codes.device)
     nvfp4_weight_to_canonical(pw.codes, pw.scales, pw.N, pw.K, codes, scales, stream)
     return codes, scales
 
 
-def gemm(a_codes, a_scales, a_g_dec, pw, out=None, g_dec=None, stream=None):
+@_on_stream
+def gemm(a_codes, a_scales, a_g_dec, pw, out=None, g_dec=None, *, stream=None):
     """NVFP4 activations x packed weight -> fp32 [M, N] (per-segment epilogue).
 
     ``g_dec`` overrides the weight's per-segment scales (same length)."""
@@ -306,7 +330,8 @@ def gemm(a_codes, a_scales, a_g_dec, pw, out=None, g_dec=None, stream=None):
     return out
 
 
-def linear(x, pw, amax=None, workspace=None, out=None, act_out=None, stream=None):
+@_on_stream
+def linear(x, pw, amax=None, workspace=None, out=None, act_out=None, *, stream=None):
     """The whole W4A4 linear layer via nvfp4_linear: bf16 x [M, K] -> fp32 [M, N].
 
     Also returns the activation codes, scales and g_dec it produced."""
@@ -329,7 +354,8 @@ def linear(x, pw, amax=None, workspace=None, out=None, act_out=None, stream=None
     return out, (codes, scales, g)
 
 
-def pack_weight_gate_up(w, stream=None):
+@_on_stream
+def pack_weight_gate_up(w, *, stream=None):
     """fp32 [2I, K] (gate rows, then up rows) -> PackedWeight in the interleaved
     gate/up layout, with the two modules' own scales (segments (0, I), (I, 2I))."""
     assert w.dtype == torch.float32 and w.dim() == 2 and w.is_cuda and w.stride(1) == 1
@@ -345,7 +371,8 @@ def pack_weight_gate_up(w, stream=None):
     return PackedWeight(codes, scales, g, N2, K, [(0, I), (I, N2)])
 
 
-def gemm_swiglu_quantize(a_codes, a_scales, a_g_dec, pw, amax_h, out=None, stream=None):
+@_on_stream
+def gemm_swiglu_quantize(a_codes, a_scales, a_g_dec, pw, amax_h, out=None, *, stream=None):
     """NVFP4 activations x interleaved gate/up weight -> NVFP4 of bf16(silu(g) * u):
     (codes uint8 [M, I/2], scales uint8 [M, I/16], g_dec float32 [1])."""
     M = a_codes.shape[0]
@@ -361,7 +388,8 @@ def gemm_swiglu_quantize(a_codes, a_scales, a_g_dec, pw, amax_h, out=None, strea
     return out
 
 
-def swiglu(gu, stream=None):
+@_on_stream
+def swiglu(gu, *, stream=None):
     """fp32 [M, 2I] gate+up output -> bf16 [M, I] = bf16(silu(g) * u)."""
     assert gu.dtype == torch.float32 and gu.dim() == 2 and gu.stride(1) == 1
     M, N2 = gu.shape
@@ -370,7 +398,8 @@ def swiglu(gu, stream=None):
     return h
 
 
-def kv_fp8_encode(x, amax, out=None, stream=None):
+@_on_stream
+def kv_fp8_encode(x, amax, out=None, *, stream=None):
     """Contiguous bf16 cuda tensor + device amax [1] -> uint8 E4M3FN codes of the same shape."""
     assert x.dtype == torch.bfloat16 and x.is_contiguous()
     codes = torch.empty(x.shape, dtype=torch.uint8, device=x.device) if out is None else out
@@ -378,7 +407,8 @@ def kv_fp8_encode(x, amax, out=None, stream=None):
     return codes
 
 
-def kv_fp8_decode(codes, amax, out=None, stream=None):
+@_on_stream
+def kv_fp8_decode(codes, amax, out=None, *, stream=None):
     """uint8 E4M3FN codes + device amax [1] -> bf16 tensor of the same shape."""
     assert codes.dtype == torch.uint8 and codes.is_contiguous()
     y = torch.empty(codes.shape, dtype=torch.bfloat16, device=codes.device) if out is None else out
@@ -393,14 +423,16 @@ class AmaxObserver:
         self.amax = torch.zeros(1, dtype=torch.float32, device=device)
         self.ws = torch.empty(max(nvfp4_amax_observe_workspace_bytes(0, 0), 16), dtype=torch.uint8, device=device)
 
-    def observe(self, x, stream=None):
+    @_on_stream
+    def observe(self, x, *, stream=None):
         assert x.dtype == torch.bfloat16 and x.dim() == 2 and (x.stride(1) == 1 or x.shape[1] <= 1)
         M, K = x.shape
         nvfp4_amax_observe(x, M, K, max(x.stride(0), K), self.amax, self.ws, self.ws.numel(), stream)
         return self.amax
 
 
-def quantize_stats(x, amax, stream=None):
+@_on_stream
+def quantize_stats(x, amax, *, stream=None):
     """(saturated-scale blocks, clipped elements) of bf16 x under the static maximum amax [1]."""
     M, K = x.shape
     counts = torch.empty(2, dtype=torch.int32, device=x.device)

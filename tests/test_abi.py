@@ -204,3 +204,12 @@ def test_binding_has_no_cpu_fallback(monkeypatch):
     monkeypatch.setattr(nv, "LIB_PATH", "/nonexistent/libnvfp4_w4a4.so")
     with pytest.raises(ImportError):
         nv.lib()
+
+
+def test_convenience_layer_stream_must_be_a_torch_stream():
+    """The allocating helpers take a torch.cuda.Stream (their tensors are allocated
+    on it); a raw handle is refused before anything is touched."""
+    for fn, args in [(nv.linear, (None, None)), (nv.quantize_act, (None,)), (nv.gemm, (None, None, None, None)),
+                     (nv.pack_weight, (None,))]:
+        with pytest.raises(TypeError):
+            fn(*args, stream=12345)

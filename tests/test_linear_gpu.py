@@ -118,3 +118,22 @@ def test_linear_strided_input_and_output(M):
     assert torch.equal(c, c2) and torch.equal(s, s2) and torch.equal(g, g2)
     assert torch.equal(big[:, 8:8 + N], ref)
     assert torch.all(big[:, :8] == 7.0) and torch.all(big[:, 8 + N:] == 7.0)
+
+
+def test_convenience_layer_on_a_side_stream():
+    """quantize_act, gemm and linear enqueued on a side torch stream (their outputs
+    and scratch allocated on it) give the default stream's results."""
+    d = W.tiny()
+    pw = gpu_pack(d.w, d.segments)
+    x = to_dev_bf16(d.x_bits)
+    ref, (c0, s0, g0) = nv.linear(x, pw)
+    ref_g = nv.gemm(c0, s0, g0, pw)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    out, _ = nv.linear(x, pw, stream=side)
+    c1, s1, g1 = nv.quantize_act(x, stream=side)
+    out_g = nv.gemm(c1, s1, g1, pw, stream=side)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref) and torch.equal(out_g, ref_g)
+    assert torch.equal(c1, c0) and torch.equal(s1, s0) and torch.equal(g1, g0)

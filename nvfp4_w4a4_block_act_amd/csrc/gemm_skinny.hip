@@ -8,11 +8,12 @@
 //
 // Design (gfx950):
 //  * each weight byte is read from HBM exactly once: 0.5625 B per weight
-//    (codes + scales); a workgroup of eight waves owns S = 3 strips of 16
-//    output columns (256 workgroups for N = 12288, one per CU), and its waves
-//    split the K tiles of those strips (split-K inside the workgroup, reduced
-//    through LDS); each wave keeps two batches (one k tile of the S strips
-//    each) in flight, requesting batch u + 2 after the MFMAs of batch u;
+//    (codes + scales); a workgroup of eight waves owns S strips of 16 output
+//    columns (S = 1..3 chosen per N by pick_strips: 3 for N = 12288, i.e. 256
+//    workgroups, one per CU), and its waves split the K tiles of those strips
+//    (split-K inside the workgroup, reduced through LDS); each wave keeps two
+//    batches (one k tile of the S strips each) in flight, requesting batch
+//    u + 2 after the MFMAs of batch u;
 //  * the 16 x 16 x 32 fp16 MFMA does the arithmetic with M padded to 16:
 //    lane l holds row/column l % 16 and the 32 k of group g = l / 16 of a
 //    128-k tile.  A K-permutation shared by both operands makes each lane's
@@ -446,20 +447,56 @@ hipError_t launch_fill_zero(float* out, int M, int N, int64_t ldo, hipStream_t s
   return hipGetLastError();
 }
 
-constexpr int kSkS = 3, kSkNW = 8, kSkU = 5;
+constexpr int kSkNW = 8, kSkU = 5;
+constexpr int kCUs = 256;   // compute units of a gfx950 (MI355X) device
+
+// Strips per workgroup (1..3): the fewest strips on the busiest CU -- a launch
+// of more than 256 workgroups puts a second one on some CUs -- with ties going
+// to more strips per workgroup (fewer, longer weight streams).  Measured at
+// K = 5120 (us per launch, M = 1, skinny GEMM; S = 1 / 2 / 3): N = 2048
+// 3.9 / 4.7 / 5.7, N = 5120 5.7 / 5.0 / 5.8, N = 8192 6.0 / 5.7 / 6.3,
+// N = 12288 8.5 / 9.0 / 7.8; the one-launch layer follows the same pattern.
+static int pick_strips(int nstrips) {
+  int best = 3, cost = 0;
+  for (int s = 3; s >= 1; --s) {
+    const int wgs = (nstrips + s - 1) / s;
+    const int c = (wgs + kCUs - 1) / kCUs * s;
+    if (s == 3 || c < cost) {
+      best = s;
+      cost = c;
+    }
+  }
+  return best;
+}
+
+template <int S>
+static void launch_skinny(int nstrips, hipStream_t stream, const uint8_t* a_codes, const uint8_t* a_scales,
+                          const float* a_g, int M, int K, const uint8_t* w_codes, const uint8_t* w_scales, int N,
+                          const SegTable& st, const float* w_g, float* out, int64_t ldo) {
+  const int grid = (nstrips + S - 1) / S;
+  if (K % 32 == 0)
+    gemm_skinny_kernel<S, kSkNW, kSkU, true><<<grid, 64 * kSkNW, 0, stream>>>(
+        a_codes, a_scales, a_g, M, K, w_codes, w_scales, N, st, w_g, out, ldo);
+  else
+    gemm_skinny_kernel<S, kSkNW, kSkU, false><<<grid, 64 * kSkNW, 0, stream>>>(
+        a_codes, a_scales, a_g, M, K, w_codes, w_scales, N, st, w_g, out, ldo);
+}
 
 hipError_t launch_gemm_skinny(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_g, int M,
                               int K, const uint8_t* w_codes, const uint8_t* w_scales, int N,
                               const SegTable& st, const float* w_g, float* out, int64_t ldo,
                               hipStream_t stream) {
   const int nstrips = (N + kStrip - 1) / kStrip;
-  const int grid = (nstrips + kSkS - 1) / kSkS;
-  if (K % 32 == 0)
-    gemm_skinny_kernel<kSkS, kSkNW, kSkU, true><<<grid, 64 * kSkNW, 0, stream>>>(
-        a_codes, a_scales, a_g, M, K, w_codes, w_scales, N, st, w_g, out, ldo);
-  else
-    gemm_skinny_kernel<kSkS, kSkNW, kSkU, false><<<grid, 64 * kSkNW, 0, stream>>>(
-        a_codes, a_scales, a_g, M, K, w_codes, w_scales, N, st, w_g, out, ldo);
+  switch (pick_strips(nstrips)) {
+    case 1:
+      launch_skinny<1>(nstrips, stream, a_codes, a_scales, a_g, M, K, w_codes, w_scales, N, st, w_g, out, ldo);
+      break;
+    case 2:
+      launch_skinny<2>(nstrips, stream, a_codes, a_scales, a_g, M, K, w_codes, w_scales, N, st, w_g, out, ldo);
+      break;
+    default:
+      launch_skinny<3>(nstrips, stream, a_codes, a_scales, a_g, M, K, w_codes, w_scales, N, st, w_g, out, ldo);
+  }
   return hipGetLastError();
 }
 
@@ -471,13 +508,33 @@ bool linear_decode_fits(int64_t M, int64_t K) {
 // measured about 0.4 us per launch faster for the 1-row instantiation at
 // K = 5120, N = 12288, slower for 2 to 6 rows and no better for 8 or 16 (or in
 // the skinny GEMM).
-template <int MAXM>
-static void launch_decode(int grid, hipStream_t stream, const uint16_t* x, int64_t ldx, const float* amax_in,
+template <int S, int MAXM>
+static void launch_decode(int nstrips, hipStream_t stream, const uint16_t* x, int64_t ldx, const float* amax_in,
                           uint8_t* a_codes, uint8_t* a_scales, float* a_g, int M, int K, const uint8_t* w_codes,
                           const uint8_t* w_scales, int N, const SegTable& st, const float* w_g, float* out,
                           int64_t ldo) {
-  linear_decode_kernel<kSkS, kSkNW, kSkU, MAXM, MAXM == 1><<<grid, 64 * kSkNW, 0, stream>>>(
+  const int grid = (nstrips + S - 1) / S;
+  linear_decode_kernel<S, kSkNW, kSkU, MAXM, MAXM == 1><<<grid, 64 * kSkNW, 0, stream>>>(
       x, ldx, amax_in, a_codes, a_scales, a_g, M, K, w_codes, w_scales, N, st, w_g, out, ldo);
+}
+
+template <int S>
+static void launch_decode_rows(int nstrips, hipStream_t stream, const uint16_t* x, int64_t ldx,
+                               const float* amax_in, uint8_t* a_codes, uint8_t* a_scales, float* a_g, int M, int K,
+                               const uint8_t* w_codes, const uint8_t* w_scales, int N, const SegTable& st,
+                               const float* w_g, float* out, int64_t ldo) {
+  if (M == 1)
+    launch_decode<S, 1>(nstrips, stream, x, ldx, amax_in, a_codes, a_scales, a_g, M, K, w_codes, w_scales, N, st,
+                        w_g, out, ldo);
+  else if (M <= 4)
+    launch_decode<S, 4>(nstrips, stream, x, ldx, amax_in, a_codes, a_scales, a_g, M, K, w_codes, w_scales, N, st,
+                        w_g, out, ldo);
+  else if (M <= 8)
+    launch_decode<S, 8>(nstrips, stream, x, ldx, amax_in, a_codes, a_scales, a_g, M, K, w_codes, w_scales, N, st,
+                        w_g, out, ldo);
+  else
+    launch_decode<S, kDecMaxM>(nstrips, stream, x, ldx, amax_in, a_codes, a_scales, a_g, M, K, w_codes, w_scales, N,
+                               st, w_g, out, ldo);
 }
 
 hipError_t launch_linear_decode(const uint16_t* x, int64_t ldx, const float* amax_in, uint8_t* a_codes,
@@ -485,19 +542,19 @@ hipError_t launch_linear_decode(const uint16_t* x, int64_t ldx, const float* ama
                                 const uint8_t* w_scales, int N, const SegTable& st, const float* w_g, float* out,
                                 int64_t ldo, hipStream_t stream) {
   const int nstrips = (N + kStrip - 1) / kStrip;
-  const int grid = (nstrips + kSkS - 1) / kSkS;
-  if (M == 1)
-    launch_decode<1>(grid, stream, x, ldx, amax_in, a_codes, a_scales, a_g, M, K, w_codes, w_scales, N, st, w_g, out,
-                     ldo);
-  else if (M <= 4)
-    launch_decode<4>(grid, stream, x, ldx, amax_in, a_codes, a_scales, a_g, M, K, w_codes, w_scales, N, st, w_g, out,
-                     ldo);
-  else if (M <= 8)
-    launch_decode<8>(grid, stream, x, ldx, amax_in, a_codes, a_scales, a_g, M, K, w_codes, w_scales, N, st, w_g, out,
-                     ldo);
-  else
-    launch_decode<kDecMaxM>(grid, stream, x, ldx, amax_in, a_codes, a_scales, a_g, M, K, w_codes, w_scales, N, st,
+  switch (pick_strips(nstrips)) {
+    case 1:
+      launch_decode_rows<1>(nstrips, stream, x, ldx, amax_in, a_codes, a_scales, a_g, M, K, w_codes, w_scales, N, st,
                             w_g, out, ldo);
+      break;
+    case 2:
+      launch_decode_rows<2>(nstrips, stream, x, ldx, amax_in, a_codes, a_scales, a_g, M, K, w_codes, w_scales, N, st,
+                            w_g, out, ldo);
+      break;
+    default:
+      launch_decode_rows<3>(nstrips, stream, x, ldx, amax_in, a_codes, a_scales, a_g, M, K, w_codes, w_scales, N, st,
+                            w_g, out, ldo);
+  }
   return hipGetLastError();
 }
 

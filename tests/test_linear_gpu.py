@@ -137,3 +137,28 @@ def test_convenience_layer_on_a_side_stream():
     torch.cuda.synchronize()
     assert torch.equal(out, ref) and torch.equal(out_g, ref_g)
     assert torch.equal(c1, c0) and torch.equal(s1, s0) and torch.equal(g1, g0)
+
+
+@pytest.mark.parametrize("N", [2000, 5000, 8232])
+@pytest.mark.parametrize("M", [1, 7, 16])
+def test_linear_strips_per_workgroup(M, N):
+    """Output widths for which the launchers pick 1, 2 and 3 strips of 16 columns
+    per workgroup (125, 313 and 515 strips), with ragged segments and a ragged k
+    tile: one launch bit-identical to quantize + GEMM, sampled columns within the
+    oracle's tolerance."""
+    rng = np.random.default_rng(700 + M + N)
+    K = 1040
+    segs = [(0, 700), (700, N - 9), (N - 9, N)]
+    w = np.concatenate([(0.02 * (1 + i) * rng.standard_normal((e - b, K))).astype(np.float32)
+                        for i, (b, e) in enumerate(segs)])
+    x_bits = W.random_act(800 + M, M, K, "student_t")
+    say(f"[strips] M={M} N={N}")
+    pw = gpu_pack(w, segs)
+    x = to_dev_bf16(x_bits)
+    out, (c, s, g) = nv.linear(x, pw)
+    ref_gpu = nv.gemm(*nv.quantize_act(x), pw)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref_gpu)
+    cols = np.sort(np.unique(np.concatenate([rng.choice(N, 200, replace=False), [0, 699, 700, N - 10, N - 9, N - 1]])))
+    ref, bnd = oracle_linear_rows(x_bits, w, segs, cols=cols)
+    assert_within_tol(out.cpu().numpy().astype(np.float64)[:, cols], ref, bnd, f"strips M={M} N={N}")

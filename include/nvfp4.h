@@ -161,9 +161,10 @@ nvfp4_status nvfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const f
  * caller's buffers as well, in the canonical layout.  Results are bit-identical
  * to calling nvfp4_quantize_act then nvfp4_gemm.
  *
- * Decode-sized inputs (1 <= M <= 16, K <= 5120) run as ONE launch: every GEMM
- * workgroup encodes the (small) activation tensor itself while its weight loads
- * are in flight, so no workspace and no hand-over between workgroups is needed.
+ * Decode-sized inputs (1 <= M <= 16 with K <= 5120, M <= 8 with K <= 10240,
+ * M <= 4 with K <= 20480) run as ONE launch: every GEMM workgroup encodes the
+ * (small) activation tensor itself while its weight loads are in flight, so no
+ * workspace and no hand-over between workgroups is needed.
  * Other inputs run the quantizer and the GEMM kernels back to back on the
  * stream (the GEMM's 4 GiB operand limit for M > 16 applies).
  *

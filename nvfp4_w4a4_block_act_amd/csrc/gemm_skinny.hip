@@ -281,8 +281,18 @@ __global__ __launch_bounds__(64 * NW) void gemm_skinny_kernel(
 // priority after each batch of step 5 (set_issue_priority).  The results are
 // bit-identical to the activation quantizer followed by the skinny GEMM.
 constexpr int kDecMaxM = 16;
-constexpr int kDecMaxK = 5120;
 constexpr int kDecRowBytes = kTileK / 2 + 16;   // LDS bytes per row of one tile (padded)
+
+// k tiles per wave (U) of the one-launch layer for an M x K input, 0 when it
+// has no instance: the wave-private activation area (MAXM * U tiles of
+// kDecRowBytes) must fit LDS and the lane's block registers (MAXM * U / 8
+// steps of two 16-byte chunks) the register file, so longer K takes fewer rows.
+static int decode_tiles_per_wave(int64_t M, int64_t K) {
+  if (K <= 8 * 5 * kTileK) return 5;               // K <= 5120: every row bound
+  if (K <= 8 * 10 * kTileK && M <= 8) return 10;   // K <= 10240
+  if (K <= 8 * 20 * kTileK && M <= 4) return 20;   // K <= 20480
+  return 0;
+}
 
 template <int S, int NW, int U, int MAXM, bool BAL>
 __global__ __launch_bounds__(64 * NW) void linear_decode_kernel(
@@ -292,7 +302,7 @@ __global__ __launch_bounds__(64 * NW) void linear_decode_kernel(
     float* __restrict__ out, int64_t ldo) {
   constexpr int kSlots = MAXM * U * (kTileK / kBlock);   // block slots of one wave
   constexpr int kQ = (kSlots + 63) / 64;
-  static_assert(NW * U * kTileK >= kDecMaxK, "one batch set covers K");
+  static_assert(U >= 2, "two weight batches in flight");
   __shared__ float red[NW][S][4][64];
   // wave-private activation tiles, row-major over (row, tile): slot group
   // v = row * U + u holds the 8 blocks of row `row` in the wave's tile u
@@ -501,40 +511,64 @@ hipError_t launch_gemm_skinny(const uint8_t* a_codes, const uint8_t* a_scales, c
 }
 
 bool linear_decode_fits(int64_t M, int64_t K) {
-  return M >= 1 && M <= kDecMaxM && K >= kBlock && K <= kDecMaxK;
+  return M >= 1 && M <= kDecMaxM && K >= kBlock && decode_tiles_per_wave(M, K) > 0;
 }
 
 // One instantiation per row bound.  The issue-priority balancing of the waves
 // measured about 0.4 us per launch faster for the 1-row instantiation at
 // K = 5120, N = 12288, slower for 2 to 6 rows and no better for 8 or 16 (or in
 // the skinny GEMM).
-template <int S, int MAXM>
-static void launch_decode(int nstrips, hipStream_t stream, const uint16_t* x, int64_t ldx, const float* amax_in,
+template <int S, int U, int MAXM>
+static bool launch_decode(int nstrips, hipStream_t stream, const uint16_t* x, int64_t ldx, const float* amax_in,
                           uint8_t* a_codes, uint8_t* a_scales, float* a_g, int M, int K, const uint8_t* w_codes,
                           const uint8_t* w_scales, int N, const SegTable& st, const float* w_g, float* out,
                           int64_t ldo) {
   const int grid = (nstrips + S - 1) / S;
-  linear_decode_kernel<S, kSkNW, kSkU, MAXM, MAXM == 1><<<grid, 64 * kSkNW, 0, stream>>>(
+  linear_decode_kernel<S, kSkNW, U, MAXM, MAXM == 1><<<grid, 64 * kSkNW, 0, stream>>>(
       x, ldx, amax_in, a_codes, a_scales, a_g, M, K, w_codes, w_scales, N, st, w_g, out, ldo);
+  return true;
 }
 
-template <int S>
-static void launch_decode_rows(int nstrips, hipStream_t stream, const uint16_t* x, int64_t ldx,
+// The row-bound instance for M (rows 1, 4, 8, 16; U = 10 stops at 8 rows and
+// U = 20 at 4, as decode_tiles_per_wave allows).  False: no instance.
+template <int S, int U>
+static bool launch_decode_rows(int nstrips, hipStream_t stream, const uint16_t* x, int64_t ldx,
                                const float* amax_in, uint8_t* a_codes, uint8_t* a_scales, float* a_g, int M, int K,
                                const uint8_t* w_codes, const uint8_t* w_scales, int N, const SegTable& st,
                                const float* w_g, float* out, int64_t ldo) {
-  if (M == 1)
-    launch_decode<S, 1>(nstrips, stream, x, ldx, amax_in, a_codes, a_scales, a_g, M, K, w_codes, w_scales, N, st,
-                        w_g, out, ldo);
-  else if (M <= 4)
-    launch_decode<S, 4>(nstrips, stream, x, ldx, amax_in, a_codes, a_scales, a_g, M, K, w_codes, w_scales, N, st,
-                        w_g, out, ldo);
-  else if (M <= 8)
-    launch_decode<S, 8>(nstrips, stream, x, ldx, amax_in, a_codes, a_scales, a_g, M, K, w_codes, w_scales, N, st,
-                        w_g, out, ldo);
-  else
-    launch_decode<S, kDecMaxM>(nstrips, stream, x, ldx, amax_in, a_codes, a_scales, a_g, M, K, w_codes, w_scales, N,
-                               st, w_g, out, ldo);
+#define NVFP4_DECODE(MAXM)                                                                                       \
+  launch_decode<S, U, MAXM>(nstrips, stream, x, ldx, amax_in, a_codes, a_scales, a_g, M, K, w_codes, w_scales, N, \
+                            st, w_g, out, ldo)
+  if (M == 1) return NVFP4_DECODE(1);
+  if (M <= 4) return NVFP4_DECODE(4);
+  if constexpr (U <= 10) {
+    if (M <= 8) return NVFP4_DECODE(8);
+    if constexpr (U == 5) {
+      if (M <= kDecMaxM) return NVFP4_DECODE(kDecMaxM);
+    }
+  }
+#undef NVFP4_DECODE
+  return false;
+}
+
+template <int S>
+static bool launch_decode_tiles(int nstrips, hipStream_t stream, const uint16_t* x, int64_t ldx,
+                                const float* amax_in, uint8_t* a_codes, uint8_t* a_scales, float* a_g, int M, int K,
+                                const uint8_t* w_codes, const uint8_t* w_scales, int N, const SegTable& st,
+                                const float* w_g, float* out, int64_t ldo) {
+  switch (decode_tiles_per_wave(M, K)) {
+    case 5:
+      return launch_decode_rows<S, 5>(nstrips, stream, x, ldx, amax_in, a_codes, a_scales, a_g, M, K, w_codes,
+                                      w_scales, N, st, w_g, out, ldo);
+    case 10:
+      return launch_decode_rows<S, 10>(nstrips, stream, x, ldx, amax_in, a_codes, a_scales, a_g, M, K, w_codes,
+                                       w_scales, N, st, w_g, out, ldo);
+    case 20:
+      return launch_decode_rows<S, 20>(nstrips, stream, x, ldx, amax_in, a_codes, a_scales, a_g, M, K, w_codes,
+                                       w_scales, N, st, w_g, out, ldo);
+    default:
+      return false;
+  }
 }
 
 hipError_t launch_linear_decode(const uint16_t* x, int64_t ldx, const float* amax_in, uint8_t* a_codes,
@@ -542,20 +576,21 @@ hipError_t launch_linear_decode(const uint16_t* x, int64_t ldx, const float* ama
                                 const uint8_t* w_scales, int N, const SegTable& st, const float* w_g, float* out,
                                 int64_t ldo, hipStream_t stream) {
   const int nstrips = (N + kStrip - 1) / kStrip;
+  bool ok;
   switch (pick_strips(nstrips)) {
     case 1:
-      launch_decode_rows<1>(nstrips, stream, x, ldx, amax_in, a_codes, a_scales, a_g, M, K, w_codes, w_scales, N, st,
-                            w_g, out, ldo);
+      ok = launch_decode_tiles<1>(nstrips, stream, x, ldx, amax_in, a_codes, a_scales, a_g, M, K, w_codes, w_scales, N,
+                                  st, w_g, out, ldo);
       break;
     case 2:
-      launch_decode_rows<2>(nstrips, stream, x, ldx, amax_in, a_codes, a_scales, a_g, M, K, w_codes, w_scales, N, st,
-                            w_g, out, ldo);
+      ok = launch_decode_tiles<2>(nstrips, stream, x, ldx, amax_in, a_codes, a_scales, a_g, M, K, w_codes, w_scales, N,
+                                  st, w_g, out, ldo);
       break;
     default:
-      launch_decode_rows<3>(nstrips, stream, x, ldx, amax_in, a_codes, a_scales, a_g, M, K, w_codes, w_scales, N, st,
-                            w_g, out, ldo);
+      ok = launch_decode_tiles<3>(nstrips, stream, x, ldx, amax_in, a_codes, a_scales, a_g, M, K, w_codes, w_scales, N,
+                                  st, w_g, out, ldo);
   }
-  return hipGetLastError();
+  return ok ? hipGetLastError() : hipErrorInvalidValue;
 }
 
 }  // namespace nvfp4

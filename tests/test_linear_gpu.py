@@ -162,3 +162,30 @@ def test_linear_strips_per_workgroup(M, N):
     cols = np.sort(np.unique(np.concatenate([rng.choice(N, 200, replace=False), [0, 699, 700, N - 10, N - 9, N - 1]])))
     ref, bnd = oracle_linear_rows(x_bits, w, segs, cols=cols)
     assert_within_tol(out.cpu().numpy().astype(np.float64)[:, cols], ref, bnd, f"strips M={M} N={N}")
+
+
+@pytest.mark.parametrize("M,K", [(1, 17408), (4, 20480), (3, 10256), (8, 10240), (6, 5136), (2, 8208),
+                                 (9, 6144), (5, 17408)])
+def test_linear_long_k(M, K):
+    """K beyond 5120: one launch while the wave-local activation tiles fit (up to
+    10240 for 8 rows, 20480 for 4), two launches otherwise ((9, 6144), (5, 17408));
+    either way bit-identical to quantize + GEMM and within the oracle's tolerance
+    on sampled columns."""
+    rng = np.random.default_rng(900 + M + K)
+    N = 700
+    segs = [(0, 300), (300, N)]
+    w = np.concatenate([(0.02 * (1 + i) * rng.standard_normal((e - b, K))).astype(np.float32)
+                        for i, (b, e) in enumerate(segs)])
+    x_bits = W.random_act(1000 + M, M, K, "student_t")
+    say(f"[long K] M={M} K={K}")
+    pw = gpu_pack(w, segs)
+    x = to_dev_bf16(x_bits)
+    out, (c, s, g) = nv.linear(x, pw)
+    c2, s2, g2 = nv.quantize_act(x)
+    ref_gpu = nv.gemm(c2, s2, g2, pw)
+    torch.cuda.synchronize()
+    assert torch.equal(c, c2) and torch.equal(s, s2) and torch.equal(g, g2)
+    assert torch.equal(out, ref_gpu)
+    cols = np.sort(np.unique(np.concatenate([rng.choice(N, 120, replace=False), [0, 299, 300, N - 1]])))
+    ref, bnd = oracle_linear_rows(x_bits, w, segs, cols=cols)
+    assert_within_tol(out.cpu().numpy().astype(np.float64)[:, cols], ref, bnd, f"long K M={M} K={K}")

@@ -210,7 +210,6 @@ __device__ __forceinline__ void mfma_half(const uint4* sa, const uint4* sw, cons
 // Epilogues of the MFMA GEMM.
 enum MfmaEpilogue : int {
   kEpiStore = 0,     // out[m][n] = acc * fl(a_g * w_g[seg(n)])
-  kEpiSplitK = 1,    // same value, added into `out` with fp32 atomics (K split across launches' y)
   kEpiSwiglu = 2,    // gate/up weights interleaved; emit NVFP4(bf16(silu(g) * u)) instead of fp32
 };
 
@@ -235,9 +234,7 @@ __device__ __forceinline__ float swiglu_f32(float g, float u) { return g / (1.0f
 constexpr int kHRow = 128 + 8;   // bf16 per LDS row of the SwiGLU tile (16-byte pad)
 
 // One launch covers output columns [n_lo, n_hi) (n_lo a multiple of 256).  With
-// kEpiSplitK, blockIdx.y selects one of gridDim.y contiguous slices of the k
-// tiles and the workgroup adds its scaled partial sums into `out` (zeroed
-// beforehand) with fp32 atomics.  With kEpiSwiglu the weight is the interleaved
+// kEpiSwiglu the weight is the interleaved
 // gate/up packing (columns 256 t .. 256 t + 127 are gate rows 128 t .., the next
 // 128 the matching up rows), and the workgroup writes the NVFP4 encoding of
 // h[m][j] = bf16(silu(g) * u) for its 128 j instead of fp32 output.
@@ -246,7 +243,6 @@ __global__ __launch_bounds__(kMfThreads, 1) void gemm_mfma_kernel(
     const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales, const float* __restrict__ a_g,
     int M, int K, const uint8_t* __restrict__ w_codes, const uint8_t* __restrict__ w_scales, int N, int n_lo,
     int n_hi, SegTable st, const float* __restrict__ w_g, float* __restrict__ out, int64_t ldo, SwigluOut so) {
-  constexpr bool SPLIT = EPI == kEpiSplitK;
   constexpr bool SW = EPI == kEpiSwiglu;
   __shared__ uint4 sW[2][kBN * kHalfRow];              // decoded weight half-tiles, 2 x 36 KB
   __shared__ uint4 sA[2][kBM * 4];                     // activation codes, 2 x 16 KB
@@ -256,9 +252,7 @@ __global__ __launch_bounds__(kMfThreads, 1) void gemm_mfma_kernel(
   const int wm = wave >> 1, wn = wave & 1;
   const int tiles = (K + kTileK - 1) / kTileK, full = K / kTileK;
   const int nstrips = (N + kStrip - 1) / kStrip;
-  // this workgroup's k tiles [tb, te)
-  const int tb = SPLIT ? (int)((int64_t)blockIdx.y * tiles / gridDim.y) : 0;
-  const int te = SPLIT ? (int)((int64_t)(blockIdx.y + 1) * tiles / gridDim.y) : tiles;
+  const int tb = 0, te = tiles;                        // the workgroup's k tiles
 
   // ---- workgroup -> output tile: XCD-major numbering, then grouped row panels
   const int num_m = (M + kBM - 1) / kBM, num_n = (n_hi - n_lo + kBN - 1) / kBN;
@@ -420,10 +414,7 @@ __global__ __launch_bounds__(kMfThreads, 1) void gemm_mfma_kernel(
       for (int r = 0; r < 16; ++r) {
         const int m = m0 + wm * 64 + rt * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
         if (m < M) {
-          if constexpr (SPLIT)
-            unsafeAtomicAdd(out + (int64_t)m * ldo + n, acc[rt][c][r] * alpha);
-          else
-            out[(int64_t)m * ldo + n] = acc[rt][c][r] * alpha;
+          out[(int64_t)m * ldo + n] = acc[rt][c][r] * alpha;
         }
       }
   }
@@ -460,16 +451,16 @@ hipError_t launch_gemm_mfma(const uint8_t* a_codes, const uint8_t* a_scales, con
   const int n_full = N / kBN * kBN;                    // columns covered by whole tiles
   const int tiles = (K + kTileK - 1) / kTileK;
   // A ragged last tile column costs a whole extra round of workgroups when the
-  // whole tiles fill their last round (e.g. 16 x 48 = 768 = 3 x 256): then the
-  // whole tiles run alone and the ragged column runs split along K, each part
-  // adding into the zeroed output with atomics.
-  // The split aims at about 128 workgroups: on the GDN in-projection (16 row
-  // panels, 40 k tiles) 8 parts measured 23.3 us against 25.0 us for 16 parts
-  // (twice the fp32 atomics) and 34.7 us for 20.
-  int ksplit = 1;
-  if (n_full > 0 && n_full < N && rounds((int64_t)num_m * (n_full / kBN)) < rounds((int64_t)num_m * (N / kBN + 1)))
-    ksplit = std::max(1, std::min(tiles, 128 / num_m));
-  const int n_main = (ksplit > 1) ? n_full : N;
+  // whole tiles fill their last round (e.g. 16 x 48 = 768 = 3 x 256).  Then the
+  // whole tiles run alone and the ragged strips -- a tall, narrow product with
+  // a weight slice of a few hundred KB -- run as the skinny GEMM over 16-row
+  // blocks, with the segment table shifted to them.  On the GDN in-projection
+  // (4096 x 64 ragged columns, K = 5120) that takes 11 us, where a K-split of
+  // the 256 x 256 tile with fp32 atomics into a zeroed output took 29 us; the
+  // result is deterministic.
+  const bool ragged = n_full > 0 && n_full < N &&
+                      rounds((int64_t)num_m * (n_full / kBN)) < rounds((int64_t)num_m * (N / kBN + 1));
+  const int n_main = ragged ? n_full : N;
   const int grid = num_m * ((n_main + kBN - 1) / kBN);
 #define NVFP4_MFMA_LAUNCH(A16, A4, T, EPI, GRID, NLO, NHI)                                                      \
   gemm_mfma_kernel<A16, A4, T, EPI><<<GRID, kMfThreads, 0, stream>>>(a_codes, a_scales, a_g, M, K, w_codes,     \
@@ -481,11 +472,18 @@ hipError_t launch_gemm_mfma(const uint8_t* a_codes, const uint8_t* a_scales, con
   else if (K % 32 == 0) NVFP4_MFMA_LAUNCH(true, false, true, EPI, GRID, NLO, NHI);                              \
   else NVFP4_MFMA_LAUNCH(false, false, true, EPI, GRID, NLO, NHI)
   NVFP4_MFMA_DISPATCH(kEpiStore, grid, 0, n_main);
-  if (ksplit > 1) {
-    const hipError_t e = launch_fill_zero(out + n_full, M, N - n_full, ldo, stream);
+  if (ragged) {
+    const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const dim3 g2(num_m, ksplit);
-    NVFP4_MFMA_DISPATCH(kEpiSplitK, g2, n_full, N);
+    SegTable sr{};
+    int first = 0;                                     // first module with columns at or past n_full
+    while (st.end[first] <= n_full) ++first;
+    sr.nseg = st.nseg - first;
+    for (int i = 0; i < sr.nseg; ++i) sr.end[i] = st.end[first + i] - n_full;
+    const int64_t strip = n_full / kStrip;
+    return launch_gemm_skinny(a_codes, a_scales, a_g, M, K, w_codes + strip * tiles * kChunkCodes,
+                              w_scales + strip * tiles * kChunkScales, N - n_full, sr, w_g + first, out + n_full,
+                              ldo, stream);
   }
 #undef NVFP4_MFMA_DISPATCH
 #undef NVFP4_MFMA_LAUNCH

@@ -26,6 +26,7 @@
 //  * for decode-sized activations a second kernel also quantizes them inside
 //    the same launch (linear_decode_kernel below).
 #include <algorithm>
+#include <cstdint>
 
 #include "common.hpp"
 #include "quant_device.hpp"
@@ -168,7 +169,10 @@ __device__ __forceinline__ void strip_pointers(const uint8_t* w_codes, const uin
 // data early, the last wave gets all of it at the end of the stream and then
 // has its whole decode and MFMA work left (about 1 us of tail).  Batches have no
 // branches (tiles past the end are clamped and their activation scales zeroed),
-// so the waits before each batch's MFMAs stay progressive.
+// so the waits before each batch's MFMAs stay progressive.  Inputs with more
+// than 16 rows run as 16-row blocks: workgroup b takes strip group
+// b % groups of row block b / groups (the ragged last tile column of the MFMA
+// GEMM runs this way).
 template <int S, int NW, int U, bool AL16>
 __global__ __launch_bounds__(64 * NW) void gemm_skinny_kernel(
     const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales, const float* __restrict__ a_g,
@@ -185,7 +189,13 @@ __global__ __launch_bounds__(64 * NW) void gemm_skinny_kernel(
   const int tiles = (K + kTileK - 1) / kTileK;       // tiles of the packed weight
   const int full = K / kTileK;                       // tiles with no k tail
   const int nstrips = (N + kStrip - 1) / kStrip;
-  const int strip0 = blockIdx.x * S;
+  const int groups = (nstrips + S - 1) / S;
+  const int rb = blockIdx.x / groups;                // 16-row block
+  const int strip0 = (blockIdx.x - rb * groups) * S;
+  a_codes += (int64_t)rb * 16 * (K / 2);
+  a_scales += (int64_t)rb * 16 * (K / kBlock);
+  out += (int64_t)rb * 16 * ldo;
+  M = min(M - rb * 16, 16);
 
   // A: row r (clamped; padded rows are zeroed through their scale)
   const int arow = min(r, M - 1);
@@ -483,7 +493,7 @@ template <int S>
 static void launch_skinny(int nstrips, hipStream_t stream, const uint8_t* a_codes, const uint8_t* a_scales,
                           const float* a_g, int M, int K, const uint8_t* w_codes, const uint8_t* w_scales, int N,
                           const SegTable& st, const float* w_g, float* out, int64_t ldo) {
-  const int grid = (nstrips + S - 1) / S;
+  const int grid = (nstrips + S - 1) / S * ((M + 15) / 16);
   if (K % 32 == 0)
     gemm_skinny_kernel<S, kSkNW, kSkU, true><<<grid, 64 * kSkNW, 0, stream>>>(
         a_codes, a_scales, a_g, M, K, w_codes, w_scales, N, st, w_g, out, ldo);
@@ -497,7 +507,11 @@ hipError_t launch_gemm_skinny(const uint8_t* a_codes, const uint8_t* a_scales, c
                               const SegTable& st, const float* w_g, float* out, int64_t ldo,
                               hipStream_t stream) {
   const int nstrips = (N + kStrip - 1) / kStrip;
-  switch (pick_strips(nstrips)) {
+  // more than 16 rows (16-row blocks, many workgroups): the strips split
+  // into groups as even as S <= 3 allows, e.g. 4 strips as 2 + 2
+  const int s = M <= 16 ? pick_strips(nstrips) : (nstrips + (nstrips + 2) / 3 - 1) / ((nstrips + 2) / 3);
+  if ((int64_t)(nstrips + s - 1) / s * ((M + 15) / 16) > INT32_MAX) return hipErrorInvalidValue;
+  switch (s) {
     case 1:
       launch_skinny<1>(nstrips, stream, a_codes, a_scales, a_g, M, K, w_codes, w_scales, N, st, w_g, out, ldo);
       break;

@@ -67,6 +67,8 @@ def _lib():
         lib.nvfp4_gemm.restype = ctypes.c_int
         lib.nvfp4_gemm.argtypes = [_vp, _vp, _vp, _i64, _i64, _vp, _vp, _i64, ctypes.POINTER(Segment), _vp,
                                    ctypes.c_int32, _vp, _i64, _vp]
+        lib.nvfp4_gemm_form.restype = ctypes.c_int
+        lib.nvfp4_gemm_form.argtypes = [_i64, _i64, _i64]
         lib.nvfp4_linear_workspace_bytes.restype = _sz
         lib.nvfp4_linear_workspace_bytes.argtypes = [_i64, _i64]
         lib.nvfp4_linear.restype = ctypes.c_int
@@ -167,6 +169,10 @@ def nvfp4_gemm(a_codes, a_scales, a_g_dec, M, K, w_codes, w_scales, N, segments,
     arr, n = _segs(segments)
     _check(_lib().nvfp4_gemm(_ptr(a_codes), _ptr(a_scales), _ptr(a_g_dec), M, K, _ptr(w_codes), _ptr(w_scales),
                              N, arr, _ptr(w_g_dec), n, _ptr(out), ldo, _stream(stream)), "nvfp4_gemm")
+
+
+def nvfp4_gemm_form(M, K, N):
+    return _lib().nvfp4_gemm_form(int(M), int(K), int(N))
 
 
 def nvfp4_linear_workspace_bytes(M, K):

@@ -171,11 +171,16 @@ nvfp4_status nvfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const f
   st.nseg = nseg;
   for (int i = 0; i < nseg; ++i) st.end[i] = segs[i].n_end;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (M <= 16)
+  if (nvfp4::gemm_prefers_skinny(M, K, N))
     return launched(nvfp4::launch_gemm_skinny(a_codes, a_scales, a_g_dec, (int)M, (int)K, w_codes, w_scales,
                                               (int)N, st, w_g_dec, out, ldo, s));
   return launched(nvfp4::launch_gemm_mfma(a_codes, a_scales, a_g_dec, (int)M, (int)K, w_codes, w_scales, (int)N,
                                           st, w_g_dec, out, ldo, s));
+}
+
+int nvfp4_gemm_form(int64_t M, int64_t K, int64_t N) {
+  if (M < 0 || K < 0 || N < 0) return -1;
+  return nvfp4::gemm_prefers_skinny(M, K, N) ? 0 : 1;
 }
 
 // ---- nvfp4_linear: the workspace holds the quantizer's amax partials (large inputs only)
@@ -235,7 +240,7 @@ nvfp4_status nvfp4_linear(const void* x_bf16, int64_t M, int64_t K, int64_t ldx,
   const hipError_t e = nvfp4::launch_quantize_act(static_cast<const uint16_t*>(x_bf16), M, K, ldx, amax_in, a_codes,
                                                   a_scales, a_g_dec, workspace, s);
   if (e != hipSuccess) return NVFP4_EHIP;
-  if (M <= 16)
+  if (nvfp4::gemm_prefers_skinny(M, K, N))
     return launched(nvfp4::launch_gemm_skinny(a_codes, a_scales, a_g_dec, (int)M, (int)K, w_codes, w_scales, (int)N,
                                               st, w_g_dec, out, ldo, s));
   return launched(nvfp4::launch_gemm_mfma(a_codes, a_scales, a_g_dec, (int)M, (int)K, w_codes, w_scales, (int)N,

@@ -121,6 +121,9 @@ hipError_t launch_fill_zero(float* out, int M, int N, int64_t ldo, hipStream_t s
 // One-launch decode-form linear layer (activation quantization fused into the
 // skinny GEMM); valid when linear_decode_fits(M, K).
 bool linear_decode_fits(int64_t M, int64_t K);
+// nvfp4_gemm's form for M rows: the weight-streaming skinny GEMM (over 16-row
+// blocks when M > 16) or the MFMA GEMM.
+bool gemm_prefers_skinny(int64_t M, int64_t K, int64_t N);
 hipError_t launch_linear_decode(const uint16_t* x, int64_t ldx, const float* amax_in, uint8_t* a_codes,
                                 uint8_t* a_scales, float* a_g, int M, int K, const uint8_t* w_codes,
                                 const uint8_t* w_scales, int N, const SegTable& st, const float* w_g, float* out,

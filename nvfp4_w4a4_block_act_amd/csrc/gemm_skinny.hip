@@ -524,6 +524,22 @@ hipError_t launch_gemm_skinny(const uint8_t* a_codes, const uint8_t* a_scales, c
   return hipGetLastError();
 }
 
+bool gemm_prefers_skinny(int64_t M, int64_t K, int64_t N) {
+  if (M <= 16) return true;
+  // The MFMA GEMM needs about 256 tiles of 256 x 256 to fill the chip; a round
+  // of them costs ~2.5 us per 128-k tile however few run (97-103 us at K = 5120
+  // for M = 17..256, N = 12288).  The skinny GEMM over 16-row blocks streams
+  // the packed weight once per block, at ~6 TB/s effective because later
+  // blocks find it in the 256 MB last-level cache (N = 12288: 12 us at M = 17,
+  // 87 us at M = 256; N = 34816: 65 us at M = 64, 128 us at M = 128 against
+  // 115 us for the MFMA GEMM).
+  const double ktiles = (double)((K + kTileK - 1) / kTileK);
+  const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);
+  const double t_mfma = (double)((tiles + 255) / 256) * ktiles * 2.5e-6;
+  const double t_skinny = (double)((M + 15) / 16) * (double)N * (double)K * 0.5625 / 6e12 + 3e-6;
+  return t_skinny < t_mfma;
+}
+
 bool linear_decode_fits(int64_t M, int64_t K) {
   return M >= 1 && M <= kDecMaxM && K >= kBlock && decode_tiles_per_wave(M, K) > 0;
 }

@@ -213,3 +213,15 @@ def test_convenience_layer_stream_must_be_a_torch_stream():
                      (nv.pack_weight, (None,))]:
         with pytest.raises(TypeError):
             fn(*args, stream=12345)
+
+
+def test_gemm_form_query():
+    """nvfp4_gemm_form: the skinny GEMM for M <= 16 and wherever too few
+    256 x 256 tiles would fill the chip, the MFMA GEMM for the prefill shapes."""
+    assert nv.nvfp4_gemm_form(-1, 16, 16) == -1
+    assert nv.nvfp4_gemm_form(16, 5120, 12288) == 0
+    assert nv.nvfp4_gemm_form(17, 5120, 12288) == 0
+    assert nv.nvfp4_gemm_form(512, 5120, 12288) == 1
+    assert nv.nvfp4_gemm_form(8192, 5120, 34816) == 1
+    assert nv.nvfp4_gemm_form(4096, 5120, 12352) == 1
+    assert nv.nvfp4_gemm_form(32768, 17408, 5120) == 1

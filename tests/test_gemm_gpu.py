@@ -130,13 +130,14 @@ def test_gemm_subnormal_block_scales(M):
     check_linear(xb, w, [(0, 40), (40, N)], f"subnormal scales M={M}")
 
 
-@pytest.mark.parametrize("M,N,K", [(300, 32808, 1040), (40, 65584, 512)])
+@pytest.mark.parametrize("M,N,K", [(300, 32808, 1040), (520, 65584, 512)])
 def test_gemm_ragged_column_split_along_k(M, N, K):
     """Shapes whose whole 256x256 tiles exactly fill their last round of 256
-    workgroups (2 x 128 and 1 x 256 tiles): the ragged last column then runs as a
+    workgroups (2 x 128 and 3 x 256 tiles): the ragged last column then runs as a
     separate launch of the skinny GEMM over 16-row blocks, with the segment
     table shifted to its columns.  (300, 32808, 1040) also has ragged rows and a
     k tail (K % 128 == 16)."""
+    assert nv.nvfp4_gemm_form(M, K, N) == 1
     rng = np.random.default_rng(M + N + K)
     segs = [(0, 1000), (1000, N - 20), (N - 20, N)]
     w = np.concatenate([(0.02 * (1 + 2 * i) * rng.standard_normal((e - b, K))).astype(np.float32)

@@ -145,7 +145,7 @@ nvfp4_status nvfp4_weight_to_canonical(const uint8_t* w_codes, const uint8_t* w_
  *   out               fp32 [M][ldo], ldo >= N; must not overlap any input.
  * M <= 16 runs the bandwidth-bound skinny path; larger M the MFMA path, except
  * where too few 256 x 256 tiles would run to fill the chip (e.g. M up to ~256 at
- * K = 5120, N = 12288), which runs the skinny path over 16-row blocks.  The MFMA
+ * K = 5120, N = 12288), which streams the weight once per 32 or 64 rows.  The MFMA
  * path addresses its operands with 32-bit byte offsets: for M > 16 the activation
  * codes (M * K / 2 bytes) and the packed weight codes must each be below 4 GiB,
  * else NVFP4_ESHAPE.
@@ -157,8 +157,8 @@ nvfp4_status nvfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const f
                         float* out, int64_t ldo, void* stream);
 
 /* Which kernel form nvfp4_gemm (and the GEMM step of nvfp4_linear) runs for an
- * M x K x N product: 0 = the weight-streaming skinny GEMM (over 16-row blocks
- * when M > 16), 1 = the MFMA GEMM; -1 for negative sizes.  Informational: the
+ * M x K x N product: 0 = the weight-streaming skinny GEMM (32 or 64 rows per
+ * weight pass when M > 16), 1 = the MFMA GEMM; -1 for negative sizes.  Informational: the
  * results of both forms meet the same tolerance. */
 int nvfp4_gemm_form(int64_t M, int64_t K, int64_t N);
 

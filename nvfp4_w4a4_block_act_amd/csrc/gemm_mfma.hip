@@ -453,8 +453,8 @@ hipError_t launch_gemm_mfma(const uint8_t* a_codes, const uint8_t* a_scales, con
   // A ragged last tile column costs a whole extra round of workgroups when the
   // whole tiles fill their last round (e.g. 16 x 48 = 768 = 3 x 256).  Then the
   // whole tiles run alone and the ragged strips -- a tall, narrow product with
-  // a weight slice of a few hundred KB -- run as the skinny GEMM over 16-row
-  // blocks, with the segment table shifted to them.  On the GDN in-projection
+  // a weight slice of a few hundred KB -- run as the weight-streaming GEMM over
+  // 64-row blocks, with the segment table shifted to them.  On the GDN in-projection
   // (4096 x 64 ragged columns, K = 5120) that takes 11 us, where a K-split of
   // the 256 x 256 tile with fp32 atomics into a zeroed output took 29 us; the
   // result is deterministic.

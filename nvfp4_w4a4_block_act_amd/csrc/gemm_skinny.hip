@@ -169,10 +169,7 @@ __device__ __forceinline__ void strip_pointers(const uint8_t* w_codes, const uin
 // data early, the last wave gets all of it at the end of the stream and then
 // has its whole decode and MFMA work left (about 1 us of tail).  Batches have no
 // branches (tiles past the end are clamped and their activation scales zeroed),
-// so the waits before each batch's MFMAs stay progressive.  Inputs with more
-// than 16 rows run as 16-row blocks: workgroup b takes strip group
-// b % groups of row block b / groups (the ragged last tile column of the MFMA
-// GEMM runs this way).
+// so the waits before each batch's MFMAs stay progressive.
 template <int S, int NW, int U, bool AL16>
 __global__ __launch_bounds__(64 * NW) void gemm_skinny_kernel(
     const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales, const float* __restrict__ a_g,
@@ -189,13 +186,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_skinny_kernel(
   const int tiles = (K + kTileK - 1) / kTileK;       // tiles of the packed weight
   const int full = K / kTileK;                       // tiles with no k tail
   const int nstrips = (N + kStrip - 1) / kStrip;
-  const int groups = (nstrips + S - 1) / S;
-  const int rb = blockIdx.x / groups;                // 16-row block
-  const int strip0 = (blockIdx.x - rb * groups) * S;
-  a_codes += (int64_t)rb * 16 * (K / 2);
-  a_scales += (int64_t)rb * 16 * (K / kBlock);
-  out += (int64_t)rb * 16 * ldo;
-  M = min(M - rb * 16, 16);
+  const int strip0 = blockIdx.x * S;
 
   // A: row r (clamped; padded rows are zeroed through their scale)
   const int arow = min(r, M - 1);
@@ -258,6 +249,155 @@ __global__ __launch_bounds__(64 * NW) void gemm_skinny_kernel(
     }
   }
   reduce_store<S, NW>(acc, red, scol, wgv, strip0, M, N, st, ag, out, ldo);
+}
+
+// ---- the same weight stream for more than 16 rows.
+// Workgroup b takes strip group b % groups of the block of 16 MT rows
+// b / groups: each weight fragment is decoded once and multiplied by the MT
+// row tiles' activations, so the packed weight is streamed once per 16 MT rows.
+// Every accumulator sees the same MFMA sequence as in gemm_skinny_kernel, so
+// each row's result is bit-identical to that kernel's.  Used by nvfp4_gemm where
+// too few 256 x 256 tiles would fill the chip for the MFMA GEMM, and for the
+// MFMA GEMM's ragged last tile column.
+template <int S, int NW, int MT>
+__device__ __forceinline__ void reduce_store_rows(const float4_t (&acc)[S][MT], float (&red)[NW][S][MT][4][64],
+                                                  float (&scol)[S * kStrip], float wgv, int strip0, int rows,
+                                                  int N, const SegTable& st, float ag, float* __restrict__ out,
+                                                  int64_t ldo) {
+  static_assert(S * kStrip <= 64, "one lane of wave 0 per column");
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (wave == 0) {
+    const int n = min(strip0 * kStrip + min(lane, S * kStrip - 1), N - 1);
+    const float wc = __shfl(wgv, seg_of(st, n), 64);
+    if (lane < S * kStrip) scol[lane] = wc;
+  }
+#pragma unroll
+  for (int s = 0; s < S; ++s)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) red[wave][s][mt][i][lane] = acc[s][mt][i];
+  __syncthreads();
+  for (int e = threadIdx.x; e < rows * S * kStrip; e += 64 * NW) {
+    const int row = e / (S * kStrip), c = e % (S * kStrip);
+    const int n = strip0 * kStrip + c;
+    if (n >= N) continue;
+    const int mt = row >> 4, rr = row & 15;
+    const int s = c / kStrip, l = (rr >> 2) * kStrip + c % kStrip;
+    float v = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) v += red[w][s][mt][rr & 3][l];
+    out[(int64_t)row * ldo + n] = v * (ag * scol[c]);
+  }
+}
+
+template <int S, int NW, int U, bool AL16, int MT>
+__global__ __launch_bounds__(64 * NW) void gemm_rows_kernel(
+    const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales, const float* __restrict__ a_g,
+    int M, int K, const uint8_t* __restrict__ w_codes, const uint8_t* __restrict__ w_scales, int N,
+    SegTable st, const float* __restrict__ w_g, float* __restrict__ out, int64_t ldo) {
+  constexpr int kDepth = 2;
+  static_assert(U >= kDepth, "pipeline depth");
+  __shared__ float red[NW][S][MT][4][64];
+  __shared__ float scol[S * kStrip];
+  const float ag = *a_g;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r = lane & 15, g = lane >> 4;
+  const int tiles = (K + kTileK - 1) / kTileK;
+  const int full = K / kTileK;
+  const int nstrips = (N + kStrip - 1) / kStrip;
+  const int groups = (nstrips + S - 1) / S;
+  const int rb = blockIdx.x / groups;                // block of 16 MT rows
+  const int strip0 = (blockIdx.x - rb * groups) * S;
+  const int64_t row0 = (int64_t)rb * 16 * MT;
+  const int rows = (int)min((int64_t)16 * MT, (int64_t)M - row0);
+
+  // A: row tile mt, row r (clamped; padded rows are zeroed through their scale)
+  const uint8_t* ac[MT];
+  const uint8_t* as[MT];
+  uint32_t amask[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const int row = 16 * mt + r;
+    const int64_t arow = row0 + min(row, rows - 1);
+    amask[mt] = (row < rows) ? 0xFFFFu : 0u;
+    ac[mt] = a_codes + arow * (K / 2) + g * 16;
+    as[mt] = a_scales + arow * (K / kBlock) + g * 2;
+  }
+  const uint8_t* wc[S];
+  const uint8_t* ws[S];
+  strip_pointers<S>(w_codes, w_scales, strip0, nstrips, tiles, lane, wc, ws);
+  const float wgv = load_segment_scale(w_g, st);
+
+  float4_t acc[S][MT];
+#pragma unroll
+  for (int s = 0; s < S; ++s)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[s][mt] = float4_t{0.f, 0.f, 0.f, 0.f};
+
+  // one batch: the weight fragments of the S strips, decoded once, against the
+  // MT row tiles' activation fragments (same MFMA order as tile_mfma)
+  auto batch = [&](const uint4 (&av)[MT], const uint32_t (&asc)[MT], bool live, const uint4 (&w)[S],
+                   const uint32_t (&wsv)[S]) {
+    half8_t A[MT][4];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) decode_a(av[mt], asc[mt], live ? amask[mt] : 0u, A[mt]);
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      const half2_t s0 = scale_pair(wsv[s] & 0xFF), s1 = scale_pair(wsv[s] >> 8);
+      const half8_t B0 = decode8(w[s].x, s0), B1 = decode8(w[s].y, s0);
+      const half8_t B2 = decode8(w[s].z, s1), B3 = decode8(w[s].w, s1);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        acc[s][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[mt][0], B0, acc[s][mt], 0, 0, 0);
+        acc[s][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[mt][1], B1, acc[s][mt], 0, 0, 0);
+        acc[s][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[mt][2], B2, acc[s][mt], 0, 0, 0);
+        acc[s][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[mt][3], B3, acc[s][mt], 0, 0, 0);
+      }
+    }
+  };
+
+  for (int t0 = wave; t0 < full; t0 += NW * U) {
+    uint4 av[U][MT];
+    uint32_t asc[U][MT];
+    uint4 wv[U][S];
+    uint32_t wsc[U][S];
+    auto request = [&](int u) {
+      const int t = min(t0 + u * NW, full - 1);
+#pragma unroll
+      for (int s = 0; s < S; ++s) {
+        wv[u][s] = *reinterpret_cast<const uint4*>(wc[s] + (int64_t)t * kChunkCodes);
+        wsc[u][s] = *reinterpret_cast<const uint16_t*>(ws[s] + (int64_t)t * kChunkScales);
+      }
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) load_a_full<AL16>(ac[mt], as[mt], t, av[u][mt], asc[u][mt]);
+    };
+#pragma unroll
+    for (int u = 0; u < kDepth; ++u) request(u);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      batch(av[u], asc[u], t0 + u * NW < full, wv[u], wsc[u]);
+      __builtin_amdgcn_sched_barrier(0);
+      if (u + kDepth < U) request(u + kDepth);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  if (full < tiles && wave == full % NW) {           // ragged last tile
+    const int t = full;
+    uint4 av[MT], w[S];
+    uint32_t asc[MT], wsv[S];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) load_a_tail(ac[mt], as[mt], t, t * kTileK + 32 * g, K, av[mt], asc[mt]);
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      w[s] = *reinterpret_cast<const uint4*>(wc[s] + (int64_t)t * kChunkCodes);
+      wsv[s] = *reinterpret_cast<const uint16_t*>(ws[s] + (int64_t)t * kChunkScales);
+    }
+    batch(av, asc, true, w, wsv);
+  }
+  reduce_store_rows<S, NW, MT>(acc, red, scol, wgv, strip0, rows, N, st, ag, out + row0 * ldo, ldo);
 }
 
 // ---- decode-form linear layer in one launch (M <= 16, K <= 5120).
@@ -493,7 +633,7 @@ template <int S>
 static void launch_skinny(int nstrips, hipStream_t stream, const uint8_t* a_codes, const uint8_t* a_scales,
                           const float* a_g, int M, int K, const uint8_t* w_codes, const uint8_t* w_scales, int N,
                           const SegTable& st, const float* w_g, float* out, int64_t ldo) {
-  const int grid = (nstrips + S - 1) / S * ((M + 15) / 16);
+  const int grid = (nstrips + S - 1) / S;
   if (K % 32 == 0)
     gemm_skinny_kernel<S, kSkNW, kSkU, true><<<grid, 64 * kSkNW, 0, stream>>>(
         a_codes, a_scales, a_g, M, K, w_codes, w_scales, N, st, w_g, out, ldo);
@@ -502,42 +642,97 @@ static void launch_skinny(int nstrips, hipStream_t stream, const uint8_t* a_code
         a_codes, a_scales, a_g, M, K, w_codes, w_scales, N, st, w_g, out, ldo);
 }
 
+template <int S, int MT>
+static void launch_rows(int nstrips, int64_t blocks, hipStream_t stream, const uint8_t* a_codes,
+                        const uint8_t* a_scales, const float* a_g, int M, int K, const uint8_t* w_codes,
+                        const uint8_t* w_scales, int N, const SegTable& st, const float* w_g, float* out,
+                        int64_t ldo) {
+  const int grid = (int)((nstrips + S - 1) / S * blocks);
+  if (K % 32 == 0)
+    gemm_rows_kernel<S, kSkNW, kSkU, true, MT><<<grid, 64 * kSkNW, 0, stream>>>(
+        a_codes, a_scales, a_g, M, K, w_codes, w_scales, N, st, w_g, out, ldo);
+  else
+    gemm_rows_kernel<S, kSkNW, kSkU, false, MT><<<grid, 64 * kSkNW, 0, stream>>>(
+        a_codes, a_scales, a_g, M, K, w_codes, w_scales, N, st, w_g, out, ldo);
+}
+
+// Rows per weight pass of gemm_rows_kernel: 32 up to 32 rows, else 64.
+static int rows_per_pass(int64_t M) { return M <= 32 ? 32 : 64; }
+
+// Strips per workgroup of gemm_rows_kernel: every workgroup decodes its S weight
+// fragments and its MT activation tiles per k tile, so the busiest CU's work is
+// ceil(workgroups / 256) * (S + MT); the fewest, ties to larger S (fewer
+// activation re-decodes).  E.g. N = 34816, M = 128: S = 3 (1452 workgroups).
+static int pick_strips_rows(int nstrips, int64_t blocks, int mt) {
+  int best = 3;
+  int64_t cost = 0;
+  for (int s = 3; s >= 1; --s) {
+    const int64_t wgs = (int64_t)(nstrips + s - 1) / s * blocks;
+    const int64_t c = (wgs + kCUs - 1) / kCUs * (s + mt);
+    if (s == 3 || c < cost) {
+      best = s;
+      cost = c;
+    }
+  }
+  return best;
+}
+
 hipError_t launch_gemm_skinny(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_g, int M,
                               int K, const uint8_t* w_codes, const uint8_t* w_scales, int N,
                               const SegTable& st, const float* w_g, float* out, int64_t ldo,
                               hipStream_t stream) {
   const int nstrips = (N + kStrip - 1) / kStrip;
-  // more than 16 rows (16-row blocks, many workgroups): the strips split
-  // into groups as even as S <= 3 allows, e.g. 4 strips as 2 + 2
-  const int s = M <= 16 ? pick_strips(nstrips) : (nstrips + (nstrips + 2) / 3 - 1) / ((nstrips + 2) / 3);
-  if ((int64_t)(nstrips + s - 1) / s * ((M + 15) / 16) > INT32_MAX) return hipErrorInvalidValue;
-  switch (s) {
-    case 1:
-      launch_skinny<1>(nstrips, stream, a_codes, a_scales, a_g, M, K, w_codes, w_scales, N, st, w_g, out, ldo);
-      break;
-    case 2:
-      launch_skinny<2>(nstrips, stream, a_codes, a_scales, a_g, M, K, w_codes, w_scales, N, st, w_g, out, ldo);
-      break;
-    default:
-      launch_skinny<3>(nstrips, stream, a_codes, a_scales, a_g, M, K, w_codes, w_scales, N, st, w_g, out, ldo);
+  if (M <= 16) {
+#define NVFP4_SKINNY(S) launch_skinny<S>(nstrips, stream, a_codes, a_scales, a_g, M, K, w_codes, w_scales, N, st, w_g, out, ldo)
+    switch (pick_strips(nstrips)) {
+      case 1: NVFP4_SKINNY(1); break;
+      case 2: NVFP4_SKINNY(2); break;
+      default: NVFP4_SKINNY(3);
+    }
+#undef NVFP4_SKINNY
+    return hipGetLastError();
   }
+  const int rp = rows_per_pass(M);
+  const int64_t blocks = (M + rp - 1) / rp;
+  const int s = pick_strips_rows(nstrips, blocks, rp / 16);
+  if ((nstrips + s - 1) / s * blocks > INT32_MAX) return hipErrorInvalidValue;
+#define NVFP4_ROWS(S, MT) launch_rows<S, MT>(nstrips, blocks, stream, a_codes, a_scales, a_g, M, K, w_codes, w_scales, N, st, w_g, out, ldo)
+  if (rp == 32) {
+    switch (s) {
+      case 1: NVFP4_ROWS(1, 2); break;
+      case 2: NVFP4_ROWS(2, 2); break;
+      default: NVFP4_ROWS(3, 2);
+    }
+  } else {
+    switch (s) {
+      case 1: NVFP4_ROWS(1, 4); break;
+      case 2: NVFP4_ROWS(2, 4); break;
+      default: NVFP4_ROWS(3, 4);
+    }
+  }
+#undef NVFP4_ROWS
   return hipGetLastError();
 }
 
 bool gemm_prefers_skinny(int64_t M, int64_t K, int64_t N) {
   if (M <= 16) return true;
-  // The MFMA GEMM needs about 256 tiles of 256 x 256 to fill the chip; a round
-  // of them costs ~2.5 us per 128-k tile however few run (97-103 us at K = 5120
-  // for M = 17..256, N = 12288).  The skinny GEMM over 16-row blocks streams
-  // the packed weight once per block, at ~6 TB/s effective because later
-  // blocks find it in the 256 MB last-level cache (N = 12288: 12 us at M = 17,
-  // 87 us at M = 256; N = 34816: 65 us at M = 64, 128 us at M = 128 against
-  // 115 us for the MFMA GEMM).
+  // Cost models measured at K = 5120 (N = 5120, 12288, 34816):
+  //  * the MFMA GEMM needs about 256 tiles of 256 x 256 to fill the chip; a
+  //    round of them costs ~2.5 us per 128-k tile however few run (94-128 us
+  //    for M = 17..256);
+  //  * gemm_rows_kernel streams the packed weight once per 32 or 64 rows at
+  //    ~6 TB/s (later passes find it in the 256 MB last-level cache) and decodes
+  //    both operands for every MFMA, ~4.6e-15 s per multiply-add over the rows
+  //    it computes (N = 12288: 9.4 us at M = 17, 17.6 us at M = 64, 64 us at
+  //    M = 256, 125 us at M = 512 against 110 us for the MFMA GEMM).
   const double ktiles = (double)((K + kTileK - 1) / kTileK);
   const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);
   const double t_mfma = (double)((tiles + 255) / 256) * ktiles * 2.5e-6;
-  const double t_skinny = (double)((M + 15) / 16) * (double)N * (double)K * 0.5625 / 6e12 + 3e-6;
-  return t_skinny < t_mfma;
+  const int rp = rows_per_pass(M);
+  const double passes = (double)((M + rp - 1) / rp);
+  const double t_stream = passes * (double)N * (double)K * 0.5625 / 6e12;
+  const double t_mac = passes * rp * (double)N * (double)K * 4.6e-15;
+  return std::max(t_stream, t_mac) + 3e-6 < t_mfma;
 }
 
 bool linear_decode_fits(int64_t M, int64_t K) {

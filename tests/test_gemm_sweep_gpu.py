@@ -1,5 +1,5 @@
 """Seeded randomized parity sweep of nvfp4_gemm with M > 16 in both of its
-forms -- the MFMA GEMM and the skinny GEMM over 16-row blocks (the form is
+forms -- the MFMA GEMM and the weight-streaming GEMM over 32- or 64-row blocks (the form is
 asserted per case) -- over random M, K (multiples of 16, most of them ragged
 against the 128-k tile), N (ragged against the 256-column tile), module splits
 and activation distributions, against the oracle (all outputs, or a sample of
@@ -20,7 +20,7 @@ pytestmark = pytest.mark.gpu
 
 def _sweep_case(seed, form):
     """A seeded random shape for which nvfp4_gemm takes `form` (1: MFMA GEMM,
-    0: skinny GEMM over 16-row blocks), with 1-5 modules and a ragged k tile."""
+    0: weight-streaming GEMM over row blocks), with 1-5 modules and a ragged k tile."""
     rng = np.random.default_rng(7000 + seed)
     while True:
         if form == 1:

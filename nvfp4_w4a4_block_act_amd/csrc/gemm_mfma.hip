@@ -454,10 +454,11 @@ hipError_t launch_gemm_mfma(const uint8_t* a_codes, const uint8_t* a_scales, con
   // whole tiles fill their last round (e.g. 16 x 48 = 768 = 3 x 256).  Then the
   // whole tiles run alone and the ragged strips -- a tall, narrow product with
   // a weight slice of a few hundred KB -- run as the weight-streaming GEMM over
-  // 64-row blocks, with the segment table shifted to them.  On the GDN in-projection
-  // (4096 x 64 ragged columns, K = 5120) that takes 11 us, where a K-split of
-  // the 256 x 256 tile with fp32 atomics into a zeroed output took 29 us; the
-  // result is deterministic.
+  // row blocks, with the segment table shifted to them.  On the GDN
+  // in-projection (4096 x 64 ragged columns, K = 5120: 16-row blocks, 2 strips
+  // per workgroup) that takes 11-13 us, where a K-split of the 256 x 256 tile
+  // with fp32 atomics into a zeroed output took 29 us; the result is
+  // deterministic.
   const bool ragged = n_full > 0 && n_full < N &&
                       rounds((int64_t)num_m * (n_full / kBN)) < rounds((int64_t)num_m * (N / kBN + 1));
   const int n_main = ragged ? n_full : N;

@@ -134,7 +134,7 @@ def test_gemm_subnormal_block_scales(M):
 def test_gemm_ragged_column_split_along_k(M, N, K):
     """Shapes whose whole 256x256 tiles exactly fill their last round of 256
     workgroups (2 x 128 and 3 x 256 tiles): the ragged last column then runs as a
-    separate launch of the weight-streaming GEMM over 64-row blocks, with the segment
+    separate launch of the weight-streaming GEMM over row blocks, with the segment
     table shifted to its columns.  (300, 32808, 1040) also has ragged rows and a
     k tail (K % 128 == 16)."""
     assert nv.nvfp4_gemm_form(M, K, N) == 1

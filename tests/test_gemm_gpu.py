@@ -222,3 +222,30 @@ def test_gemm_down_proj_full_size():
     rows = _sample(d.M, 24, rng, [0, d.M - 1])
     cols = _sample(d.N, 400, rng, [0, d.N - 1])
     check_linear(d.x_bits, d.w, d.segments, "down proj (sampled)", rows, cols)
+
+
+@pytest.mark.parametrize("M,N,K", [(24, 700, 1040), (32, 200, 5120), (100, 1500, 2064), (70, 100, 1040),
+                                   (300, 2000, 512)])
+def test_gemm_row_blocks_bit_identical_to_16_rows(M, N, K):
+    """nvfp4_gemm's weight-streaming form for M > 16 (32-row passes: (24, 700),
+    (32, 200); 64-row: (100, 1500), (300, 2000); 16-row passes for outputs of at
+    most 8 strips: (70, 100)) gives, for every 16-row slice of the quantized
+    activations, exactly the M <= 16 kernel's result on that slice, and the
+    oracle's within tolerance."""
+    assert nv.nvfp4_gemm_form(M, K, N) == 0
+    rng = np.random.default_rng(M * 7 + N + K)
+    segs = [(0, N // 3), (N // 3, N)]
+    w = np.concatenate([(0.02 * (1 + 3 * i) * rng.standard_normal((e - b, K))).astype(np.float32)
+                        for i, (b, e) in enumerate(segs)])
+    x_bits = W.random_act(M + 2 * K, M, K, "student_t")
+    say(f"[row blocks] M={M} N={N} K={K}")
+    pw = gpu_pack(w, segs)
+    c, s, g = nv.quantize_act(to_dev_bf16(x_bits))
+    out = nv.gemm(c, s, g, pw)
+    for r0 in range(0, M, 16):
+        part = nv.gemm(c[r0:r0 + 16], s[r0:r0 + 16], g, pw)
+        assert torch.equal(part, out[r0:r0 + 16]), f"rows {r0}..{r0 + 15} differ from the 16-row kernel"
+    torch.cuda.synchronize()
+    rows = _sample(M, 24, rng, [0, 15, 16, M - 1])
+    ref, bnd = oracle_linear_rows(x_bits, w, segs, rows=rows)
+    assert_within_tol(out.cpu().numpy().astype(np.float64)[rows], ref, bnd, f"row blocks M={M} N={N}")

@@ -390,6 +390,19 @@ def host_info():
     return info
 
 
+def oracle_threads():
+    """Threads the oracle uses at most: its fp64 matmuls run on the BLAS thread
+    pool; its elementwise numpy steps on one thread."""
+    try:
+        import threadpoolctl
+        n = [d.get("num_threads") for d in threadpoolctl.threadpool_info() if d.get("user_api") == "blas"]
+        if n and n[0]:
+            return int(n[0])
+    except Exception:
+        pass
+    return cpu_threads()
+
+
 def gpu_state():
     """GPU clocks and power as rocm-smi reports them, read once after the timed
     region (a snapshot, not an average over it); None where unavailable."""
@@ -559,10 +572,11 @@ def cpu_baseline_decode(d16, Ms, target_s, step_bytes):
         t_all += time.perf_counter() - t0
         reps += 1
     per_step = t_all / reps * (N / cols)
-    return {"value": round(step_bytes / per_step / 1e9, 4), "unit": "GB/s", "cores": cpu_threads(),
+    return {"value": round(step_bytes / per_step / 1e9, 4), "unit": "GB/s", "cores": oracle_threads(),
             "kind": "oracle", "host": host_info(),
             "sample": f"{reps} oracle steps over {cols} of {N} output columns (all three token counts), "
-                      f"scaled by {N / cols:.1f} to the full step; {t_all:.1f} s of CPU time"}
+                      f"scaled by {N / cols:.1f} to the full step; {t_all:.1f} s of CPU time; fp64 GEMMs on "
+                      f"the BLAS threads, encode/decode steps single-threaded numpy"}
 
 
 # ---------------------------------------------------------------------------------------
@@ -635,10 +649,11 @@ def cpu_baseline_gemm(d, target_s, flops):
         t_all += time.perf_counter() - t0
         reps += 1
     per_step = t_all / reps * (d.M / rows) * (d.N / cols)
-    return {"value": round(flops / per_step / 1e12, 6), "unit": "TFLOP/s", "cores": cpu_threads(),
+    return {"value": round(flops / per_step / 1e12, 6), "unit": "TFLOP/s", "cores": oracle_threads(),
             "kind": "oracle", "host": host_info(),
             "sample": f"{reps} oracle steps over {rows} of {d.M} rows and {cols} of {d.N} output columns, "
-                      f"scaled by {d.M * d.N / (rows * cols):.1f} to the full step; {t_all:.1f} s of CPU time"}
+                      f"scaled by {d.M * d.N / (rows * cols):.1f} to the full step; {t_all:.1f} s of CPU time; "
+                      f"fp64 GEMM on the BLAS threads, encode/decode steps single-threaded numpy"}
 
 
 def bench_quantize(args, torch, nv, W, dev):

@@ -1,6 +1,8 @@
 """GPU parity of the weight packer (bit-exact) and of the W4A4 GEMM with the
 per-segment epilogue (|gpu - oracle| <= 1e-5 * sum|a||b| + 1e-6 elementwise),
 on every workload shape, ragged tails and the mismatch negative control."""
+import functools
+
 import numpy as np
 import pytest
 import torch
@@ -216,12 +218,49 @@ def test_gemm_gdn_in_proj_full_size_and_negative_control():
             assert frac < 0.5
 
 
+@functools.lru_cache(maxsize=1)
+def _down_proj():
+    return W.down_proj()
+
+
 def test_gemm_down_proj_full_size():
-    d = W.down_proj()
+    d = _down_proj()
     rng = np.random.default_rng(3)
     rows = _sample(d.M, 24, rng, [0, d.M - 1])
     cols = _sample(d.N, 400, rng, [0, d.N - 1])
     check_linear(d.x_bits, d.w, d.segments, "down proj (sampled)", rows, cols)
+
+
+@pytest.mark.parametrize("calibrated", [False, True])
+def test_quantizer_down_proj_activations_full_size(calibrated):
+    """The standalone activation quantizer over the full 32768 x 17408 down
+    projection input (the two-pass dynamic path the bench times, and a calibrated
+    scale at 0.7 of the maximum, which saturates blocks): g_dec exact, codes and
+    scales of 64 sampled rows (first and last included) bit-exact against the
+    oracle with the same tensor maximum; the row holding the maximum is among
+    them."""
+    d = _down_proj()
+    mag = d.x_bits & 0x7FFF
+    at = int(np.argmax(mag))
+    amax = float(W.bf16_to_f32(np.array([mag.flat[at]], np.uint16))[0])
+    del mag
+    if calibrated:
+        amax = float(np.float32(amax) * np.float32(0.7))
+    say(f"[quantizer full size] calibrated={calibrated} amax={amax}")
+    x = to_dev_bf16(d.x_bits)
+    am = torch.tensor([amax], dtype=torch.float32, device=DEV) if calibrated else None
+    c, s, g = nv.quantize_act(x, am)
+    torch.cuda.synchronize()
+    del x
+    rng = np.random.default_rng(17 + calibrated)
+    rows = _sample(d.M, 64, rng, [0, at // d.K, d.M - 1])   # the row holding the maximum
+    oc, os_, og, _ = Q.quantize(W.bf16_to_f32(d.x_bits[rows]), np.float32(amax))
+    if calibrated:
+        assert (os_ == 0x7E).any()   # the maximum's block saturates at E4M3 448
+    assert float(g.cpu()[0]) == float(og)
+    rows_t = torch.from_numpy(rows).to(DEV)
+    assert np.array_equal(c.index_select(0, rows_t).cpu().numpy(), oc)
+    assert np.array_equal(s.index_select(0, rows_t).cpu().numpy(), os_)
 
 
 @pytest.mark.parametrize("M,N,K", [(24, 700, 1040), (32, 200, 5120), (100, 1500, 2064), (70, 100, 1040),

@@ -74,11 +74,18 @@ nvfp4_status nvfp4_quantize_act(const void* x_bf16, int64_t M, int64_t K, int64_
     return NVFP4_EALIGN;
   const size_t need = nvfp4::quantize_act_workspace(M, K);
   if (!amax_in && need > 0 && (!workspace || workspace_bytes < need)) return NVFP4_EWORKSPACE;
-  if (!empty) {
-    const size_t xb = (size_t)((M - 1) * ldx + K) * 2, cb = (size_t)(M * K / 2), sb = (size_t)(M * K / 16);
-    if (overlap(x_bf16, xb, codes, cb) || overlap(x_bf16, xb, scales, sb) || overlap(codes, cb, scales, sb) ||
-        overlap(x_bf16, xb, g_dec_out, 4) || overlap(codes, cb, g_dec_out, 4) || overlap(scales, sb, g_dec_out, 4))
-      return NVFP4_EINVAL;
+  // outputs (codes, scales, g_dec, and the workspace the dynamic mode writes)
+  // must not overlap each other or the inputs (x, amax_in)
+  const size_t xb = empty ? 0 : (size_t)((M - 1) * ldx + K) * 2, cb = (size_t)(M * K / 2), sb = (size_t)(M * K / 16);
+  const void* outs[4] = {codes, scales, g_dec_out, amax_in ? nullptr : workspace};
+  const size_t osz[4] = {cb, sb, 4, amax_in ? 0 : need};
+  const void* ins[2] = {x_bf16, amax_in};
+  const size_t isz[2] = {xb, 4};
+  for (int i = 0; i < 4; ++i) {
+    for (int j = 0; j < 2; ++j)
+      if (overlap(outs[i], osz[i], ins[j], isz[j])) return NVFP4_EINVAL;
+    for (int j = i + 1; j < 4; ++j)
+      if (overlap(outs[i], osz[i], outs[j], osz[j])) return NVFP4_EINVAL;
   }
   return launched(nvfp4::launch_quantize_act(static_cast<const uint16_t*>(x_bf16), M, K, ldx, amax_in, codes,
                                              scales, g_dec_out, workspace, static_cast<hipStream_t>(stream)));
@@ -115,7 +122,8 @@ nvfp4_status nvfp4_pack_weight(const float* w, int64_t N, int64_t K, int64_t ldw
   if (overlap(w, wb, w_codes, cb) || overlap(w, wb, w_scales, sb) || overlap(w_codes, cb, w_scales, sb) ||
       overlap(w_g_dec, nseg * 4, w, wb) || overlap(w_g_dec, nseg * 4, w_codes, cb) ||
       overlap(w_g_dec, nseg * 4, w_scales, sb) || overlap(workspace, need, w, wb) ||
-      overlap(workspace, need, w_codes, cb) || overlap(workspace, need, w_scales, sb))
+      overlap(workspace, need, w_codes, cb) || overlap(workspace, need, w_scales, sb) ||
+      overlap(workspace, need, w_g_dec, nseg * 4))
     return NVFP4_EINVAL;
   return launched(nvfp4::launch_pack_weight(w, N, K, ldw, segs, nseg, w_codes, w_scales, w_g_dec, workspace,
                                             static_cast<hipStream_t>(stream)));
@@ -263,6 +271,7 @@ nvfp4_status nvfp4_pack_weight_gate_up(const float* w, int64_t I, int64_t K, int
   const size_t wb = (size_t)((2 * I - 1) * ldw + K) * 4;
   if (overlap(w, wb, w_codes, cb) || overlap(w, wb, w_scales, sb) || overlap(w_codes, cb, w_scales, sb) ||
       overlap(workspace, need, w_codes, cb) || overlap(workspace, need, w_scales, sb) ||
+      overlap(workspace, need, w, wb) || overlap(workspace, need, w_g_dec, 8) ||
       overlap(w_g_dec, 8, w_codes, cb) || overlap(w_g_dec, 8, w_scales, sb) || overlap(w_g_dec, 8, w, wb))
     return NVFP4_EINVAL;
   return launched(nvfp4::launch_pack_weight_gate_up(w, I, K, ldw, w_codes, w_scales, w_g_dec, workspace,

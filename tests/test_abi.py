@@ -58,6 +58,9 @@ def q(x=A, M=4, K=32, ldx=32, amax=None, codes=A + (1 << 20), scales=A + (2 << 2
     (dict(codes=A + 16), 1),                                      # codes overlap x
     (dict(ldx=1 << 31), 2), (dict(ldx=1 << 62), 2),               # leading dimension bound (no overflow)
     (dict(M=4096, K=4096, ldx=4096, codes=A + (64 << 20), scales=A + (80 << 20), g=A + (96 << 20)), 5),
+    (dict(amax=A + (3 << 20)), 1),                                # calibrated amax aliases g_dec
+    (dict(M=4096, K=4096, ldx=4096, codes=A + (64 << 20), scales=A + (80 << 20), g=A + (96 << 20),
+          ws=A + (64 << 20) + 4096, wsb=1 << 20), 1),             # workspace inside the codes
 ])
 def test_quantize_act_validation(kw, status):
     assert q(**kw) == status
@@ -108,6 +111,7 @@ def p(w=A, N=32, K=32, ldw=32, sg=((0, 32),), wc=A + (1 << 20), ws=A + (2 << 20)
 @pytest.mark.parametrize("kw,status", [
     (dict(N=0, sg=((0, 1),)), 1), (dict(K=40), 2), (dict(ldw=16), 2), (dict(sg=((0, 31),)), 4),
     (dict(w=A + 4), 3), (dict(workb=0), 5), (dict(work=None), 5), (dict(wc=A + 64), 1), (dict(ldw=1 << 31), 2),
+    (dict(wg=A + (4 << 20) + 16), 1),                              # workspace holds w_g_dec
 ])
 def test_pack_validation(kw, status):
     assert p(**kw) == status

@@ -250,7 +250,11 @@ def _empty(n, dtype, device):
 
 
 class Workspace:
-    """A growable device scratch buffer owned by the caller."""
+    """A growable device scratch buffer owned by the caller.
+
+    The kernels write into it, so calls that share one Workspace must be ordered
+    (issued on one stream, or synchronized between streams).  Growing it frees the
+    old buffer through torch's stream-ordered allocator."""
 
     def __init__(self, device):
         self.device = device

@@ -670,11 +670,18 @@ def bench_quantize(args, torch, nv, W, dev):
     sec, _ = time_region(torch, lambda i: nv.quantize_act(x, None, ws, out=(c, s, g)), args.steps, 3)
     nbytes = M * K * (2 + 2 + 9 / 16)      # amax pass reads x, encode pass reads x and writes codes+scales
     value = nbytes * args.steps / sec / 1e9
+    # static mode (a calibrated amax; here the tensor's own maximum): the encode pass alone
+    amax = (g * 2688.0).contiguous()
+    sec_s, _ = time_region(torch, lambda i: nv.quantize_act(x, amax, ws, out=(c, s, g)), args.steps, 3)
+    static_bytes = M * K * (2 + 9 / 16)
     return {"metric": "NVFP4 activation quantize GB/s (dynamic scale), % of MI355X HBM roofline",
             "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": 3,
             "ms_per_step": round(sec / args.steps * 1e3, 4), "higher_is_better": True, "scaling": "weak",
             "vs_baseline": None, "dtype": "f32", "data": "synthetic",
-            "config": {"workload": "down_proj_activation_quantize_m32768_k17408"},
+            "config": {"workload": "down_proj_activation_quantize_m32768_k17408",
+                       "algorithmic_bytes_dynamic": int(nbytes), "algorithmic_bytes_static": int(static_bytes),
+                       "static_ms": round(sec_s / args.steps * 1e3, 4),
+                       "static_GBps": round(static_bytes * args.steps / sec_s / 1e9, 1)},
             "roofline": {"bound": "hbm", "achieved": round(value, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(value / HBM_PEAK_GBS, 4), "traffic": None}}
 

@@ -421,6 +421,8 @@ def gpu_state():
 # ---------------------------------------------------------------------------------------
 DECODE_COUNTERS = "linear_decode_kernel_decode_k5120_n12288_counters.md"
 DECODE_SOURCES = ("gemm_skinny.hip", "quant_device.hpp", "common.hpp")
+QUANT_COUNTERS = "quantize_act_kernel_down_proj_activation_m32768_k17408.md"
+QUANT_SOURCES = ("quantize.hip", "quant_device.hpp", "common.hpp")
 
 
 def bench_decode(args, torch, nv, W, dev):
@@ -683,7 +685,11 @@ def bench_quantize(args, torch, nv, W, dev):
                        "static_ms": round(sec_s / args.steps * 1e3, 4),
                        "static_GBps": round(static_bytes * args.steps / sec_s / 1e9, 1)},
             "roofline": {"bound": "hbm", "achieved": round(value, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": round(value / HBM_PEAK_GBS, 4), "traffic": None}}
+                         "frac": round(value / HBM_PEAK_GBS, 4),
+                         "traffic": measured_traffic(QUANT_COUNTERS, QUANT_SOURCES),
+                         "traffic_unit": "bytes per dynamic-mode call (amax pass, its reduction and the encode)",
+                         "algorithmic_bytes_per_call": int(nbytes),
+                         "kernel": "amax_partial_kernel + amax_finalize_kernel + quantize_act_kernel"}}
 
 
 if __name__ == "__main__":

@@ -127,3 +127,27 @@ def test_leading_dimension():
     oc, os_, og, _ = Q.quantize(bf16_to_f32(bits[:, 8:168]))
     assert np.array_equal(c.cpu().numpy(), oc) and np.array_equal(s.cpu().numpy(), os_)
     assert np.float32(g.cpu().numpy()[0]) == og
+
+
+@pytest.mark.parametrize("static", [False, True])
+def test_leading_dimension_two_pass(static):
+    """A strided view above the single-launch size (the amax pass, its reduction and
+    the one-block-per-thread encode all address rows through ldx)."""
+    import torch
+    import nvfp4_w4a4_block_act_amd as nv
+    from gpu_util import to_dev_bf16
+    bits = random_act(13, 600, 432, "student_t")
+    full = to_dev_bf16(bits)
+    view = full[:, 16:16 + 400]                 # ldx = 432, 32-byte aligned start
+    sub = bf16_to_f32(bits[:, 16:416])
+    amax = np.float32(0.5 * np.max(np.abs(sub))) if static else None
+    am = torch.tensor([float(amax)], dtype=torch.float32, device="cuda:0") if static else None
+    c, s, g = nv.quantize_act(view, am)
+    torch.cuda.synchronize()
+    oc, os_, og, _ = Q.quantize(sub, amax)
+    assert np.array_equal(c.cpu().numpy(), oc) and np.array_equal(s.cpu().numpy(), os_)
+    assert np.float32(g.cpu().numpy()[0]) == og
+
+
+def test_all_zero_two_pass():
+    check(np.zeros((300, 1024), np.uint16), None, "all zero, two-pass")

@@ -5,7 +5,8 @@ named ``nvfp4_*`` take torch tensors, check nothing the library does not check
 itself, pass ``data_ptr()`` values and torch's current HIP stream, and raise
 ``NVFP4Error`` on a non-OK status.  Every step of the computation runs in the
 library's HIP kernels; torch only supplies device memory and the stream.
-There is no fallback: if the library is not built, importing it raises.
+There is no fallback: if the library is not built, the first call into it
+raises ImportError.
 
 Convenience layer (allocation only): ``quantize_act``, ``pack_weight``,
 ``gemm`` and ``PackedWeight`` allocate outputs with torch and call the C ABI.

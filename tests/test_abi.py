@@ -60,6 +60,8 @@ def q(x=A, M=4, K=32, ldx=32, amax=None, codes=A + (1 << 20), scales=A + (2 << 2
     (dict(M=4096, K=4096, ldx=4096, codes=A + (64 << 20), scales=A + (80 << 20), g=A + (96 << 20)), 5),
     (dict(amax=A + (3 << 20)), 1),                                # calibrated amax aliases g_dec
     (dict(M=4096, K=4096, ldx=4096, codes=A + (64 << 20), scales=A + (80 << 20), g=A + (96 << 20),
+          ws=A + (128 << 20), wsb=4096), 5),                      # partial maxima only, no room for the maximum
+    (dict(M=4096, K=4096, ldx=4096, codes=A + (64 << 20), scales=A + (80 << 20), g=A + (96 << 20),
           ws=A + (64 << 20) + 4096, wsb=1 << 20), 1),             # workspace inside the codes
 ])
 def test_quantize_act_validation(kw, status):
@@ -68,7 +70,8 @@ def test_quantize_act_validation(kw, status):
 
 def test_quantize_workspace_query():
     assert nv.nvfp4_quantize_act_workspace_bytes(16, 5120) == 0
-    assert nv.nvfp4_quantize_act_workspace_bytes(8192, 5120) > 0
+    assert nv.nvfp4_quantize_act_workspace_bytes(8192, 5120) > 4096
+    assert nv.nvfp4_linear_workspace_bytes(8192, 5120) == nv.nvfp4_quantize_act_workspace_bytes(8192, 5120)
 
 
 def segs(pairs):

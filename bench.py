@@ -404,16 +404,29 @@ def oracle_threads():
 
 
 def gpu_state():
-    """GPU clocks and power as rocm-smi reports them, read once after the timed
-    region (a snapshot, not an average over it); None where unavailable."""
+    """GPU power and clocks as amd-smi (else rocm-smi) reports them when called; None
+    where neither tool answers.  amd-smi's readings trail the load by about a second,
+    so a snapshot taken right after a timed region reflects that region."""
     import subprocess
+    try:
+        r = subprocess.run(["amd-smi", "metric", "--power", "--clock", "--json"], capture_output=True,
+                           text=True, timeout=20)
+        card = json.loads(r.stdout)["gpu_data"][0]
+        clk = [v["clk"]["value"] for k, v in card["clock"].items()
+               if k.startswith("gfx") and isinstance(v, dict) and isinstance(v.get("clk"), dict)]
+        out = {"source": "amd-smi", "socket_power_W": card["power"]["socket_power"]["value"]}
+        if clk:
+            out.update({"gfx_clk_MHz_mean": round(sum(clk) / len(clk), 1), "gfx_clk_MHz_max": max(clk)})
+        return out
+    except Exception:
+        pass
     try:
         r = subprocess.run(["rocm-smi", "--showclocks", "--showpower", "--json"], capture_output=True,
                            text=True, timeout=20)
         card = next(iter(json.loads(r.stdout).values()))
         keep = {k: v for k, v in card.items() if "sclk" in k.lower() or "mclk" in k.lower()
                 or "power" in k.lower()}
-        return keep or None
+        return dict(keep, source="rocm-smi") if keep else None
     except Exception:
         return None
 

@@ -80,19 +80,24 @@ __global__ void kv_fp8_decode_kernel(const uint8_t* __restrict__ codes, int64_t 
   if (blockIdx.x == 0 && t < n) out[t] = (uint16_t)kv_decode_one(codes[t], g);
 }
 
-static int kv_grid(int64_t n) {
-  return (int)std::max<int64_t>(1, std::min<int64_t>((n / 16 + 255) / 256, 256 * 8));
+// Workgroups of 256 threads, one 16-element chunk per thread, capped at
+// max_groups (the threads then loop).  The encode takes a grid that covers the
+// tensor (k + v step of a 32768 x 1024 cache: 5.33 against 5.19 TB/s with eight
+// workgroups per CU, alternating runs on one box); the decode keeps eight per CU
+// (the covering grid measured 21.3 against 19.0 us per tensor for it).
+static int kv_grid(int64_t n, int64_t max_groups) {
+  return (int)std::max<int64_t>(1, std::min<int64_t>((n / 16 + 255) / 256, max_groups));
 }
 
 hipError_t launch_kv_fp8_encode(const uint16_t* x, int64_t n, const float* amax, uint8_t* codes,
                                 hipStream_t stream) {
-  kv_fp8_encode_kernel<<<kv_grid(n), 256, 0, stream>>>(x, n, amax, codes);
+  kv_fp8_encode_kernel<<<kv_grid(n, (int64_t)1 << 20), 256, 0, stream>>>(x, n, amax, codes);
   return hipGetLastError();
 }
 
 hipError_t launch_kv_fp8_decode(const uint8_t* codes, int64_t n, const float* amax, uint16_t* out,
                                 hipStream_t stream) {
-  kv_fp8_decode_kernel<<<kv_grid(n), 256, 0, stream>>>(codes, n, amax, out);
+  kv_fp8_decode_kernel<<<kv_grid(n, 256 * 8), 256, 0, stream>>>(codes, n, amax, out);
   return hipGetLastError();
 }
 

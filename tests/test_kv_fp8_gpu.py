@@ -48,7 +48,7 @@ def test_kv_tensor_with_calibrated_saturation():
     check(bits, amax, "kv saturating")
 
 
-@pytest.mark.parametrize("n", [1, 15, 16, 17, 31, 33, 1000])
+@pytest.mark.parametrize("n", [1, 15, 16, 17, 31, 33, 1000, 12293, (1 << 20) + 7])
 def test_ragged_lengths(n):
     rng = np.random.default_rng(n)
     check(W.bf16_bits(rng.standard_normal(n).astype(np.float32)), 2.5, f"ragged {n}")

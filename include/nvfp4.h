@@ -20,6 +20,8 @@
  *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
  *    Work is enqueued on it and the call returns without synchronizing;
  *    device-side faults surface at the caller's next synchronization.
+ *    Kernels write into a call's workspace, so calls that share one must be
+ *    ordered (one stream, or synchronized between streams).
  *  - Arguments are validated on the host before anything is launched; a
  *    non-OK status means nothing was enqueued.  The library never prints and
  *    never aborts.  NVFP4_EHIP reports a failed launch (hipGetLastError).

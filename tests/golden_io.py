@@ -48,7 +48,8 @@ def fp32_round(q):
 
 def load_quant_fixtures():
     """List of dicts: name, amax (None = dynamic), g_dec (Fraction), x [1, 16*B] float32,
-    scales [1, B] uint8, codes [1, 16*B] uint8 (unpacked nibbles)."""
+    scales [1, B] uint8, codes [1, 16*B] uint8 (unpacked nibbles), packed [1, 8*B] uint8
+    (the stored bytes, as the fixture file writes them out)."""
     out, cur = [], None
     with open(os.path.join(GOLDEN, "quant_blocks.txt")) as f:
         for line in f:
@@ -60,19 +61,22 @@ def load_quant_fixtures():
                 kv = dict(p.split("=", 1) for p in parts[2:])
                 cur = {"name": parts[1],
                        "amax": None if kv["amax"] == "dynamic" else float(kv["amax"]),
-                       "g_dec": parse_rational(kv["g_dec"]), "x": [], "scales": [], "codes": []}
+                       "g_dec": parse_rational(kv["g_dec"]), "x": [], "scales": [], "codes": [], "packed": []}
             elif parts[0] == "block":
                 kv = dict(p.split("=", 1) for p in parts[1:])
                 xs = [parse_value(t) for t in kv["x"].split(",")]
                 cs = [int(c, 16) for c in kv["codes"]]
-                assert len(xs) == 16 and len(cs) == 16
+                bs = [int(kv["bytes"][2 * j:2 * j + 2], 16) for j in range(len(kv["bytes"]) // 2)]
+                assert len(xs) == 16 and len(cs) == 16 and len(bs) == 8
                 cur["x"] += xs
                 cur["codes"] += cs
+                cur["packed"] += bs
                 cur["scales"].append(int(kv["scale"], 16))
             elif parts[0] == "end":
                 cur["x"] = np.array([cur["x"]], np.float32)
                 cur["codes"] = np.array([cur["codes"]], np.uint8)
                 cur["scales"] = np.array([cur["scales"]], np.uint8)
+                cur["packed"] = np.array([cur["packed"]], np.uint8)
                 out.append(cur)
                 cur = None
     return out

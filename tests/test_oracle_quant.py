@@ -19,6 +19,23 @@ def test_hand_worked_fixtures(fx):
     assert np.float32(g_dec).tobytes() == fp32_round(fx["g_dec"]).tobytes()
 
 
+@pytest.mark.parametrize("fx", FIXTURES, ids=[f["name"] for f in FIXTURES])
+def test_hand_worked_packed_bytes(fx):
+    """The stored byte order (reading S12 of the format passage: two codes per byte, the
+    even element in the low nibble): quantize's packed output equals the fixture's
+    literal bytes, not just its unpacked nibbles."""
+    codes, _, _, _ = Q.quantize(fx["x"], fx["amax"])
+    assert codes.dtype == np.uint8 and codes.shape == fx["packed"].shape
+    assert np.array_equal(codes, fx["packed"]), (codes, fx["packed"])
+
+
+def test_unpack_codes_literal():
+    """unpack_codes on literal bytes: 0x21 holds element 0 = 1 (low nibble) and element 1 = 2;
+    0xF0 holds 0 then 0xF; 0x8A holds 0xA then 8."""
+    got = Q.unpack_codes(np.array([[0x21, 0xF0, 0x8A]], np.uint8))
+    assert got.tolist() == [[0x1, 0x2, 0x0, 0xF, 0xA, 0x8]]
+
+
 def _tensors():
     t = tiny()
     yield "tiny_act", bf16_to_f32(t.x_bits)

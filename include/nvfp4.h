@@ -22,14 +22,19 @@
  *    device-side faults surface at the caller's next synchronization.
  *    Kernels write into a call's workspace, so calls that share one must be
  *    ordered (one stream, or synchronized between streams).
- *  - Arguments are validated on the host before anything is launched; a
- *    non-OK status means nothing was enqueued.  The library never prints and
- *    never aborts.  NVFP4_EHIP reports a failed launch (hipGetLastError).
+ *  - Arguments are validated on the host before anything is launched: every
+ *    status except NVFP4_EHIP means nothing was enqueued.  NVFP4_EHIP means the
+ *    HIP runtime rejected a launch (hipGetLastError); a call that enqueues
+ *    several kernels (the two-pass quantizer, nvfp4_linear outside its
+ *    one-launch range, a GEMM with a ragged last tile column) may already have
+ *    enqueued the kernels before the rejected one, and all of its outputs are
+ *    then unspecified.  The library never prints and never aborts.
  *  - Element codes are packed two per byte, the even k in the low nibble:
  *    byte j of a row = code[2j] | code[2j+1] << 4; code = sign << 3 | mag,
  *    mag 0..7 = 0, 0.5, 1, 1.5, 2, 3, 4, 6.  Scales are E4M3FN bytes
  *    (0x00..0x7E).  Blocks of 16 run along K.
- *  - Every pointer must be 16-byte aligned; K must be a multiple of 16.
+ *  - Every pointer must be 16-byte aligned, scalars and small tables included
+ *    (NVFP4_EALIGN); K must be a multiple of 16.
  *  - Every row count, column count and leading dimension must be below 2^31
  *    (NVFP4_ESHAPE otherwise).
  */
@@ -180,7 +185,9 @@ int nvfp4_gemm_form(int64_t M, int64_t K, int64_t N);
  *
  *   workspace  device scratch of nvfp4_linear_workspace_bytes(M, K) bytes
  *              (NULL allowed when that is 0 or amax_in is given); contents
- *              need no setup.
+ *              need no setup.  In dynamic mode it is written, so it must not
+ *              overlap any input or output (NVFP4_EINVAL).
+ * K == 0 writes g_dec and zero outputs; M == 0 writes g_dec only.
  * ------------------------------------------------------------------------- */
 size_t nvfp4_linear_workspace_bytes(int64_t M, int64_t K);
 
@@ -205,8 +212,12 @@ nvfp4_status nvfp4_linear(const void* x_bf16, int64_t M, int64_t K, int64_t ldx,
  *   h     = bf16(silu(g) * u), silu(z) = z / (1 + e^-z), evaluated in fp32
  *           (round to nearest even to bf16);
  *   codes, scales, g_dec = nvfp4_quantize_act(h, amax_in = amax_h).
- * The result is bit-identical to nvfp4_gemm (unfused packing), nvfp4_swiglu
- * and nvfp4_quantize_act run one after another.
+ * The fused kernel is the MFMA GEMM with this epilogue.  Its result is
+ * bit-identical to nvfp4_gemm (unfused packing), nvfp4_swiglu and
+ * nvfp4_quantize_act run one after another whenever that nvfp4_gemm takes the
+ * MFMA form (nvfp4_gemm_form(M, K, 2I) == 1); where nvfp4_gemm takes the
+ * weight-streaming form (small M) the two sum in different fp32 orders, and g
+ * and u agree within the GEMM tolerance instead.
  * ------------------------------------------------------------------------- */
 
 /* Pack a gate+up weight pair for nvfp4_gemm_swiglu_quantize.  w is fp32

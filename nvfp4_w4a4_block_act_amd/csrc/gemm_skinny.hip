@@ -430,19 +430,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_rows_kernel(
 // launch) are measurably faster for small M.  BAL lowers each wave's issue
 // priority after each batch of step 5 (set_issue_priority).  The results are
 // bit-identical to the activation quantizer followed by the skinny GEMM.
-constexpr int kDecMaxM = 16;
 constexpr int kDecRowBytes = kTileK / 2 + 16;   // LDS bytes per row of one tile (padded)
-
-// k tiles per wave (U) of the one-launch layer for an M x K input, 0 when it
-// has no instance: the wave-private activation area (MAXM * U tiles of
-// kDecRowBytes) must fit LDS and the lane's block registers (MAXM * U / 8
-// steps of two 16-byte chunks) the register file, so longer K takes fewer rows.
-static int decode_tiles_per_wave(int64_t M, int64_t K) {
-  if (K <= 8 * 5 * kTileK) return 5;               // K <= 5120: every row bound
-  if (K <= 8 * 10 * kTileK && M <= 8) return 10;   // K <= 10240
-  if (K <= 8 * 20 * kTileK && M <= 4) return 20;   // K <= 20480
-  return 0;
-}
 
 template <int S, int NW, int U, int MAXM, bool BAL>
 __global__ __launch_bounds__(64 * NW) void linear_decode_kernel(
@@ -608,7 +596,6 @@ hipError_t launch_fill_zero(float* out, int M, int N, int64_t ldo, hipStream_t s
 }
 
 constexpr int kSkNW = 8, kSkU = 5;
-constexpr int kCUs = 256;   // compute units of a gfx950 (MI355X) device
 
 // Strips per workgroup (1..3): the fewest strips on the busiest CU -- a launch
 // of more than 256 workgroups puts a second one on some CUs -- with ties going
@@ -654,15 +641,6 @@ static void launch_rows(int nstrips, int64_t blocks, hipStream_t stream, const u
   else
     gemm_rows_kernel<S, kSkNW, kSkU, false, MT><<<grid, 64 * kSkNW, 0, stream>>>(
         a_codes, a_scales, a_g, M, K, w_codes, w_scales, N, st, w_g, out, ldo);
-}
-
-// Rows per weight pass of gemm_rows_kernel: 16 for outputs of at most 8 strips
-// (there the activation work dominates: the 64 ragged columns of the GDN
-// in-projection take 12.9 us in 16-row passes with 2 strips per workgroup and
-// 15.3 us in 64-row passes with 1), else 32 up to 32 rows and 64 beyond.
-static int rows_per_pass(int64_t M, int64_t N) {
-  if ((N + kStrip - 1) / kStrip <= 8) return 16;
-  return M <= 32 ? 32 : 64;
 }
 
 // Strips per workgroup of gemm_rows_kernel: every workgroup decodes its S weight
@@ -724,31 +702,6 @@ hipError_t launch_gemm_skinny(const uint8_t* a_codes, const uint8_t* a_scales, c
   }
 #undef NVFP4_ROWS
   return hipGetLastError();
-}
-
-bool gemm_prefers_skinny(int64_t M, int64_t K, int64_t N) {
-  if (M <= 16) return true;
-  // Cost models measured at K = 5120 (N = 5120, 12288, 34816):
-  //  * the MFMA GEMM needs about 256 tiles of 256 x 256 to fill the chip; a
-  //    round of them costs ~2.5 us per 128-k tile however few run (94-128 us
-  //    for M = 17..256);
-  //  * gemm_rows_kernel streams the packed weight once per 32 or 64 rows at
-  //    ~6 TB/s (later passes find it in the 256 MB last-level cache) and decodes
-  //    both operands for every MFMA, ~4.6e-15 s per multiply-add over the rows
-  //    it computes (N = 12288: 9.4 us at M = 17, 17.6 us at M = 64, 64 us at
-  //    M = 256, 125 us at M = 512 against 110 us for the MFMA GEMM).
-  const double ktiles = (double)((K + kTileK - 1) / kTileK);
-  const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);
-  const double t_mfma = (double)((tiles + 255) / 256) * ktiles * 2.5e-6;
-  const int rp = rows_per_pass(M, N);
-  const double passes = (double)((M + rp - 1) / rp);
-  const double t_stream = passes * (double)N * (double)K * 0.5625 / 6e12;
-  const double t_mac = passes * rp * (double)N * (double)K * 4.6e-15;
-  return std::max(t_stream, t_mac) + 3e-6 < t_mfma;
-}
-
-bool linear_decode_fits(int64_t M, int64_t K) {
-  return M >= 1 && M <= kDecMaxM && K >= kBlock && decode_tiles_per_wave(M, K) > 0;
 }
 
 // One instantiation per row bound.  The issue-priority balancing of the waves

@@ -36,10 +36,8 @@
 namespace nvfp4 {
 
 constexpr int kQThreads = 256;
-constexpr int kPartials = 1024;              // amax workgroups in the two-pass path
 constexpr int kAmaxLoads = 4;                // amax pass: 16-byte loads in flight per thread
 constexpr int64_t kMaxEncodeGrid = 1 << 20;  // encoder workgroups (blocks beyond loop)
-constexpr int64_t kSmallElems = 1 << 17;     // single-launch path up to 128K elements
 
 // Encode the bf16 block (m, b) of x.
 __device__ __forceinline__ void encode_block_at(const uint16_t* __restrict__ x, int64_t ldx, int K, int64_t m,
@@ -179,11 +177,6 @@ __global__ void g_dec_only_kernel(const float* __restrict__ amax_in, float* __re
   *g_dec_out = amax_in ? *amax_in / kGMax : 0.0f;
 }
 
-size_t quantize_act_workspace(int64_t M, int64_t K) {
-  // the partial maxima, then the maximum itself
-  return (M * K > kSmallElems) ? kPartials * sizeof(uint32_t) + 16 : 0;
-}
-
 hipError_t launch_quantize_act(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
                                const float* amax_in, uint8_t* codes, uint8_t* scales,
                                float* g_dec_out, void* workspace, hipStream_t stream) {
@@ -222,8 +215,6 @@ __global__ __launch_bounds__(kQThreads) void amax_observe_finalize_kernel(const 
   m = block_reduce_max(m, red);
   if (threadIdx.x == 0) *running = fmaxf(*running, __uint_as_float(m << 16));
 }
-
-size_t amax_observe_workspace() { return kPartials * sizeof(uint32_t); }
 
 hipError_t launch_amax_observe(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, float* running,
                                void* workspace, hipStream_t stream) {
@@ -291,8 +282,6 @@ hipError_t launch_quantize_stats(const uint16_t* x, int64_t M, int64_t K, int64_
 }
 
 // ---- weights: per-module encode into the tiled layout ----------------------------
-constexpr int kSegParts = 64;   // amax workgroups per segment
-
 // partial[s * kSegParts + p] = max |w| bits over a slice of segment s's rows.
 __global__ __launch_bounds__(kQThreads) void seg_amax_kernel(const float* __restrict__ w, int K, int64_t ldw,
                                                              SegTable st, uint32_t* __restrict__ partial) {
@@ -376,10 +365,6 @@ __global__ __launch_bounds__(kQThreads) void weight_to_canonical_kernel(
     *reinterpret_cast<uint2*>(codes + (int64_t)n * (K / 2) + (int64_t)b * 8) = c;
     scales[(int64_t)n * nb + b] = w_scales[chunk * kChunkScales + chunk_scale_off(r, bb >> 1) + (bb & 1)];
   }
-}
-
-size_t pack_weight_workspace(int64_t, int64_t, int nseg) {
-  return (size_t)nseg * kSegParts * sizeof(uint32_t);
 }
 
 static hipError_t pack_weight_impl(const float* w, int64_t N, int64_t K, int64_t ldw, const SegTable& st,

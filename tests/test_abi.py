@@ -140,6 +140,51 @@ def test_linear_validation(kw, status):
     assert lin(**kw) == status
 
 
+def test_linear_validates_everything_before_any_launch():
+    """Empty K with a bad output, and a dynamic-mode workspace that overlaps an input,
+    are rejected on the host.  (Had anything been launched first, this machine's HIP
+    runtime would have turned it into NVFP4_EHIP instead.)"""
+    assert lin(x=None, K=0, out=None) == 1
+    assert lin(x=None, K=0, out=A + (7 << 20) + 4) == 3
+    big = dict(M=4096, K=4096, ldx=4096, ac=A + (64 << 20), as_=A + (80 << 20), ag=A + (96 << 20),
+               wc=A + (128 << 20), ws=A + (160 << 20), wg=A + (192 << 20), out=A + (256 << 20))
+    wsb = nv.nvfp4_linear_workspace_bytes(4096, 4096)
+    assert lin(work=A + 64, workb=wsb, **big) == 1                 # workspace inside x
+    assert lin(work=A + (128 << 20), workb=wsb, **big) == 1        # workspace inside the weight codes
+    assert lin(work=A + (300 << 20) + 4, workb=wsb, **big) == 3    # misaligned workspace
+
+
+@pytest.mark.parametrize("call", [
+    lambda: q(g=A + (3 << 20) + 4),                                # g_dec_out
+    lambda: q(amax=A + (4 << 20) + 8),                             # calibrated amax
+    lambda: g(ag=A + (2 << 20) + 4),                               # activation g_dec
+    lambda: g(wg=A + (5 << 20) + 8),                               # per-module g_dec
+    lambda: nv.lib().nvfp4_quantize_stats(A, 4, 32, 32, A + (1 << 20), A + (2 << 20) + 4, None),   # counts
+    lambda: nv.lib().nvfp4_swiglu(A + 4, 4, 64, 128, A + (1 << 20), 64, None),                     # gu
+    lambda: nv.lib().nvfp4_swiglu(A, 4, 64, 128, A + (1 << 20) + 2, 64, None),                     # h
+    lambda: nv.lib().nvfp4_amax_observe(A, 4, 32, 32, A + (1 << 20) + 4, A + (2 << 20), 4096, None),
+    lambda: nv.lib().nvfp4_kv_fp8_encode(A, 64, A + (1 << 20) + 4, A + (2 << 20), None),
+])
+def test_every_pointer_is_checked_for_alignment(call):
+    assert call() == 3
+
+
+def _no_gpu_here():
+    import torch
+    return not os.path.exists("/dev/kfd") and not torch.cuda.is_available()
+
+
+def test_runtime_rejection_maps_to_ehip():
+    """On a machine without a GPU the HIP runtime rejects every launch: a call whose
+    arguments pass validation returns NVFP4_EHIP (skipped where a GPU exists, since the
+    fake addresses must never reach a real launch)."""
+    if not _no_gpu_here():
+        pytest.skip("a GPU is present; the fake device addresses must not be launched on")
+    assert g() == 6
+    assert q() == 6
+    assert lin() == 6
+
+
 def gu_pack(w=A, I=128, K=32, ldw=32, wc=A + (1 << 20), ws=A + (2 << 20), wg=A + (3 << 20), work=A + (4 << 20),
             workb=4096):
     return nv.lib().nvfp4_pack_weight_gate_up(w, I, K, ldw, wc, ws, wg, work, workb, None)

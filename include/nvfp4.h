@@ -291,6 +291,24 @@ nvfp4_status nvfp4_kv_fp8_encode(const void* x_bf16, int64_t n, const float* ama
 
 nvfp4_status nvfp4_kv_fp8_decode(const uint8_t* codes, int64_t n, const float* amax, void* out_bf16, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * Diagnostic: the device conversion steps the encoders and GEMMs are built
+ * on, applied to the binary32 values with bit patterns first_bits + i,
+ * i < n, so that tests can compare them with the format definitions over
+ * whole ranges (e.g. every binary32 in [0, 8] or [0, 448]).  Values 2j and
+ * 2j + 1 are converted as one pair, as the encoders pair elements.
+ *   op 0  out[i] = E2M1 code (sign << 3 | magnitude code; nearest, ties to
+ *         even, saturating at 6): the element step of every NVFP4 encoder.
+ *   op 1  out[i] = E4M3FN code (nearest, ties to even, saturating at 448):
+ *         the block-scale step and the FP8 KV-cache encode.
+ *   op 2  out[2i], out[2i + 1] = fp16 bits (little endian) of the exact
+ *         decode the GEMMs feed the matrix cores: E2M1 code (first_bits + i) & 15
+ *         times E4M3 code ((first_bits + i) >> 4) & 127.
+ * out holds n bytes (op 0, 1) or 2n bytes (op 2); first_bits + n <= 2^32
+ * (NVFP4_ESHAPE otherwise); op outside 0..2 is NVFP4_EINVAL.
+ * ------------------------------------------------------------------------- */
+nvfp4_status nvfp4_convert_sweep(int32_t op, uint32_t first_bits, int64_t n, uint8_t* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -92,6 +92,8 @@ def _lib():
         lib.nvfp4_kv_fp8_decode.argtypes = [_vp, _i64, _vp, _vp, _vp]
         lib.nvfp4_swiglu.restype = ctypes.c_int
         lib.nvfp4_swiglu.argtypes = [_vp, _i64, _i64, _i64, _vp, _i64, _vp]
+        lib.nvfp4_convert_sweep.restype = ctypes.c_int
+        lib.nvfp4_convert_sweep.argtypes = [ctypes.c_int32, ctypes.c_uint32, _i64, _vp, _vp]
         _LIB = lib
     return _LIB
 
@@ -226,6 +228,11 @@ def nvfp4_kv_fp8_decode(codes, n, amax, out, stream=None):
 
 def nvfp4_swiglu(gu, M, I, ldgu, h, ldh, stream=None):
     _check(_lib().nvfp4_swiglu(_ptr(gu), M, I, ldgu, _ptr(h), ldh, _stream(stream)), "nvfp4_swiglu")
+
+
+def nvfp4_convert_sweep(op, first_bits, n, out, stream=None):
+    _check(_lib().nvfp4_convert_sweep(int(op), int(first_bits), int(n), _ptr(out), _stream(stream)),
+           "nvfp4_convert_sweep")
 
 
 # ---- convenience layer: allocate with torch, call the C ABI --------------------------

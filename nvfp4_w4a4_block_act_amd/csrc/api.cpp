@@ -430,4 +430,14 @@ nvfp4_status nvfp4_kv_fp8_decode(const uint8_t* codes, int64_t n, const float* a
                                               static_cast<hipStream_t>(stream)));
 }
 
+// ---- diagnostic: the device conversion steps over a range of bit patterns
+nvfp4_status nvfp4_convert_sweep(int32_t op, uint32_t first_bits, int64_t n, uint8_t* out, void* stream) {
+  if (op < 0 || op > 2 || n < 0) return NVFP4_EINVAL;
+  if ((uint64_t)first_bits + (uint64_t)n > (1ull << 32)) return NVFP4_ESHAPE;
+  if (n == 0) return NVFP4_OK;
+  if (!out) return NVFP4_EINVAL;
+  if (!aligned16(out)) return NVFP4_EALIGN;
+  return launched(nvfp4::launch_convert_sweep(op, first_bits, n, out, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -26,13 +26,25 @@ __device__ __forceinline__ int seg_of(const SegTable& st, int n) {
 
 // ---- E4M3FN -----------------------------------------------------------------
 // Round a non-negative binary32 s (finite or +inf) to the nearest E4M3FN
-// magnitude code, ties to even mantissa, saturating at 448 (0x7E).  gfx950's
+// magnitude code, ties to even mantissa, saturating at 448 (0x7E); the pair
+// form rounds two values into the low two bytes (sign bits kept).  gfx950's
 // v_cvt_pk_fp8_f32 rounds to nearest even on OCP E4M3FN; with its input clamped
 // to 448 it equals this rule for every binary32 value (checked exhaustively on
 // the device for all values in [0, 448], subnormals included; larger inputs and
 // +inf clamp to 448).
-__device__ __forceinline__ uint32_t e4m3_encode_rne_sat(float s) {
-  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(fminf(s, 448.0f), 0.0f, 0, false) & 0x7Fu;
+__device__ __forceinline__ uint32_t e4m3_pair_rne_sat(float s0, float s1) {
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(fminf(s0, 448.0f), fminf(s1, 448.0f), 0, false) & 0xFFFFu;
+}
+__device__ __forceinline__ uint32_t e4m3_encode_rne_sat(float s) { return e4m3_pair_rne_sat(s, 0.0f) & 0x7Fu; }
+
+// ---- E2M1 ---------------------------------------------------------------------
+// Round two binary32 values to E2M1 codes (sign << 3 | magnitude code, nearest,
+// ties to even, saturating at 6) and place them in byte SEL of w, the first in
+// the low nibble: gfx950's v_cvt_scalef32_pk_fp4_f32 with unit scale, the one
+// conversion every encoder here uses (checked exhaustively on the device).
+template <int SEL>
+__device__ __forceinline__ uint32_t e2m1_pack_pair(uint32_t w, float a, float b) {
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, a, b, 1.0f, SEL);
 }
 
 // Exact binary32 value of an E4M3FN magnitude code 0..0x7E (v_cvt_f32_fp8 is

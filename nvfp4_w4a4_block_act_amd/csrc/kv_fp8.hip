@@ -24,9 +24,9 @@ __device__ __forceinline__ float kv_g_enc(float amax) { return (amax == 0.0f) ? 
 
 // Codes of one bf16 word pair (elements lo, hi of `w`), as bits 0-15 of the result.
 __device__ __forceinline__ uint32_t kv_encode_pair(uint32_t w, float g) {
-  const float y0 = fminf(__uint_as_float((w << 16) & 0x7FFF0000u) * g, 448.0f);
-  const float y1 = fminf(__uint_as_float(w & 0x7FFF0000u) * g, 448.0f);
-  const uint32_t m = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y0, y1, 0, false) & 0xFFFFu;
+  const float y0 = __uint_as_float((w << 16) & 0x7FFF0000u) * g;
+  const float y1 = __uint_as_float(w & 0x7FFF0000u) * g;
+  const uint32_t m = e4m3_pair_rne_sat(y0, y1);
   const uint32_t sign = ((w >> 8) & 0x80u) | ((w >> 16) & 0x8000u);   // bf16 sign bits 15, 31 -> 7, 15
   return m | sign;
 }

@@ -105,6 +105,7 @@ hipError_t launch_amax_observe(const uint16_t* x, int64_t M, int64_t K, int64_t 
                                void* workspace, hipStream_t stream);
 hipError_t launch_quantize_stats(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, const float* amax_in,
                                  uint32_t* counts, hipStream_t stream);
+hipError_t launch_convert_sweep(int op, uint32_t first, int64_t n, uint8_t* out, hipStream_t stream);
 hipError_t launch_kv_fp8_encode(const uint16_t* x, int64_t n, const float* amax, uint8_t* codes,
                                 hipStream_t stream);
 hipError_t launch_kv_fp8_decode(const uint8_t* codes, int64_t n, const float* amax, uint16_t* out,

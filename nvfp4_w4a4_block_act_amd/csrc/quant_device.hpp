@@ -37,14 +37,14 @@ __device__ __forceinline__ uint32_t encode_block(const float (&x)[16], float bma
     for (int i = 0; i < 16; ++i) y[i] = x[i] * rb;
   }
   uint32_t lo = 0, hi = 0;
-  lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo, y[0], y[1], 1.0f, 0);
-  lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo, y[2], y[3], 1.0f, 1);
-  lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo, y[4], y[5], 1.0f, 2);
-  lo = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo, y[6], y[7], 1.0f, 3);
-  hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi, y[8], y[9], 1.0f, 0);
-  hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi, y[10], y[11], 1.0f, 1);
-  hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi, y[12], y[13], 1.0f, 2);
-  hi = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi, y[14], y[15], 1.0f, 3);
+  lo = e2m1_pack_pair<0>(lo, y[0], y[1]);
+  lo = e2m1_pack_pair<1>(lo, y[2], y[3]);
+  lo = e2m1_pack_pair<2>(lo, y[4], y[5]);
+  lo = e2m1_pack_pair<3>(lo, y[6], y[7]);
+  hi = e2m1_pack_pair<0>(hi, y[8], y[9]);
+  hi = e2m1_pack_pair<1>(hi, y[10], y[11]);
+  hi = e2m1_pack_pair<2>(hi, y[12], y[13]);
+  hi = e2m1_pack_pair<3>(hi, y[14], y[15]);
   out = make_uint2(lo, hi);
   return sc;
 }
@@ -116,9 +116,8 @@ __device__ __forceinline__ EncCtx make_ctx(float amax, const float* rtab) {
 // Encode one bf16 block given as two 16-byte chunks (element 2 i in the low
 // half of word i): returns the scale code and the 8 code bytes in `c`.  Works
 // pair by pair on the packed words to keep few values live.
-#define NVFP4_PAIR(W, I, SEL, MUL)                                                                     \
-  W = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(W, MUL(__uint_as_float(d[I] << 16)),                  \
-                                               MUL(__uint_as_float(d[I] & 0xFFFF0000u)), 1.0f, SEL)
+#define NVFP4_PAIR(W, I, SEL, MUL) \
+  W = e2m1_pack_pair<SEL>(W, MUL(__uint_as_float(d[I] << 16)), MUL(__uint_as_float(d[I] & 0xFFFF0000u)))
 #define NVFP4_PAIRS(MUL)                                                                               \
   NVFP4_PAIR(lo, 0, 0, MUL); NVFP4_PAIR(lo, 1, 1, MUL); NVFP4_PAIR(lo, 2, 2, MUL);                   \
   NVFP4_PAIR(lo, 3, 3, MUL); NVFP4_PAIR(hi, 4, 0, MUL); NVFP4_PAIR(hi, 5, 1, MUL);                   \

@@ -281,6 +281,46 @@ hipError_t launch_quantize_stats(const uint16_t* x, int64_t M, int64_t K, int64_
   return hipGetLastError();
 }
 
+// ---- conversion sweep (diagnostic) ------------------------------------------------
+// For the binary32 value v_i with bit pattern first + i, i < n (values 2 j and
+// 2 j + 1 form one pair, the first in the low half, as the encoders pair them):
+//   op 0: out[i] = E2M1 code of v_i through e2m1_pack_pair (the element step);
+//   op 1: out[i] = E4M3 code of v_i through e4m3_pair_rne_sat (the block-scale
+//         step and the KV-cache codec);
+//   op 2: out[2 i .. 2 i + 1] = fp16 bits (little endian) of the GEMMs' exact
+//         decode (decode8 with scale_pair) of E2M1 code (first + i) & 15 times
+//         E4M3 code ((first + i) >> 4) & 127.
+__global__ __launch_bounds__(kQThreads) void convert_sweep_kernel(int op, uint32_t first, int64_t n,
+                                                                 uint8_t* __restrict__ out) {
+  const int64_t pairs = (n + 1) / 2;
+  for (int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; j < pairs; j += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t i0 = 2 * j;
+    const bool two = i0 + 1 < n;
+    const uint32_t b0 = first + (uint32_t)i0, b1 = two ? b0 + 1 : b0;
+    if (op == 0) {
+      const uint32_t c = e2m1_pack_pair<0>(0u, __uint_as_float(b0), __uint_as_float(b1));
+      out[i0] = (uint8_t)(c & 15u);
+      if (two) out[i0 + 1] = (uint8_t)((c >> 4) & 15u);
+    } else if (op == 1) {
+      const uint32_t c = e4m3_pair_rne_sat(__uint_as_float(b0), __uint_as_float(b1));
+      out[i0] = (uint8_t)(c & 0xFFu);
+      if (two) out[i0 + 1] = (uint8_t)(c >> 8);
+    } else {
+      const uint32_t h0 = __builtin_bit_cast(uint16_t, decode8(b0 & 15u, scale_pair((b0 >> 4) & 127u))[0]);
+      const uint32_t h1 = __builtin_bit_cast(uint16_t, decode8(b1 & 15u, scale_pair((b1 >> 4) & 127u))[0]);
+      *reinterpret_cast<uint16_t*>(out + 2 * i0) = (uint16_t)h0;
+      if (two) *reinterpret_cast<uint16_t*>(out + 2 * i0 + 2) = (uint16_t)h1;
+    }
+  }
+}
+
+hipError_t launch_convert_sweep(int op, uint32_t first, int64_t n, uint8_t* out, hipStream_t stream) {
+  if (n == 0) return hipSuccess;
+  const int grid = (int)std::min<int64_t>(((n + 1) / 2 + kQThreads - 1) / kQThreads, 256 * 64);
+  convert_sweep_kernel<<<grid, kQThreads, 0, stream>>>(op, first, n, out);
+  return hipGetLastError();
+}
+
 // ---- weights: per-module encode into the tiled layout ----------------------------
 // partial[s * kSegParts + p] = max |w| bits over a slice of segment s's rows.
 __global__ __launch_bounds__(kQThreads) void seg_amax_kernel(const float* __restrict__ w, int K, int64_t ldw,

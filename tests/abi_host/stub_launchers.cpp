@@ -58,6 +58,7 @@ hipError_t launch_amax_observe(const uint16_t*, int64_t, int64_t, int64_t, float
 hipError_t launch_quantize_stats(const uint16_t*, int64_t, int64_t, int64_t, const float*, uint32_t*, hipStream_t) {
   return record();
 }
+hipError_t launch_convert_sweep(int, uint32_t, int64_t, uint8_t*, hipStream_t) { return record(); }
 hipError_t launch_kv_fp8_encode(const uint16_t*, int64_t, const float*, uint8_t*, hipStream_t) { return record(); }
 hipError_t launch_kv_fp8_decode(const uint8_t*, int64_t, const float*, uint16_t*, hipStream_t) { return record(); }
 }  // namespace nvfp4

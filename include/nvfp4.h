@@ -16,7 +16,8 @@
  * Conventions for every call:
  *  - Buffer pointers are DEVICE pointers unless marked "host".  The caller
  *    allocates and owns every buffer; the library never allocates, frees or
- *    retains device memory and keeps no mutable global state.
+ *    retains device memory.  Its only global state is nvfp4_linear_noalloc's
+ *    scratch: a static device array per GPU and the cached device addresses.
  *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
  *    Work is enqueued on it and the call returns without synchronizing;
  *    device-side faults surface at the caller's next synchronization.
@@ -196,6 +197,23 @@ nvfp4_status nvfp4_linear(const void* x_bf16, int64_t M, int64_t K, int64_t ldx,
                           const uint8_t* w_codes, const uint8_t* w_scales, int64_t N,
                           const nvfp4_segment* segs, const float* w_g_dec, int32_t nseg,
                           float* out, int64_t ldo, void* workspace, size_t workspace_bytes, void* stream);
+
+/* nvfp4_linear for callers that cannot allocate device memory -- code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc:
+ * the same call and results, with the workspace replaced by the library's own
+ * scratch, a file-scope device array of 4112 bytes per GPU (enough for the
+ * quantizer's partial maxima at every M and K; a workspace need beyond it
+ * would be NVFP4_EWORKSPACE), held until the process ends.  Its device address
+ * is looked up on the first call for the stream's GPU (NVFP4_EHIP if that
+ * lookup fails, with nothing enqueued); the call itself allocates nothing.
+ * Every call on one GPU shares that GPU's scratch, so calls that overlap in
+ * time on one GPU (different streams, not ordered) race; calls on one stream
+ * are ordered.  The scratch needs no clearing: each call writes what it reads. */
+nvfp4_status nvfp4_linear_noalloc(const void* x_bf16, int64_t M, int64_t K, int64_t ldx, const float* amax_in,
+                                  uint8_t* a_codes, uint8_t* a_scales, float* a_g_dec,
+                                  const uint8_t* w_codes, const uint8_t* w_scales, int64_t N,
+                                  const nvfp4_segment* segs, const float* w_g_dec, int32_t nseg,
+                                  float* out, int64_t ldo, void* stream);
 
 /* ---------------------------------------------------------------------------
  * Fused gate+up projection with the SwiGLU -> NVFP4 epilogue.

@@ -75,6 +75,9 @@ def _lib():
         lib.nvfp4_linear.restype = ctypes.c_int
         lib.nvfp4_linear.argtypes = [_vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _i64,
                                      ctypes.POINTER(Segment), _vp, ctypes.c_int32, _vp, _i64, _vp, _sz, _vp]
+        lib.nvfp4_linear_noalloc.restype = ctypes.c_int
+        lib.nvfp4_linear_noalloc.argtypes = [_vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _i64,
+                                             ctypes.POINTER(Segment), _vp, ctypes.c_int32, _vp, _i64, _vp]
         lib.nvfp4_pack_weight_gate_up.restype = ctypes.c_int
         lib.nvfp4_pack_weight_gate_up.argtypes = [_vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _sz, _vp]
         lib.nvfp4_gemm_swiglu_quantize.restype = ctypes.c_int
@@ -188,6 +191,14 @@ def nvfp4_linear(x, M, K, ldx, amax_in, a_codes, a_scales, a_g_dec, w_codes, w_s
     _check(_lib().nvfp4_linear(_ptr(x), M, K, ldx, _ptr(amax_in), _ptr(a_codes), _ptr(a_scales), _ptr(a_g_dec),
                                _ptr(w_codes), _ptr(w_scales), N, arr, _ptr(w_g_dec), n, _ptr(out), ldo,
                                _ptr(workspace), workspace_bytes, _stream(stream)), "nvfp4_linear")
+
+
+def nvfp4_linear_noalloc(x, M, K, ldx, amax_in, a_codes, a_scales, a_g_dec, w_codes, w_scales, N, segments,
+                         w_g_dec, out, ldo, stream=None):
+    arr, n = _segs(segments)
+    _check(_lib().nvfp4_linear_noalloc(_ptr(x), M, K, ldx, _ptr(amax_in), _ptr(a_codes), _ptr(a_scales),
+                                       _ptr(a_g_dec), _ptr(w_codes), _ptr(w_scales), N, arr, _ptr(w_g_dec), n,
+                                       _ptr(out), ldo, _stream(stream)), "nvfp4_linear_noalloc")
 
 
 def nvfp4_pack_weight_gate_up(w, I, K, ldw, w_codes, w_scales, w_g_dec, workspace, workspace_bytes, stream=None):

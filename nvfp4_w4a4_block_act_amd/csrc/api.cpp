@@ -276,11 +276,11 @@ size_t nvfp4_linear_workspace_bytes(int64_t M, int64_t K) {
   return nvfp4::quantize_act_workspace(M, K);
 }
 
-nvfp4_status nvfp4_linear(const void* x_bf16, int64_t M, int64_t K, int64_t ldx, const float* amax_in,
-                          uint8_t* a_codes, uint8_t* a_scales, float* a_g_dec, const uint8_t* w_codes,
-                          const uint8_t* w_scales, int64_t N, const nvfp4_segment* segs, const float* w_g_dec,
-                          int32_t nseg, float* out, int64_t ldo, void* workspace, size_t workspace_bytes,
-                          void* stream) {
+static nvfp4_status linear_impl(const void* x_bf16, int64_t M, int64_t K, int64_t ldx, const float* amax_in,
+                                uint8_t* a_codes, uint8_t* a_scales, float* a_g_dec, const uint8_t* w_codes,
+                                const uint8_t* w_scales, int64_t N, const nvfp4_segment* segs, const float* w_g_dec,
+                                int32_t nseg, float* out, int64_t ldo, void* workspace, size_t workspace_bytes,
+                                void* stream) {
   const nvfp4_status s = check_linear(x_bf16, M, K, ldx, amax_in, a_codes, a_scales, a_g_dec, w_codes, w_scales,
                                       N, segs, w_g_dec, nseg, out, ldo, workspace, workspace_bytes);
   if (s != NVFP4_OK) return s;
@@ -301,6 +301,28 @@ nvfp4_status nvfp4_linear(const void* x_bf16, int64_t M, int64_t K, int64_t ldx,
                                               tab, w_g_dec, out, ldo, st));
   return launched(nvfp4::launch_gemm_mfma(a_codes, a_scales, a_g_dec, (int)M, (int)K, w_codes, w_scales, (int)N,
                                           tab, w_g_dec, out, ldo, st));
+}
+
+nvfp4_status nvfp4_linear(const void* x_bf16, int64_t M, int64_t K, int64_t ldx, const float* amax_in,
+                          uint8_t* a_codes, uint8_t* a_scales, float* a_g_dec, const uint8_t* w_codes,
+                          const uint8_t* w_scales, int64_t N, const nvfp4_segment* segs, const float* w_g_dec,
+                          int32_t nseg, float* out, int64_t ldo, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  return linear_impl(x_bf16, M, K, ldx, amax_in, a_codes, a_scales, a_g_dec, w_codes, w_scales, N, segs, w_g_dec,
+                     nseg, out, ldo, workspace, workspace_bytes, stream);
+}
+
+// The same with the library's own scratch (one static device array per GPU)
+// in place of the caller's workspace: no allocation anywhere in the call.
+nvfp4_status nvfp4_linear_noalloc(const void* x_bf16, int64_t M, int64_t K, int64_t ldx, const float* amax_in,
+                                  uint8_t* a_codes, uint8_t* a_scales, float* a_g_dec, const uint8_t* w_codes,
+                                  const uint8_t* w_scales, int64_t N, const nvfp4_segment* segs,
+                                  const float* w_g_dec, int32_t nseg, float* out, int64_t ldo, void* stream) {
+  if (M >= 0 && K >= 0 && nvfp4::quantize_act_workspace(M, K) > nvfp4::kScratchBytes) return NVFP4_EWORKSPACE;
+  void* scratch = nullptr;
+  if (nvfp4::scratch_for_stream(static_cast<hipStream_t>(stream), &scratch) != hipSuccess) return NVFP4_EHIP;
+  return linear_impl(x_bf16, M, K, ldx, amax_in, a_codes, a_scales, a_g_dec, w_codes, w_scales, N, segs, w_g_dec,
+                     nseg, out, ldo, scratch, nvfp4::kScratchBytes, stream);
 }
 
 // ---- fused gate+up GEMM with the SwiGLU -> NVFP4 epilogue

@@ -28,6 +28,8 @@ constexpr int kPartials = 1024;             // amax workgroups of the two-pass a
 constexpr int64_t kSmallElems = 1 << 17;    // single-launch activation quantizer up to 128K elements
 constexpr int kSegParts = 64;               // amax workgroups per weight segment (packer)
 constexpr int kDecMaxM = 16;                // rows of the one-launch decode layer
+constexpr size_t kScratchBytes = kPartials * sizeof(uint32_t) + 16;   // nvfp4_linear_noalloc's scratch
+constexpr int kMaxDevices = 64;             // GPUs whose scratch address is cached
 
 // k tiles per wave (U) of the one-launch decode layer for an M x K input, 0
 // when it has no instance: the wave-private activation area (MAXM * U tiles of
@@ -105,6 +107,9 @@ hipError_t launch_amax_observe(const uint16_t* x, int64_t M, int64_t K, int64_t 
                                void* workspace, hipStream_t stream);
 hipError_t launch_quantize_stats(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, const float* amax_in,
                                  uint32_t* counts, hipStream_t stream);
+// Device address of the current GPU's (or `stream`'s GPU's) copy of the
+// allocation-free scratch (kScratchBytes), looked up once per device.
+hipError_t scratch_for_stream(hipStream_t stream, void** out);
 hipError_t launch_convert_sweep(int op, uint32_t first, int64_t n, uint8_t* out, hipStream_t stream);
 hipError_t launch_kv_fp8_encode(const uint16_t* x, int64_t n, const float* amax, uint8_t* codes,
                                 hipStream_t stream);

@@ -29,6 +29,7 @@
 //    every 1024-thread workgroup recomputes the whole-tensor maximum from L2
 //    with all of its loads in flight at once.
 #include <algorithm>
+#include <mutex>
 
 #include "common.hpp"
 #include "quant_device.hpp"
@@ -279,6 +280,43 @@ hipError_t launch_quantize_stats(const uint16_t* x, int64_t M, int64_t K, int64_
   const int grid = (int)std::min<int64_t>((blocks + kQThreads - 1) / kQThreads, 256 * 8);
   quantize_stats_kernel<<<grid, kQThreads, 0, stream>>>(x, M, (int)K, ldx, amax_in, counts);
   return hipGetLastError();
+}
+
+// ---- allocation-free scratch --------------------------------------------------------
+// The two-pass quantizer's workspace (partial maxima, then the maximum) for the
+// entry point that allocates nothing: a file-scope device array, one copy per
+// GPU, held until the process ends.  Its device address is looked up once per
+// device and cached; kernels receive that address, never the host-side name.
+// Calls that overlap on one GPU share it and race (the caller orders them).
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+hipError_t scratch_for_stream(hipStream_t stream, void** out) {
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int cur = 0;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return e;
+  int dev = cur;
+  if (stream) {
+    hipDevice_t d = 0;
+    e = hipStreamGetDevice(stream, &d);
+    if (e != hipSuccess) return e;
+    dev = (int)d;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess) return e;
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    const hipError_t back = (dev != cur) ? hipSetDevice(cur) : hipSuccess;
+    if (e != hipSuccess) return e;
+    if (back != hipSuccess) return back;
+    if (!p) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return hipSuccess;
 }
 
 // ---- conversion sweep (diagnostic) ------------------------------------------------

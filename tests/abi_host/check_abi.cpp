@@ -96,6 +96,12 @@ int main() {
       // the GEMM launch after an enqueued quantizer is rejected: EHIP (the header
       // says the kernels before it may already be enqueued)
       {"linear second launch fails", [qws] { return lin(at(0), 4096, 4096, 4096, nullptr, at<float>(224), at(300), qws); }, NVFP4_EHIP, 2, 1},
+      // ---- nvfp4_linear_noalloc: the library's scratch in place of the workspace
+      {"noalloc large ok", [] { nvfp4_segment sg[1] = {{0, 32}}; return nvfp4_linear_noalloc(at(0), 4096, 4096, 4096, nullptr, at<uint8_t>(64), at<uint8_t>(80), at<float>(96), at<uint8_t>(128), at<uint8_t>(160), 32, sg, at<float>(192), 1, at<float>(224), 32, nullptr); }, NVFP4_OK, 2},
+      {"noalloc decode ok", [] { nvfp4_segment sg[1] = {{0, 32}}; return nvfp4_linear_noalloc(at(0), 4, 32, 32, nullptr, at<uint8_t>(64), at<uint8_t>(80), at<float>(96), at<uint8_t>(128), at<uint8_t>(160), 32, sg, at<float>(192), 1, at<float>(224), 32, nullptr); }, NVFP4_OK, 1},
+      {"noalloc bad shape", [] { nvfp4_segment sg[1] = {{0, 32}}; return nvfp4_linear_noalloc(at(0), 4, 24, 32, nullptr, at<uint8_t>(64), at<uint8_t>(80), at<float>(96), at<uint8_t>(128), at<uint8_t>(160), 32, sg, at<float>(192), 1, at<float>(224), 32, nullptr); }, NVFP4_ESHAPE, 0},
+      {"noalloc out over x", [] { nvfp4_segment sg[1] = {{0, 32}}; return nvfp4_linear_noalloc(at(0), 4096, 4096, 4096, nullptr, at<uint8_t>(64), at<uint8_t>(80), at<float>(96), at<uint8_t>(128), at<uint8_t>(160), 32, sg, at<float>(192), 1, at<float>(16), 32, nullptr); }, NVFP4_EINVAL, 0},
+      {"noalloc scratch lookup fails", [] { stub::scratch_fails = true; nvfp4_segment sg[1] = {{0, 32}}; const nvfp4_status s = nvfp4_linear_noalloc(at(0), 4, 32, 32, nullptr, at<uint8_t>(64), at<uint8_t>(80), at<float>(96), at<uint8_t>(128), at<uint8_t>(160), 32, sg, at<float>(192), 1, at<float>(224), 32, nullptr); stub::scratch_fails = false; return s; }, NVFP4_EHIP, 0},
       // ---- pack, swiglu, calibration, KV codec
       {"pack ok", [] { return nvfp4_pack_weight(at<float>(0), 32, 32, 32, one, 1, at<uint8_t>(1), at<uint8_t>(2), at<float>(3), at(4), 4096, nullptr); }, NVFP4_OK, 1},
       {"pack ws misaligned", [] { return nvfp4_pack_weight(at<float>(0), 32, 32, 32, one, 1, at<uint8_t>(1), at<uint8_t>(2), at<float>(3), at(4, 4), 4096, nullptr); }, NVFP4_EALIGN, 0},

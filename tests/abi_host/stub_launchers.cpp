@@ -8,6 +8,7 @@
 namespace stub {
 int launches = 0;
 int fail_from = -1;   // launch index from which launches fail (-1: never)
+bool scratch_fails = false;
 }  // namespace stub
 
 static hipError_t record() {
@@ -59,6 +60,12 @@ hipError_t launch_quantize_stats(const uint16_t*, int64_t, int64_t, int64_t, con
   return record();
 }
 hipError_t launch_convert_sweep(int, uint32_t, int64_t, uint8_t*, hipStream_t) { return record(); }
+// the allocation-free scratch: a fake device address, or a lookup error
+hipError_t scratch_for_stream(hipStream_t, void** out) {
+  if (stub::scratch_fails) return hipErrorInvalidSymbol;
+  *out = reinterpret_cast<void*>(uintptr_t(1) << 44);
+  return hipSuccess;
+}
 hipError_t launch_kv_fp8_encode(const uint16_t*, int64_t, const float*, uint8_t*, hipStream_t) { return record(); }
 hipError_t launch_kv_fp8_decode(const uint8_t*, int64_t, const float*, uint16_t*, hipStream_t) { return record(); }
 }  // namespace nvfp4

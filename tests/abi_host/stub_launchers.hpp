@@ -6,4 +6,5 @@
 namespace stub {
 extern int launches;
 extern int fail_from;
+extern bool scratch_fails;
 }  // namespace stub

@@ -13,8 +13,16 @@ the 16 copies in turn are captured in one HIP graph, replayed once per 16
 timed steps (remainders replay single-step graphs); inputs are resident in HBM
 before the timed region starts.
 
+The same run then measures the prefill half of the metric (``config.prefill``):
+the gate+up (8192 x 5120 x 2 x 17408), GDN in-projection (4096 x 5120 x 12352)
+and down-projection (32768 x 17408 x 5120) GEMMs -- quantize + GEMM + epilogue
+per step, the GEMM kernel alone timed with event pairs, each with its roofline
+against the fp16 matrix-core peak and an oracle baseline -- and the standalone
+activation quantizer over the down projection's input (GB/s against HBM).
+
 Prints one JSON line (see the keys below).  ``--config`` selects another
-workload (prefill_gate_up, gdn_in_proj, down_proj, down_proj_quantize, tiny).
+workload on its own (prefill_gate_up, gdn_in_proj, down_proj,
+down_proj_quantize, tiny, ...); ``--no-prefill`` skips the prefill legs.
 """
 import argparse
 import json
@@ -40,6 +48,10 @@ def parse():
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying HIP graphs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--no-prefill", action="store_true", help="decode only (no prefill legs in the default run)")
+    ap.add_argument("--prefill-steps", type=int, default=20, help="timed steps of each prefill leg")
+    ap.add_argument("--prefill-cpu-seconds", type=float, default=5.0,
+                    help="target CPU time of each prefill leg's oracle sample")
     return ap.parse_args()
 
 
@@ -564,34 +576,73 @@ def bench_decode(args, torch, nv, W, dev):
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline_decode(d16, Ms, args.cpu_seconds, step_bytes)
+    if not args.no_prefill:
+        del copies, pw0, xs, acts, outs, ws
+        if not args.no_graph:
+            del long_graph, singles
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        res["config"]["prefill"] = prefill_legs(args, torch, nv, W, dev)
     return res
+
+
+# ---- the oracle on the host: its row-independent steps over a thread pool ----------
+def _row_chunks(rows, threads):
+    return [c for c in np.array_split(np.arange(rows), max(1, min(threads, rows))) if len(c)]
+
+
+def oracle_quantize(x32, amax, pool, threads):
+    """oracle.nvfp4.quantize of a float32 [R, K] tensor with the given tensor maximum,
+    row chunks on the pool (rows are independent once the maximum is fixed)."""
+    from oracle import nvfp4 as Q
+    parts = list(pool.map(lambda r: Q.quantize(x32[r], amax), _row_chunks(x32.shape[0], threads)))
+    return (np.concatenate([p[0] for p in parts]), np.concatenate([p[1] for p in parts]), parts[0][2])
+
+
+def oracle_dequantize(c, s, g, pool, threads):
+    from oracle import nvfp4 as Q
+    parts = list(pool.map(lambda r: Q.dequantize(c[r], s[r], g), _row_chunks(c.shape[0], threads)))
+    return np.concatenate(parts)
+
+
+def oracle_amax(x32, pool, threads):
+    return np.float32(max(pool.map(lambda r: np.max(np.abs(x32[r])), _row_chunks(x32.shape[0], threads))))
+
+
+def cpu_kind(threads):
+    return (f"oracle (numpy; its encode/decode steps on {threads} threads over row chunks, "
+            f"fp64 GEMMs on the BLAS threads)")
 
 
 def cpu_baseline_decode(d16, Ms, target_s, step_bytes):
     """The oracle on the host: per call, quantize + decode the activations and run the fp64
-    GEMM against pre-decoded weights.  Sample: a slice of the weight's output columns
-    (weights are encoded outside the timed part, like the GPU's pre-packed weights)."""
+    GEMM against the decoded weights (the weight decode is part of every oracle step).
+    Sample: a slice of the weight's output columns (weights are encoded outside the
+    timed part, like the GPU's pre-packed weights)."""
+    from concurrent.futures import ThreadPoolExecutor
     from oracle import gemm as G
     from oracle import nvfp4 as Q
     from workloads import bf16_to_f32
     N, K = d16.N, d16.K
     cols = 1536
+    threads = cpu_threads()
     wc, ws, wg, _ = Q.quantize(d16.w[:cols], np.float32(np.max(np.abs(d16.w))))
     t_all, reps = 0.0, 0
-    while t_all < target_s and reps < 1000:
-        t0 = time.perf_counter()
-        w_hat = Q.dequantize(wc, ws, wg)
-        for M in Ms:
-            c, s, g, _ = Q.quantize(bf16_to_f32(d16.x_bits[:M]))
-            G.gemm_f64(Q.dequantize(c, s, g), w_hat)
-        t_all += time.perf_counter() - t0
-        reps += 1
+    with ThreadPoolExecutor(threads) as pool:
+        while t_all < target_s and reps < 1000:
+            t0 = time.perf_counter()
+            w_hat = oracle_dequantize(wc, ws, wg, pool, threads)
+            for M in Ms:
+                x32 = bf16_to_f32(d16.x_bits[:M])
+                c, s, g = oracle_quantize(x32, oracle_amax(x32, pool, threads), pool, threads)
+                G.gemm_f64(oracle_dequantize(c, s, g, pool, threads), w_hat)
+            t_all += time.perf_counter() - t0
+            reps += 1
     per_step = t_all / reps * (N / cols)
-    return {"value": round(step_bytes / per_step / 1e9, 4), "unit": "GB/s", "cores": oracle_threads(),
+    return {"value": round(step_bytes / per_step / 1e9, 4), "unit": "GB/s", "cores": max(threads, oracle_threads()),
             "kind": "oracle", "host": host_info(),
             "sample": f"{reps} oracle steps over {cols} of {N} output columns (all three token counts), "
-                      f"scaled by {N / cols:.1f} to the full step; {t_all:.1f} s of CPU time; fp64 GEMMs on "
-                      f"the BLAS threads, encode/decode steps single-threaded numpy"}
+                      f"scaled by {N / cols:.1f} to the full step; {t_all:.1f} s of CPU time; {cpu_kind(threads)}"}
 
 
 # ---------------------------------------------------------------------------------------
@@ -601,13 +652,17 @@ GEMM_CONFIGS = {
     "gdn_in_proj": lambda W: W.gdn_in_proj(),
     "down_proj": lambda W: W.down_proj(),
 }
+GEMM_METRIC = "NVFP4 W4A4 prefill GEMM TFLOP/s (quantize + GEMM + epilogue), % of MI355X fp16 MFMA roofline"
 
 
-def bench_gemm(args, torch, nv, W, dev):
-    d = GEMM_CONFIGS[args.config](W)
+def gemm_leg(args, torch, nv, dev, d, steps, warmup, cpu_seconds, x=None):
+    """One prefill workload: quantize (dynamic scale) + GEMM + per-module epilogue per
+    step, timed over `steps` steps; the GEMM call alone timed with an event pair around
+    each launch on its stream.  TFLOP/s counts 2 M N K."""
     M, K, N = d.M, d.K, d.N
     pw = nv.pack_weight(torch.from_numpy(d.w).to(dev), d.segments)
-    x = to_dev_bf16(torch, d.x_bits, dev)
+    if x is None:
+        x = to_dev_bf16(torch, d.x_bits, dev)
     c = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
     s = torch.empty((M, K // 16), dtype=torch.uint8, device=dev)
     g = torch.empty(1, dtype=torch.float32, device=dev)
@@ -619,90 +674,164 @@ def bench_gemm(args, torch, nv, W, dev):
         nv.quantize_act(x, None, ws, out=(c, s, g))
         nv.gemm(c, s, g, pw, out=out)
 
-    steps = max(1, args.steps)
-    sec, wall = time_region(torch, step, steps, min(args.warmup, 5))
+    sec, _ = time_region(torch, step, steps, warmup)
     flops = 2.0 * M * N * K
-    value = flops * steps / sec / 1e12
-    mean, med, p10, p90 = kernel_time_pairs(torch, lambda i: nv.gemm(c, s, g, pw, out=out), max(8, steps // 2), 2)
+    mean, med, p10, p90 = kernel_time_pairs(torch, lambda i: nv.gemm(c, s, g, pw, out=out), max(8, steps), 2)
     achieved = flops / mean / 1e12
-    state = gpu_state()
-    res = {
-        "metric": "NVFP4 W4A4 prefill GEMM TFLOP/s (quantize + GEMM + epilogue), % of MI355X fp16 MFMA roofline",
-        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": steps, "warmup": min(args.warmup, 5),
-        "ms_per_step": round(sec / steps * 1e3, 4), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "f16",
-        "dtype_note": "NVFP4 operands decoded exactly to fp16, fp16 MFMA products, fp32 accumulation",
-        "data": "synthetic",
-        "config": {"workload": d.name, "M": M, "K": K, "N": N, "segments": len(d.segments),
-                   "gemm_kernel_mean_ms": round(mean * 1e3, 4), "gemm_kernel_median_ms": round(med * 1e3, 4),
-                   "gemm_kernel_p10_ms": round(p10 * 1e3, 4), "gemm_kernel_p90_ms": round(p90 * 1e3, 4),
-                   "gpu_state_after_run": state},
-        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": F16_MFMA_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved / F16_MFMA_PEAK_TFLOPS, 4), "traffic": None,
-                     "kernel": "gemm_mfma_kernel"},
-    }
-    if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline_gemm(d, args.cpu_seconds, flops)
+    leg = {"workload": d.name, "M": M, "K": K, "N": N, "segments": len(d.segments),
+           "gemm_form": "mfma" if nv.nvfp4_gemm_form(M, K, N) == 1 else "weight_streaming",
+           "steps": steps, "step_ms": round(sec / steps * 1e3, 4),
+           "step_TFLOPs": round(flops * steps / sec / 1e12, 2),
+           "gemm_kernel_mean_ms": round(mean * 1e3, 4), "gemm_kernel_median_ms": round(med * 1e3, 4),
+           "gemm_kernel_p10_ms": round(p10 * 1e3, 4), "gemm_kernel_p90_ms": round(p90 * 1e3, 4),
+           "gpu_state_after_run": gpu_state(),
+           "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": F16_MFMA_PEAK_TFLOPS,
+                        "unit": "TFLOP/s", "frac": round(achieved / F16_MFMA_PEAK_TFLOPS, 4), "traffic": None,
+                        "kernel": "gemm_mfma_kernel" if nv.nvfp4_gemm_form(M, K, N) == 1 else "gemm_rows_kernel"}}
+    if cpu_seconds > 0:
+        leg["cpu_baseline"] = cpu_baseline_gemm(d, cpu_seconds, flops)
+    del pw, c, s, g, out, ws
+    return leg
+
+
+def bench_gemm(args, torch, nv, W, dev):
+    d = GEMM_CONFIGS[args.config](W)
+    steps = max(1, args.steps)
+    leg = gemm_leg(args, torch, nv, dev, d, steps, min(args.warmup, 5),
+                   0 if args.no_cpu_baseline else args.cpu_seconds)
+    res = {"metric": GEMM_METRIC, "value": leg["step_TFLOPs"], "unit": "TFLOP/s", "n_gpus": 1, "steps": steps,
+           "warmup": min(args.warmup, 5), "ms_per_step": leg["step_ms"], "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+           "dtype_note": "NVFP4 operands decoded exactly to fp16, fp16 MFMA products, fp32 accumulation",
+           "data": "synthetic",
+           "config": {k: v for k, v in leg.items() if k not in ("roofline", "cpu_baseline")},
+           "roofline": leg["roofline"]}
+    if "cpu_baseline" in leg:
+        res["cpu_baseline"] = leg["cpu_baseline"]
     return res
 
 
 def cpu_baseline_gemm(d, target_s, flops):
     """The oracle on the host for one quantize + GEMM step of a prefill workload:
-    quantize and decode a row sample of the activations, fp64 GEMM against a
-    column sample of the pre-decoded weight, scaled to the full M x N."""
+    quantize and decode a row sample of the activations (with the whole tensor's
+    maximum), fp64 GEMM against a column sample of the decoded weight, scaled to the
+    full M x N."""
+    from concurrent.futures import ThreadPoolExecutor
     from oracle import gemm as G
     from oracle import nvfp4 as Q
     from workloads import bf16_to_f32
     rows, cols = min(d.M, 512), min(d.N, 4096)
+    threads = cpu_threads()
     wc, ws, wg, _ = Q.quantize(d.w[:cols], np.float32(np.max(np.abs(d.w[:cols]))))
-    w_hat = Q.dequantize(wc, ws, wg)
     t_all, reps = 0.0, 0
-    while t_all < target_s and reps < 1000:
-        t0 = time.perf_counter()
-        c, s, g, _ = Q.quantize(bf16_to_f32(d.x_bits[:rows]))
-        G.gemm_f64(Q.dequantize(c, s, g), w_hat)
-        t_all += time.perf_counter() - t0
-        reps += 1
+    with ThreadPoolExecutor(threads) as pool:
+        w_hat = oracle_dequantize(wc, ws, wg, pool, threads)
+        while t_all < target_s and reps < 1000:
+            t0 = time.perf_counter()
+            x32 = bf16_to_f32(d.x_bits[:rows])
+            c, s, g = oracle_quantize(x32, oracle_amax(x32, pool, threads), pool, threads)
+            G.gemm_f64(oracle_dequantize(c, s, g, pool, threads), w_hat)
+            t_all += time.perf_counter() - t0
+            reps += 1
     per_step = t_all / reps * (d.M / rows) * (d.N / cols)
-    return {"value": round(flops / per_step / 1e12, 6), "unit": "TFLOP/s", "cores": oracle_threads(),
+    return {"value": round(flops / per_step / 1e12, 6), "unit": "TFLOP/s", "cores": max(threads, oracle_threads()),
             "kind": "oracle", "host": host_info(),
             "sample": f"{reps} oracle steps over {rows} of {d.M} rows and {cols} of {d.N} output columns, "
                       f"scaled by {d.M * d.N / (rows * cols):.1f} to the full step; {t_all:.1f} s of CPU time; "
-                      f"fp64 GEMM on the BLAS threads, encode/decode steps single-threaded numpy"}
+                      f"{cpu_kind(threads)}"}
 
 
-def bench_quantize(args, torch, nv, W, dev):
-    rng = np.random.default_rng(0)
-    M, K = 32768, 17408
-    x = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
-    for r0 in range(0, M, 2048):
-        x[r0:r0 + 2048] = to_dev_bf16(torch, W.swiglu_rows(rng, 2048, K), dev)
+def quantize_leg(args, torch, nv, dev, x, x_bits, steps, cpu_seconds):
+    """The standalone activation quantizer over one tensor: dynamic scale (amax pass,
+    its reduction, the encode) as the leg's rate, the static (calibrated) mode too."""
+    M, K = x.shape
     c = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
     s = torch.empty((M, K // 16), dtype=torch.uint8, device=dev)
     g = torch.empty(1, dtype=torch.float32, device=dev)
     ws = nv.Workspace(dev)
     torch.cuda.synchronize()
-    sec, _ = time_region(torch, lambda i: nv.quantize_act(x, None, ws, out=(c, s, g)), args.steps, 3)
+    sec, _ = time_region(torch, lambda i: nv.quantize_act(x, None, ws, out=(c, s, g)), steps, 3)
     nbytes = M * K * (2 + 2 + 9 / 16)      # amax pass reads x, encode pass reads x and writes codes+scales
-    value = nbytes * args.steps / sec / 1e9
-    # static mode (a calibrated amax; here the tensor's own maximum): the encode pass alone
-    amax = (g * 2688.0).contiguous()
-    sec_s, _ = time_region(torch, lambda i: nv.quantize_act(x, amax, ws, out=(c, s, g)), args.steps, 3)
+    value = nbytes * steps / sec / 1e9
+    amax = (g * 2688.0).contiguous()       # static mode with a calibrated maximum (here the tensor's own)
+    sec_s, _ = time_region(torch, lambda i: nv.quantize_act(x, amax, ws, out=(c, s, g)), steps, 3)
     static_bytes = M * K * (2 + 9 / 16)
-    return {"metric": "NVFP4 activation quantize GB/s (dynamic scale), % of MI355X HBM roofline",
-            "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": 3,
-            "ms_per_step": round(sec / args.steps * 1e3, 4), "higher_is_better": True, "scaling": "weak",
-            "vs_baseline": None, "dtype": "f32", "data": "synthetic",
-            "config": {"workload": "down_proj_activation_quantize_m32768_k17408",
-                       "algorithmic_bytes_dynamic": int(nbytes), "algorithmic_bytes_static": int(static_bytes),
-                       "static_ms": round(sec_s / args.steps * 1e3, 4),
-                       "static_GBps": round(static_bytes * args.steps / sec_s / 1e9, 1)},
-            "roofline": {"bound": "hbm", "achieved": round(value, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": round(value / HBM_PEAK_GBS, 4),
-                         "traffic": measured_traffic(QUANT_COUNTERS, QUANT_SOURCES),
-                         "traffic_unit": "bytes per dynamic-mode call (amax pass, its reduction and the encode)",
-                         "algorithmic_bytes_per_call": int(nbytes),
-                         "kernel": "amax_partial_kernel + amax_finalize_kernel + quantize_act_kernel"}}
+    leg = {"workload": f"down_proj_activation_quantize_m{M}_k{K}", "M": M, "K": K, "steps": steps,
+           "dynamic_ms": round(sec / steps * 1e3, 4), "dynamic_GBps": round(value, 1),
+           "algorithmic_bytes_dynamic": int(nbytes), "algorithmic_bytes_static": int(static_bytes),
+           "static_ms": round(sec_s / steps * 1e3, 4),
+           "static_GBps": round(static_bytes * steps / sec_s / 1e9, 1),
+           "roofline": {"bound": "hbm", "achieved": round(value, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": round(value / HBM_PEAK_GBS, 4),
+                        "traffic": measured_traffic(QUANT_COUNTERS, QUANT_SOURCES),
+                        "traffic_unit": "bytes per dynamic-mode call (amax pass, its reduction and the encode)",
+                        "algorithmic_bytes_per_call": int(nbytes),
+                        "kernel": "amax_partial_kernel + amax_finalize_kernel + quantize_act_kernel"}}
+    if cpu_seconds > 0:
+        leg["cpu_baseline"] = cpu_baseline_quantize(x_bits, cpu_seconds, nbytes)
+    del c, s, g, ws, amax
+    return leg
+
+
+def cpu_baseline_quantize(x_bits, target_s, nbytes):
+    """The oracle's quantize of a row sample (with the whole tensor's maximum, and the
+    maximum pass over the sample itself), scaled to the full tensor."""
+    from concurrent.futures import ThreadPoolExecutor
+    from workloads import bf16_to_f32
+    M = x_bits.shape[0]
+    rows = min(M, 256)
+    threads = cpu_threads()
+    amax = np.float32(np.max(np.abs(bf16_to_f32(x_bits[:rows]))))
+    t_all, reps = 0.0, 0
+    with ThreadPoolExecutor(threads) as pool:
+        while t_all < target_s and reps < 1000:
+            t0 = time.perf_counter()
+            x32 = bf16_to_f32(x_bits[:rows])
+            oracle_amax(x32, pool, threads)
+            oracle_quantize(x32, amax, pool, threads)
+            t_all += time.perf_counter() - t0
+            reps += 1
+    per_call = t_all / reps * (M / rows)
+    return {"value": round(nbytes / per_call / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "host": host_info(),
+            "sample": f"{reps} oracle quantize calls over {rows} of {M} rows, scaled by {M / rows:.1f}; "
+                      f"{t_all:.1f} s of CPU time; {cpu_kind(threads)}"}
+
+
+def bench_quantize(args, torch, nv, W, dev):
+    d = W.down_proj()
+    x = to_dev_bf16(torch, d.x_bits, dev)
+    leg = quantize_leg(args, torch, nv, dev, x, d.x_bits, args.steps, 0 if args.no_cpu_baseline else args.cpu_seconds)
+    res = {"metric": "NVFP4 activation quantize GB/s (dynamic scale), % of MI355X HBM roofline",
+           "value": leg["dynamic_GBps"], "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": 3,
+           "ms_per_step": leg["dynamic_ms"], "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": "f32", "data": "synthetic",
+           "config": {k: v for k, v in leg.items() if k not in ("roofline", "cpu_baseline")},
+           "roofline": leg["roofline"]}
+    if "cpu_baseline" in leg:
+        res["cpu_baseline"] = leg["cpu_baseline"]
+    return res
+
+
+def prefill_legs(args, torch, nv, W, dev):
+    """The prefill half of the metric, in the same run as the decode headline: the
+    gate+up (8192 x 5120 x 2 x 17408), GDN in-projection (4096 x 5120 x 12352, six
+    modules) and down projection (32768 x 17408 x 5120) GEMMs, each quantize + GEMM
+    per step, and the standalone quantizer over the down projection's input."""
+    cpu_s = 0 if args.no_cpu_baseline else args.prefill_cpu_seconds
+    legs = {}
+    for name in ("prefill_gate_up", "gdn_in_proj", "down_proj"):
+        print(f"[bench] prefill leg {name}", file=sys.stderr, flush=True)
+        d = GEMM_CONFIGS[name](W)
+        x = to_dev_bf16(torch, d.x_bits, dev)
+        legs[name] = gemm_leg(args, torch, nv, dev, d, args.prefill_steps, 3, cpu_s, x=x)
+        if name == "down_proj":
+            print("[bench] prefill leg down_proj_quantize", file=sys.stderr, flush=True)
+            legs["down_proj_quantize"] = quantize_leg(args, torch, nv, dev, x, d.x_bits, args.prefill_steps, cpu_s)
+        del d, x
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+    return legs
 
 
 if __name__ == "__main__":

@@ -49,6 +49,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--no-prefill", action="store_true", help="decode only (no prefill legs in the default run)")
+    ap.add_argument("--no-gpu-state", action="store_true",
+                    help="skip the amd-smi / rocm-smi power and clock snapshot (e.g. under a profiler)")
     ap.add_argument("--prefill-steps", type=int, default=20, help="timed steps of each prefill leg")
     ap.add_argument("--prefill-cpu-seconds", type=float, default=5.0,
                     help="target CPU time of each prefill leg's oracle sample")
@@ -57,6 +59,8 @@ def parse():
 
 def main():
     args = parse()
+    global GPU_STATE
+    GPU_STATE = not args.no_gpu_state
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(how the layer would shard is a design, not code); run with --gpus 1", file=sys.stderr)
@@ -415,10 +419,16 @@ def oracle_threads():
     return cpu_threads()
 
 
+GPU_STATE = True
+
+
 def gpu_state():
     """GPU power and clocks as amd-smi (else rocm-smi) reports them when called; None
-    where neither tool answers.  amd-smi's readings trail the load by about a second,
-    so a snapshot taken right after a timed region reflects that region."""
+    where neither tool answers or --no-gpu-state is given.  amd-smi's readings trail
+    the load by about a second, so a snapshot taken right after a timed region
+    reflects that region."""
+    if not GPU_STATE:
+        return None
     import subprocess
     try:
         r = subprocess.run(["amd-smi", "metric", "--power", "--clock", "--json"], capture_output=True,
@@ -445,9 +455,9 @@ def gpu_state():
 
 # ---------------------------------------------------------------------------------------
 DECODE_COUNTERS = "linear_decode_kernel_decode_k5120_n12288_counters.md"
-DECODE_SOURCES = ("gemm_skinny.hip", "quant_device.hpp", "common.hpp")
+DECODE_SOURCES = ("gemm_skinny.hip", "quant_device.hpp", "common.hpp", "launch.hpp")
 QUANT_COUNTERS = "quantize_act_kernel_down_proj_activation_m32768_k17408.md"
-QUANT_SOURCES = ("quantize.hip", "quant_device.hpp", "common.hpp")
+QUANT_SOURCES = ("quantize.hip", "quant_device.hpp", "common.hpp", "launch.hpp")
 
 
 def bench_decode(args, torch, nv, W, dev):

@@ -24,7 +24,10 @@
 //    flight per thread per trip: 188 us against 220 us with one) writes one
 //    value per workgroup into the workspace, a one-workgroup kernel reduces
 //    them to the maximum (also in the workspace), and the encoder reads it like
-//    a calibrated one (exact, order-independent, no atomics, no memset);
+//    a calibrated one (exact, order-independent, no atomics, no memset); with
+//    at most kFuseParts partial maxima (tensors up to ~2M elements) every
+//    encode workgroup reduces them itself instead, one launch fewer (with the
+//    1024 partials of a prefill-sized tensor that measured slower);
 //  * small tensors (decode-sized activations) use a single launch in which
 //    every 1024-thread workgroup recomputes the whole-tensor maximum from L2
 //    with all of its loads in flight at once.
@@ -39,6 +42,7 @@ namespace nvfp4 {
 constexpr int kQThreads = 256;
 constexpr int kAmaxLoads = 4;                // amax pass: 16-byte loads in flight per thread
 constexpr int64_t kMaxEncodeGrid = 1 << 20;  // encoder workgroups (blocks beyond loop)
+constexpr int kFuseParts = 64;               // partial maxima an encode workgroup reduces itself
 
 // Encode the bf16 block (m, b) of x.
 __device__ __forceinline__ void encode_block_at(const uint16_t* __restrict__ x, int64_t ldx, int K, int64_t m,
@@ -95,15 +99,25 @@ __global__ __launch_bounds__(kQThreads) void amax_finalize_kernel(const uint32_t
   if (threadIdx.x == 0) *amax_out = __uint_as_float(m << 16);
 }
 
-// Encode with the tensor maximum *amax (calibrated, or the dynamic one the
-// two kernels above left in the workspace).
+// Encode with the tensor maximum: *amax (calibrated, or the dynamic one the two
+// kernels above left in the workspace), or, with `partial`, the largest of the
+// nparts partial maxima (bf16 bit patterns), reduced by every workgroup.
 __global__ __launch_bounds__(kQThreads) void quantize_act_kernel(
     const uint16_t* __restrict__ x, int64_t M, int K, int64_t ldx, const float* __restrict__ amax_in,
-    uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, float* __restrict__ g_dec_out) {
+    const uint32_t* __restrict__ partial, int nparts, uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
+    float* __restrict__ g_dec_out) {
   __shared__ float rtab[128];
+  __shared__ uint32_t red[kQThreads / 64];
   fill_rcp_table(rtab);
-  const float amax = *amax_in;
-  __syncthreads();
+  float amax;
+  if (partial) {
+    uint32_t m = 0;
+    for (int i = threadIdx.x; i < nparts; i += blockDim.x) m = max(m, partial[i]);
+    amax = __uint_as_float(block_reduce_max(m, red) << 16);   // its barriers also publish rtab
+  } else {
+    amax = *amax_in;
+    __syncthreads();
+  }
   const EncCtx cx = make_ctx(amax, rtab);
   if (blockIdx.x == 0 && threadIdx.x == 0) *g_dec_out = amax / kGMax;
 
@@ -189,7 +203,8 @@ hipError_t launch_quantize_act(const uint16_t* x, int64_t M, int64_t K, int64_t 
   // One block per thread (grid-stride beyond kMaxEncodeGrid workgroups).
   const int grid = (int)std::min<int64_t>((blocks + kQThreads - 1) / kQThreads, kMaxEncodeGrid);
   if (amax_in) {
-    quantize_act_kernel<<<grid, kQThreads, 0, stream>>>(x, M, (int)K, ldx, amax_in, codes, scales, g_dec_out);
+    quantize_act_kernel<<<grid, kQThreads, 0, stream>>>(x, M, (int)K, ldx, amax_in, nullptr, 0, codes, scales,
+                                                        g_dec_out);
   } else if (M * K <= kSmallElems) {
     const int grid = (int)((blocks + kSmallThreads - 1) / kSmallThreads);
     quantize_act_small_kernel<<<grid, kSmallThreads, 0, stream>>>(x, (int)M, (int)K, ldx, 1.0f / (float)(K / 8),
@@ -197,11 +212,19 @@ hipError_t launch_quantize_act(const uint16_t* x, int64_t M, int64_t K, int64_t 
   } else {
     uint32_t* partial = static_cast<uint32_t*>(workspace);
     const int64_t chunks = M * (K / 8);
-    const int pgrid = (int)std::max<int64_t>(1, std::min<int64_t>(kPartials, chunks / (kQThreads * 16)));
+    int pgrid = (int)std::max<int64_t>(1, std::min<int64_t>(kPartials, chunks / (kQThreads * 16)));
+    // mid-size tensors: at most kFuseParts partials, each workgroup two chunks per thread
+    if (pgrid <= kFuseParts) pgrid = (int)std::max<int64_t>(1, std::min<int64_t>(kFuseParts, chunks / (kQThreads * 2)));
     float* amax = reinterpret_cast<float*>(partial + kPartials);
     amax_partial_kernel<<<pgrid, kQThreads, 0, stream>>>(x, M, (int)K, ldx, partial);
-    amax_finalize_kernel<<<1, kQThreads, 0, stream>>>(partial, pgrid, amax);
-    quantize_act_kernel<<<grid, kQThreads, 0, stream>>>(x, M, (int)K, ldx, amax, codes, scales, g_dec_out);
+    if (pgrid <= kFuseParts) {
+      quantize_act_kernel<<<grid, kQThreads, 0, stream>>>(x, M, (int)K, ldx, nullptr, partial, pgrid, codes, scales,
+                                                          g_dec_out);
+    } else {
+      amax_finalize_kernel<<<1, kQThreads, 0, stream>>>(partial, pgrid, amax);
+      quantize_act_kernel<<<grid, kQThreads, 0, stream>>>(x, M, (int)K, ldx, amax, nullptr, 0, codes, scales,
+                                                          g_dec_out);
+    }
   }
   return hipGetLastError();
 }

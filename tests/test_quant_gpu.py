@@ -39,6 +39,8 @@ def test_decode_workload_activations(M):
     (1, 16, "normal"), (3, 48, "student_t"), (17, 272, "normal"), (100, 5136, "student_t"),
     (257, 1040, "uniform"), (64, 4112, "normal"),       # above the single-launch size: two-pass amax
     (700, 400, "student_t"),
+    # 64 partial maxima, reduced inside the encode kernel / 65, reduced by their own kernel
+    (1280, 1648, "student_t"), (1293, 1648, "student_t"),
 ])
 def test_ragged_shapes_dynamic(M, K, dist):
     check(random_act(M * 7 + K, M, K, dist), None, f"ragged {M}x{K}")

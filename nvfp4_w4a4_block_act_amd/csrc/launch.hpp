@@ -26,7 +26,7 @@ constexpr int kCUs = 256;         // compute units of a gfx950 (MI355X) device
 // Host-side sizes shared by the launchers and the dispatch code.
 constexpr int kPartials = 1024;             // amax workgroups of the two-pass activation quantizer
 constexpr int64_t kSmallElems = 1 << 17;    // single-launch activation quantizer up to 128K elements
-constexpr int kSegParts = 64;               // amax workgroups per weight segment (packer)
+constexpr int kSegParts = 256;              // amax workgroups per weight segment (packer)
 constexpr int kDecMaxM = 16;                // rows of the one-launch decode layer
 constexpr size_t kScratchBytes = kPartials * sizeof(uint32_t) + 16;   // nvfp4_linear_noalloc's scratch
 constexpr int kMaxDevices = 64;             // GPUs whose scratch address is cached

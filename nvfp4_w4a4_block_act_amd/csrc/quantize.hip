@@ -383,20 +383,38 @@ hipError_t launch_convert_sweep(int op, uint32_t first, int64_t n, uint8_t* out,
 }
 
 // ---- weights: per-module encode into the tiled layout ----------------------------
-// partial[s * kSegParts + p] = max |w| bits over a slice of segment s's rows.
+// partial[s * kSegParts + p] = max |w| bits over rows p, p + kSegParts, ... of
+// segment s: workgroup p walks its rows, its threads the row's 16-byte pieces
+// (four loads in flight per trip) when every row starts 16-byte aligned
+// (ldw % 4 == 0), else single floats.
+static_assert(kSegParts == kQThreads, "the packer reduces one partial per thread");
 __global__ __launch_bounds__(kQThreads) void seg_amax_kernel(const float* __restrict__ w, int K, int64_t ldw,
                                                              SegTable st, uint32_t* __restrict__ partial) {
   __shared__ uint32_t red[kQThreads / 64];
   const int s = blockIdx.y;
   const int64_t r0 = (s == 0) ? 0 : st.end[s - 1];
   const int64_t rows = st.end[s] - r0;
-  const int64_t total = rows * K;
+  const bool vec = (ldw % 4) == 0;
   uint32_t m = 0;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
-       i += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t r = i / K;
-    const int64_t k = i - r * K;
-    m = max(m, __float_as_uint(w[(r0 + r) * ldw + k]) & 0x7FFFFFFFu);
+  for (int64_t r = blockIdx.x; r < rows; r += gridDim.x) {
+    const float* row = w + (r0 + r) * ldw;
+    if (vec) {
+      const int k4 = K / 4;
+      for (int j0 = threadIdx.x; j0 < k4; j0 += 4 * kQThreads) {
+        float4 v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int j = j0 + u * kQThreads;
+          v[u] = j < k4 ? reinterpret_cast<const float4*>(row)[j] : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          m = max(m, max(max(__float_as_uint(v[u].x) & 0x7FFFFFFFu, __float_as_uint(v[u].y) & 0x7FFFFFFFu),
+                         max(__float_as_uint(v[u].z) & 0x7FFFFFFFu, __float_as_uint(v[u].w) & 0x7FFFFFFFu)));
+      }
+    } else {
+      for (int k = threadIdx.x; k < K; k += kQThreads) m = max(m, __float_as_uint(row[k]) & 0x7FFFFFFFu);
+    }
   }
   const uint32_t r = block_reduce_max(m, red);
   if (threadIdx.x == 0) partial[s * kSegParts + blockIdx.x] = r;
@@ -412,12 +430,13 @@ __global__ __launch_bounds__(kQThreads) void pack_weight_kernel(
     const uint32_t* __restrict__ partial, uint8_t* __restrict__ w_codes, uint8_t* __restrict__ w_scales,
     float* __restrict__ w_g_dec) {
   __shared__ float s_genc[NVFP4_MAX_SEGMENTS];
-  if ((int)threadIdx.x < st.nseg) {
-    uint32_t m = 0;
-    for (int p = 0; p < kSegParts; ++p) m = max(m, partial[threadIdx.x * kSegParts + p]);
-    const float amax = __uint_as_float(m);
-    s_genc[threadIdx.x] = g_enc_of(amax);
-    if (blockIdx.x == 0) w_g_dec[threadIdx.x] = amax / kGMax;
+  __shared__ uint32_t red[kQThreads / 64];
+  for (int s = 0; s < st.nseg; ++s) {                // each segment's maximum from its partials
+    const float amax = __uint_as_float(block_reduce_max(partial[s * kSegParts + threadIdx.x], red));
+    if (threadIdx.x == 0) {
+      s_genc[s] = g_enc_of(amax);
+      if (blockIdx.x == 0) w_g_dec[s] = amax / kGMax;
+    }
   }
   __syncthreads();
   const int nbk = Kp / kBlock;

@@ -53,6 +53,30 @@ def test_pack_ragged(N, K, segs):
     check_pack(w, segs, "ragged")
 
 
+@pytest.mark.parametrize("pad", [2, 8])
+def test_pack_leading_dimension(pad):
+    """Weight rows at a stride of K + pad floats (pad 2: rows not 16-byte aligned, the
+    amax pass reads single floats; pad 8: 16-byte pieces) pack like the dense tensor,
+    each segment's maximum taken over its rows only (the largest value sits in the pad
+    of another segment's rows and must be ignored)."""
+    rng = np.random.default_rng(70 + pad)
+    N, K = 300, 1040
+    segs = [(0, 100), (100, 300)]
+    w = np.concatenate([(0.02 * (1 + 5 * i) * rng.standard_normal((e - b, K))).astype(np.float32)
+                        for i, (b, e) in enumerate(segs)])
+    full = np.zeros((N, K + pad), np.float32)
+    full[:, :K] = w
+    full[:, K:] = 1.0e3                                   # outside the tensor
+    say(f"[pack] leading dimension K + {pad}")
+    dev = torch.from_numpy(full).to(DEV)
+    pw = nv.pack_weight(dev[:, :K], segs)
+    c, s = nv.weight_to_canonical(pw)
+    torch.cuda.synchronize()
+    oc, os_, og = Q.quantize_segments(w, segs)
+    assert np.array_equal(c.cpu().numpy(), oc) and np.array_equal(s.cpu().numpy(), os_)
+    assert pw.g_dec.cpu().numpy().tobytes() == og.tobytes()
+
+
 def test_pack_layout_is_the_documented_tiling():
     """Tiled buffer = canonical codes/scales re-blocked into 16-row x 128-k chunks, strip major;
     inside a chunk the 16 code bytes (2 scale bytes) of row n, k group g sit at slot g * 16 + n."""

@@ -39,7 +39,7 @@ bool gemm_prefers_skinny(int64_t M, int64_t K, int64_t N) {
 }
 
 bool linear_decode_fits(int64_t M, int64_t K) {
-  return M >= 1 && M <= kDecMaxM && K >= kBlock && decode_tiles_per_wave(M, K) > 0;
+  return M >= 1 && M <= decode_max_rows(K) && K >= kBlock;
 }
 
 }  // namespace nvfp4

@@ -8,9 +8,10 @@
 //
 // Design (gfx950):
 //  * each weight byte is read from HBM exactly once: 0.5625 B per weight
-//    (codes + scales); a workgroup of eight waves owns S strips of 16 output
-//    columns (S = 1..3 chosen per N by pick_strips: 3 for N = 12288, i.e. 256
-//    workgroups, one per CU), and its waves split the K tiles of those strips
+//    (codes + scales); a workgroup of eight waves (sixteen for some long-K
+//    shapes, as stream_waves sets) owns S strips of 16 output columns (S = 1..3
+//    chosen per N by skinny_strips: 3 for N = 12288, i.e. 256 workgroups, one
+//    per CU), and its waves split the K tiles of those strips
 //    (split-K inside the workgroup, reduced through LDS); each wave keeps two
 //    batches (one k tile of the S strips each) in flight, requesting batch
 //    u + 2 after the MFMAs of batch u;
@@ -27,6 +28,7 @@
 //    the same launch (linear_decode_kernel below).
 #include <algorithm>
 #include <cstdint>
+#include <type_traits>
 
 #include "common.hpp"
 #include "quant_device.hpp"
@@ -167,10 +169,11 @@ __device__ __forceinline__ void strip_pointers(const uint8_t* w_codes, const uin
 // Requesting every batch up front instead lets the memory system accept the
 // loads first come, first served: the first waves of a workgroup get all their
 // data early, the last wave gets all of it at the end of the stream and then
-// has its whole decode and MFMA work left (about 1 us of tail).  Batches have no
-// branches (tiles past the end are clamped and their activation scales zeroed),
-// so the waits before each batch's MFMAs stay progressive.
-template <int S, int NW, int U, bool AL16>
+// has its whole decode and MFMA work left (about 1 us of tail).  Every load is
+// unconditional (tiles past the end are clamped), so the waits before each
+// batch's MFMAs stay progressive; the clamped tiles of the last iteration skip
+// their decode and MFMAs.
+template <int S, int NW, int U, bool AL16, bool TAIL>
 __global__ __launch_bounds__(64 * NW) void gemm_skinny_kernel(
     const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales, const float* __restrict__ a_g,
     int M, int K, const uint8_t* __restrict__ w_codes, const uint8_t* __restrict__ w_scales, int N,
@@ -202,37 +205,82 @@ __global__ __launch_bounds__(64 * NW) void gemm_skinny_kernel(
 #pragma unroll
   for (int s = 0; s < S; ++s) acc[s] = float4_t{0.f, 0.f, 0.f, 0.f};
 
-  for (int t0 = wave; t0 < full; t0 += NW * U) {
-    // activation fragments first (a few hundred bytes, L2-resident after the
-    // first workgroups), then the first two weight batches
-    uint4 av[U];
-    uint32_t asc[U];
+  if constexpr (!TAIL) {
+    // the general loop: tiles past the end are clamped and decoded with zero
+    // scales; the fastest form where every wave's tiles fill whole iterations
+    for (int t0 = wave; t0 < full; t0 += NW * U) {
+      // activation fragments first (a few hundred bytes, L2-resident after the
+      // first workgroups), then the first two weight batches
+      uint4 av[U];
+      uint32_t asc[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) load_a_full<AL16>(ac, as, min(t0 + u * NW, full - 1), av[u], asc[u]);
-    uint4 wv[U][S];
-    uint32_t wsc[U][S];
-    auto request = [&](int u) {
-      const int t = min(t0 + u * NW, full - 1);
+      for (int u = 0; u < U; ++u) load_a_full<AL16>(ac, as, min(t0 + u * NW, full - 1), av[u], asc[u]);
+      uint4 wv[U][S];
+      uint32_t wsc[U][S];
+      auto request = [&](int u) {
+        const int t = min(t0 + u * NW, full - 1);
 #pragma unroll
-      for (int s = 0; s < S; ++s) {
-        wv[u][s] = *reinterpret_cast<const uint4*>(wc[s] + (int64_t)t * kChunkCodes);
-        wsc[u][s] = *reinterpret_cast<const uint16_t*>(ws[s] + (int64_t)t * kChunkScales);
+        for (int s = 0; s < S; ++s) {
+          wv[u][s] = *reinterpret_cast<const uint4*>(wc[s] + (int64_t)t * kChunkCodes);
+          wsc[u][s] = *reinterpret_cast<const uint16_t*>(ws[s] + (int64_t)t * kChunkScales);
+        }
+      };
+#pragma unroll
+      for (int u = 0; u < kDepth; ++u) request(u);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const uint32_t live = (t0 + u * NW < full) ? amask : 0u;
+        half8_t A[4];
+        decode_a(av[u], asc[u], live, A);
+#pragma unroll
+        for (int s = 0; s < S; ++s) tile_mfma(A, wv[u][s], wsc[u][s], acc[s]);
+        __builtin_amdgcn_sched_barrier(0);
+        if (u + kDepth < U) request(u + kDepth);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  } else {
+    // some wave's last iteration is partial: that iteration, peeled, skips the
+    // clamped tiles' decode and MFMAs (a uniform branch, kept out of the main
+    // loop so that its waits stay progressive)
+    auto iteration = [&](int t0, auto guarded) {
+      uint4 av[U];
+      uint32_t asc[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) load_a_full<AL16>(ac, as, min(t0 + u * NW, full - 1), av[u], asc[u]);
+      __builtin_amdgcn_sched_barrier(0);
+      uint4 wv[U][S];
+      uint32_t wsc[U][S];
+      auto request = [&](int u) {
+        const int t = min(t0 + u * NW, full - 1);
+#pragma unroll
+        for (int s = 0; s < S; ++s) {
+          wv[u][s] = *reinterpret_cast<const uint4*>(wc[s] + (int64_t)t * kChunkCodes);
+          wsc[u][s] = *reinterpret_cast<const uint16_t*>(ws[s] + (int64_t)t * kChunkScales);
+        }
+      };
+#pragma unroll
+      for (int u = 0; u < kDepth; ++u) {            // in batch order, so that the waits stay progressive
+        request(u);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (!decltype(guarded)::value || t0 + u * NW < full) {
+          half8_t A[4];
+          decode_a(av[u], asc[u], amask, A);
+#pragma unroll
+          for (int s = 0; s < S; ++s) tile_mfma(A, wv[u][s], wsc[u][s], acc[s]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (u + kDepth < U) request(u + kDepth);
+        __builtin_amdgcn_sched_barrier(0);
       }
     };
-#pragma unroll
-    for (int u = 0; u < kDepth; ++u) request(u);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const uint32_t live = (t0 + u * NW < full) ? amask : 0u;
-      half8_t A[4];
-      decode_a(av[u], asc[u], live, A);
-#pragma unroll
-      for (int s = 0; s < S; ++s) tile_mfma(A, wv[u][s], wsc[u][s], acc[s]);
-      __builtin_amdgcn_sched_barrier(0);
-      if (u + kDepth < U) request(u + kDepth);
-      __builtin_amdgcn_sched_barrier(0);
-    }
+    int t0 = wave;
+    for (; t0 + (U - 1) * NW < full; t0 += NW * U) iteration(t0, std::false_type{});
+    if (t0 < full) iteration(t0, std::true_type{});
   }
   if (full < tiles && wave == full % NW) {           // ragged last tile
     const int t = full;
@@ -255,22 +303,21 @@ __global__ __launch_bounds__(64 * NW) void gemm_skinny_kernel(
 // Workgroup b takes strip group b % groups of the block of 16 MT rows
 // b / groups: each weight fragment is decoded once and multiplied by the MT
 // row tiles' activations, so the packed weight is streamed once per 16 MT rows.
-// Every accumulator sees the same MFMA sequence as in gemm_skinny_kernel, so
-// each row's result is bit-identical to that kernel's.  Used by nvfp4_gemm where
-// too few 256 x 256 tiles would fill the chip for the MFMA GEMM, and for the
-// MFMA GEMM's ragged last tile column.
+// Used by nvfp4_gemm where too few 256 x 256 tiles would fill the chip for the
+// MFMA GEMM.  The kernel reproduces the summation order of gemm_skinny_kernel
+// with NW * VW waves on NW waves: wave w keeps VW accumulator sets, set j
+// playing wave w + NW j (tile t goes to set (t / NW) % VW, so each set sees its
+// tiles in the same ascending order), and the cross-wave sums of the sets are
+// chained in wave order in each thread's registers.  Every accumulator thus
+// sees the same MFMA sequence, and every output the same fp32 additions, as in
+// the skinny kernel, so each row's result is bit-identical to that kernel's,
+// while the waves stream the weight in the same order as with one set (the
+// 64-row instances would not fit in the 128 VGPRs a lane has at sixteen waves).
 template <int S, int NW, int MT>
-__device__ __forceinline__ void reduce_store_rows(const float4_t (&acc)[S][MT], float (&red)[NW][S][MT][4][64],
-                                                  float (&scol)[S * kStrip], float wgv, int strip0, int rows,
-                                                  int N, const SegTable& st, float ag, float* __restrict__ out,
-                                                  int64_t ldo) {
-  static_assert(S * kStrip <= 64, "one lane of wave 0 per column");
+__device__ __forceinline__ void reduce_rows_set(const float4_t (&acc)[S][MT], float (&red)[NW][S][MT][4][64],
+                                                 float (&part)[(16 * MT * S * kStrip + 64 * NW - 1) / (64 * NW)],
+                                                 int rows) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  if (wave == 0) {
-    const int n = min(strip0 * kStrip + min(lane, S * kStrip - 1), N - 1);
-    const float wc = __shfl(wgv, seg_of(st, n), 64);
-    if (lane < S * kStrip) scol[lane] = wc;
-  }
 #pragma unroll
   for (int s = 0; s < S; ++s)
 #pragma unroll
@@ -278,26 +325,31 @@ __device__ __forceinline__ void reduce_store_rows(const float4_t (&acc)[S][MT], 
 #pragma unroll
       for (int i = 0; i < 4; ++i) red[wave][s][mt][i][lane] = acc[s][mt][i];
   __syncthreads();
-  for (int e = threadIdx.x; e < rows * S * kStrip; e += 64 * NW) {
-    const int row = e / (S * kStrip), c = e % (S * kStrip);
-    const int n = strip0 * kStrip + c;
-    if (n >= N) continue;
-    const int mt = row >> 4, rr = row & 15;
-    const int s = c / kStrip, l = (rr >> 2) * kStrip + c % kStrip;
-    float v = 0.f;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) v += red[w][s][mt][rr & 3][l];
-    out[(int64_t)row * ldo + n] = v * (ag * scol[c]);
+  for (int i = 0; i < (16 * MT * S * kStrip + 64 * NW - 1) / (64 * NW); ++i) {
+    const int e = threadIdx.x + i * 64 * NW;
+    if (e < rows * S * kStrip) {
+      const int row = e / (S * kStrip), c = e % (S * kStrip);
+      const int mt = row >> 4, rr = row & 15;
+      const int s = c / kStrip, l = (rr >> 2) * kStrip + c % kStrip;
+      float v = part[i];
+#pragma unroll
+      for (int w = 0; w < NW; ++w) v += red[w][s][mt][rr & 3][l];
+      part[i] = v;
+    }
   }
 }
 
-template <int S, int NW, int U, bool AL16, int MT>
+template <int S, int NW, int VW, int U, bool AL16, int MT>
 __global__ __launch_bounds__(64 * NW) void gemm_rows_kernel(
     const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales, const float* __restrict__ a_g,
     int M, int K, const uint8_t* __restrict__ w_codes, const uint8_t* __restrict__ w_scales, int N,
     SegTable st, const float* __restrict__ w_g, float* __restrict__ out, int64_t ldo) {
   constexpr int kDepth = 2;
+  constexpr int kPer = (16 * MT * S * kStrip + 64 * NW - 1) / (64 * NW);
   static_assert(U >= kDepth, "pipeline depth");
+  static_assert(U % VW == 0, "tile u of an outer iteration belongs to accumulator set u % VW");
+  static_assert(S * kStrip <= 64, "one lane of wave 0 per column");
   __shared__ float red[NW][S][MT][4][64];
   __shared__ float scol[S * kStrip];
   const float ag = *a_g;
@@ -330,16 +382,47 @@ __global__ __launch_bounds__(64 * NW) void gemm_rows_kernel(
   strip_pointers<S>(w_codes, w_scales, strip0, nstrips, tiles, lane, wc, ws);
   const float wgv = load_segment_scale(w_g, st);
 
-  float4_t acc[S][MT];
+  // accumulator set j of wave w plays wave w + NW j of the NW * VW-wave order:
+  // tile t goes to set (t / NW) % VW
+  float4_t acc[VW][S][MT];
 #pragma unroll
-  for (int s = 0; s < S; ++s)
+  for (int j = 0; j < VW; ++j)
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) acc[s][mt] = float4_t{0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < S; ++s)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) acc[j][s][mt] = float4_t{0.f, 0.f, 0.f, 0.f};
 
   // one batch: the weight fragments of the S strips, decoded once, against the
-  // MT row tiles' activation fragments (same MFMA order as tile_mfma)
-  auto batch = [&](const uint4 (&av)[MT], const uint32_t (&asc)[MT], bool live, const uint4 (&w)[S],
-                   const uint32_t (&wsv)[S]) {
+  // MT row tiles' activation fragments (same MFMA order as tile_mfma).  With two
+  // accumulator sets and more row tiles than strips, the strips' fragments are
+  // decoded first and the row tiles one at a time, which holds fewer operands
+  // in registers; every accumulator sees the same MFMA sequence either way.
+  auto batch = [&](float4_t (&c)[S][MT], const uint4 (&av)[MT], const uint32_t (&asc)[MT], bool live,
+                   const uint4 (&w)[S], const uint32_t (&wsv)[S]) {
+    if constexpr (VW > 1 && MT > S) {
+      half8_t B[S][4];
+#pragma unroll
+      for (int s = 0; s < S; ++s) {
+        const half2_t s0 = scale_pair(wsv[s] & 0xFF), s1 = scale_pair(wsv[s] >> 8);
+        B[s][0] = decode8(w[s].x, s0);
+        B[s][1] = decode8(w[s].y, s0);
+        B[s][2] = decode8(w[s].z, s1);
+        B[s][3] = decode8(w[s].w, s1);
+      }
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        half8_t A[4];
+        decode_a(av[mt], asc[mt], live ? amask[mt] : 0u, A);
+#pragma unroll
+        for (int s = 0; s < S; ++s) {
+          c[s][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[0], B[s][0], c[s][mt], 0, 0, 0);
+          c[s][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[1], B[s][1], c[s][mt], 0, 0, 0);
+          c[s][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[2], B[s][2], c[s][mt], 0, 0, 0);
+          c[s][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[3], B[s][3], c[s][mt], 0, 0, 0);
+        }
+      }
+      return;
+    }
     half8_t A[MT][4];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) decode_a(av[mt], asc[mt], live ? amask[mt] : 0u, A[mt]);
@@ -350,15 +433,18 @@ __global__ __launch_bounds__(64 * NW) void gemm_rows_kernel(
       const half8_t B2 = decode8(w[s].z, s1), B3 = decode8(w[s].w, s1);
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        acc[s][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[mt][0], B0, acc[s][mt], 0, 0, 0);
-        acc[s][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[mt][1], B1, acc[s][mt], 0, 0, 0);
-        acc[s][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[mt][2], B2, acc[s][mt], 0, 0, 0);
-        acc[s][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[mt][3], B3, acc[s][mt], 0, 0, 0);
+        c[s][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[mt][0], B0, c[s][mt], 0, 0, 0);
+        c[s][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[mt][1], B1, c[s][mt], 0, 0, 0);
+        c[s][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[mt][2], B2, c[s][mt], 0, 0, 0);
+        c[s][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[mt][3], B3, c[s][mt], 0, 0, 0);
       }
     }
   };
 
-  for (int t0 = wave; t0 < full; t0 += NW * U) {
+  // U tiles per iteration; the last iteration, whose tiles past the end are
+  // clamped, skips their decode and MFMAs (a uniform branch, kept out of the
+  // main loop so that its waits stay progressive)
+  auto iteration = [&](int t0, auto guarded) {
     uint4 av[U][MT];
     uint32_t asc[U][MT];
     uint4 wv[U][S];
@@ -374,16 +460,21 @@ __global__ __launch_bounds__(64 * NW) void gemm_rows_kernel(
       for (int mt = 0; mt < MT; ++mt) load_a_full<AL16>(ac[mt], as[mt], t, av[u][mt], asc[u][mt]);
     };
 #pragma unroll
-    for (int u = 0; u < kDepth; ++u) request(u);
-    __builtin_amdgcn_sched_barrier(0);
+    for (int u = 0; u < kDepth; ++u) {              // in batch order, so that the waits stay progressive
+      request(u);
+      __builtin_amdgcn_sched_barrier(0);
+    }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      batch(av[u], asc[u], t0 + u * NW < full, wv[u], wsc[u]);
+      if (!decltype(guarded)::value || t0 + u * NW < full) batch(acc[u % VW], av[u], asc[u], true, wv[u], wsc[u]);
       __builtin_amdgcn_sched_barrier(0);
       if (u + kDepth < U) request(u + kDepth);
       __builtin_amdgcn_sched_barrier(0);
     }
-  }
+  };
+  int t0 = wave;
+  for (; t0 + (U - 1) * NW < full; t0 += NW * U) iteration(t0, std::false_type{});
+  if (t0 < full) iteration(t0, std::true_type{});
   if (full < tiles && wave == full % NW) {           // ragged last tile
     const int t = full;
     uint4 av[MT], w[S];
@@ -395,14 +486,42 @@ __global__ __launch_bounds__(64 * NW) void gemm_rows_kernel(
       w[s] = *reinterpret_cast<const uint4*>(wc[s] + (int64_t)t * kChunkCodes);
       wsv[s] = *reinterpret_cast<const uint16_t*>(ws[s] + (int64_t)t * kChunkScales);
     }
-    batch(av, asc, true, w, wsv);
+    if (VW == 1 || (t / NW) % VW == 0)
+      batch(acc[0], av, asc, true, w, wsv);
+    else
+      batch(acc[VW - 1], av, asc, true, w, wsv);
   }
-  reduce_store_rows<S, NW, MT>(acc, red, scol, wgv, strip0, rows, N, st, ag, out + row0 * ldo, ldo);
+
+  if (wave == 0) {                                   // column scales, read after the first barrier
+    const int n = min(strip0 * kStrip + min(lane, S * kStrip - 1), N - 1);
+    const float wcol = __shfl(wgv, seg_of(st, n), 64);
+    if (lane < S * kStrip) scol[lane] = wcol;
+  }
+  // cross-wave sums in the order of the NW * VW waves, chained over the sets
+  float part[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) part[i] = 0.f;
+#pragma unroll
+  for (int j = 0; j < VW; ++j) {
+    if (j > 0) __syncthreads();                      // the previous set's sums are read
+    reduce_rows_set<S, NW, MT>(acc[j], red, part, rows);
+  }
+  float* const o = out + row0 * ldo;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int e = threadIdx.x + i * 64 * NW;
+    if (e < rows * S * kStrip) {
+      const int row = e / (S * kStrip), c = e % (S * kStrip);
+      const int n = strip0 * kStrip + c;
+      if (n < N) o[(int64_t)row * ldo + n] = part[i] * (ag * scol[c]);
+    }
+  }
 }
 
-// ---- decode-form linear layer in one launch (M <= 16, K <= 5120).
-// The activation quantizer and the skinny GEMM above in a single kernel: the
-// tensor is at most 16 x 5120 bf16, and a separate quantizer launch costs about
+// ---- decode-form linear layer in one launch (M <= 16 at K <= 5120, fewer rows
+// for longer K).  The activation quantizer and the skinny GEMM above in a single
+// kernel: the tensor is at most 81920 bf16 values (16 x 5120, 8 x 10240 or
+// 4 x 20480), and a separate quantizer launch costs about
 // 5 us of launch and latency for a few KB of work on this chip.  Wave w of a
 // workgroup multiplies only k tiles w, w + NW, ..., so it needs the quantized
 // activations of those tiles alone: each wave loads and encodes exactly those
@@ -432,7 +551,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_rows_kernel(
 // bit-identical to the activation quantizer followed by the skinny GEMM.
 constexpr int kDecRowBytes = kTileK / 2 + 16;   // LDS bytes per row of one tile (padded)
 
-template <int S, int NW, int U, int MAXM, bool BAL>
+template <int S, int NW, int U, int MAXM, bool BAL, bool TAIL>
 __global__ __launch_bounds__(64 * NW) void linear_decode_kernel(
     const uint16_t* __restrict__ x, int64_t ldx, const float* __restrict__ amax_in, uint8_t* __restrict__ a_codes,
     uint8_t* __restrict__ a_scales, float* __restrict__ a_g, int M, int K, const uint8_t* __restrict__ w_codes,
@@ -562,17 +681,31 @@ __global__ __launch_bounds__(64 * NW) void linear_decode_kernel(
   for (int s = 0; s < S; ++s) acc[s] = float4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    const int t = min(wave + NW * u, tiles - 1);
-    const int k0 = t * kTileK + 32 * g;
-    const bool live0 = (wave + NW * u < tiles) && (r < M) && (k0 < K);
-    const bool live1 = live0 && (k0 + kBlock < K);
-    const uint4 cv = *reinterpret_cast<const uint4*>(&lcodes[wave][arow * U + u][16 * g]);
-    const uint32_t s2 = *reinterpret_cast<const uint16_t*>(&lscales[wave][arow * U + u][2 * g]);
-    const uint32_t sc = s2 & ((live0 ? 0xFFu : 0u) | (live1 ? 0xFF00u : 0u));
-    half8_t A[4];
-    decode_a(cv, sc, 0xFFFFu, A);
+    if constexpr (!TAIL) {                           // every wave has U tiles
+      const int t = min(wave + NW * u, tiles - 1);
+      const int k0 = t * kTileK + 32 * g;
+      const bool live0 = (wave + NW * u < tiles) && (r < M) && (k0 < K);
+      const bool live1 = live0 && (k0 + kBlock < K);
+      const uint4 cv = *reinterpret_cast<const uint4*>(&lcodes[wave][arow * U + u][16 * g]);
+      const uint32_t s2 = *reinterpret_cast<const uint16_t*>(&lscales[wave][arow * U + u][2 * g]);
+      const uint32_t sc = s2 & ((live0 ? 0xFFu : 0u) | (live1 ? 0xFF00u : 0u));
+      half8_t A[4];
+      decode_a(cv, sc, 0xFFFFu, A);
 #pragma unroll
-    for (int s = 0; s < S; ++s) tile_mfma(A, wv[u][s], wsc[u][s], acc[s]);
+      for (int s = 0; s < S; ++s) tile_mfma(A, wv[u][s], wsc[u][s], acc[s]);
+    } else if (wave + NW * u < tiles) {              // uniform: tiles past the end only complete their loads
+      const int t = wave + NW * u;
+      const int k0 = t * kTileK + 32 * g;
+      const bool live0 = (r < M) && (k0 < K);
+      const bool live1 = live0 && (k0 + kBlock < K);
+      const uint4 cv = *reinterpret_cast<const uint4*>(&lcodes[wave][arow * U + u][16 * g]);
+      const uint32_t s2 = *reinterpret_cast<const uint16_t*>(&lscales[wave][arow * U + u][2 * g]);
+      const uint32_t sc = s2 & ((live0 ? 0xFFu : 0u) | (live1 ? 0xFF00u : 0u));
+      half8_t A[4];
+      decode_a(cv, sc, 0xFFFFu, A);
+#pragma unroll
+      for (int s = 0; s < S; ++s) tile_mfma(A, wv[u][s], wsc[u][s], acc[s]);
+    }
     __builtin_amdgcn_sched_barrier(0);
     if (u + 2 < U) request(u + 2);             // two batches in flight
     if constexpr (BAL) set_issue_priority(U - 2 - u);
@@ -597,23 +730,23 @@ hipError_t launch_fill_zero(float* out, int M, int N, int64_t ldo, hipStream_t s
 
 constexpr int kSkNW = 8, kSkU = 5;
 
-// Strips per workgroup (1..3): the fewest strips on the busiest CU -- a launch
-// of more than 256 workgroups puts a second one on some CUs -- with ties going
-// to more strips per workgroup (fewer, longer weight streams).  Measured at
-// K = 5120 (us per launch, M = 1, skinny GEMM; S = 1 / 2 / 3): N = 2048
-// 3.9 / 4.7 / 5.7, N = 5120 5.7 / 5.0 / 5.8, N = 8192 6.0 / 5.7 / 6.3,
-// N = 12288 8.5 / 9.0 / 7.8; the one-launch layer follows the same pattern.
-static int pick_strips(int nstrips) {
-  int best = 3, cost = 0;
-  for (int s = 3; s >= 1; --s) {
-    const int wgs = (nstrips + s - 1) / s;
-    const int c = (wgs + kCUs - 1) / kCUs * s;
-    if (s == 3 || c < cost) {
-      best = s;
-      cost = c;
-    }
+template <int S, int NW>
+static void launch_skinny_nw(int grid, hipStream_t stream, const uint8_t* a_codes, const uint8_t* a_scales,
+                             const float* a_g, int M, int K, const uint8_t* w_codes, const uint8_t* w_scales, int N,
+                             const SegTable& st, const float* w_g, float* out, int64_t ldo) {
+  // the peeled loop where some wave's last iteration is partial
+  const bool tail = (K / kTileK) % (NW * kSkU) != 0;
+#define NVFP4_SKINNY_LAUNCH(AL, T)                                                                               \
+  gemm_skinny_kernel<S, NW, kSkU, AL, T><<<grid, 64 * NW, 0, stream>>>(a_codes, a_scales, a_g, M, K, w_codes, \
+                                                                      w_scales, N, st, w_g, out, ldo)
+  if (K % 32 == 0) {
+    if (tail) NVFP4_SKINNY_LAUNCH(true, true);
+    else NVFP4_SKINNY_LAUNCH(true, false);
+  } else {
+    if (tail) NVFP4_SKINNY_LAUNCH(false, true);
+    else NVFP4_SKINNY_LAUNCH(false, false);
   }
-  return best;
+#undef NVFP4_SKINNY_LAUNCH
 }
 
 template <int S>
@@ -621,11 +754,24 @@ static void launch_skinny(int nstrips, hipStream_t stream, const uint8_t* a_code
                           const float* a_g, int M, int K, const uint8_t* w_codes, const uint8_t* w_scales, int N,
                           const SegTable& st, const float* w_g, float* out, int64_t ldo) {
   const int grid = (nstrips + S - 1) / S;
+  if (stream_waves(K, N) == 16)
+    launch_skinny_nw<S, 16>(grid, stream, a_codes, a_scales, a_g, M, K, w_codes, w_scales, N, st, w_g, out, ldo);
+  else
+    launch_skinny_nw<S, 8>(grid, stream, a_codes, a_scales, a_g, M, K, w_codes, w_scales, N, st, w_g, out, ldo);
+}
+
+// Row blocks run eight waves; a sixteen-wave order takes two accumulator sets
+// (VW = 2) and four tiles per iteration, two per set.
+template <int S, int MT, int VW>
+static void launch_rows_vw(int grid, hipStream_t stream, const uint8_t* a_codes, const uint8_t* a_scales,
+                           const float* a_g, int M, int K, const uint8_t* w_codes, const uint8_t* w_scales, int N,
+                           const SegTable& st, const float* w_g, float* out, int64_t ldo) {
+  constexpr int U = VW == 1 ? kSkU : 4;             // a whole number of tiles per accumulator set
   if (K % 32 == 0)
-    gemm_skinny_kernel<S, kSkNW, kSkU, true><<<grid, 64 * kSkNW, 0, stream>>>(
+    gemm_rows_kernel<S, kSkNW, VW, U, true, MT><<<grid, 64 * kSkNW, 0, stream>>>(
         a_codes, a_scales, a_g, M, K, w_codes, w_scales, N, st, w_g, out, ldo);
   else
-    gemm_skinny_kernel<S, kSkNW, kSkU, false><<<grid, 64 * kSkNW, 0, stream>>>(
+    gemm_rows_kernel<S, kSkNW, VW, U, false, MT><<<grid, 64 * kSkNW, 0, stream>>>(
         a_codes, a_scales, a_g, M, K, w_codes, w_scales, N, st, w_g, out, ldo);
 }
 
@@ -634,13 +780,12 @@ static void launch_rows(int nstrips, int64_t blocks, hipStream_t stream, const u
                         const uint8_t* a_scales, const float* a_g, int M, int K, const uint8_t* w_codes,
                         const uint8_t* w_scales, int N, const SegTable& st, const float* w_g, float* out,
                         int64_t ldo) {
+  static_assert(kSkNW == 8, "row blocks replay sixteen-wave orders with eight waves");
   const int grid = (int)((nstrips + S - 1) / S * blocks);
-  if (K % 32 == 0)
-    gemm_rows_kernel<S, kSkNW, kSkU, true, MT><<<grid, 64 * kSkNW, 0, stream>>>(
-        a_codes, a_scales, a_g, M, K, w_codes, w_scales, N, st, w_g, out, ldo);
+  if (stream_waves(K, N) == 16)
+    launch_rows_vw<S, MT, 2>(grid, stream, a_codes, a_scales, a_g, M, K, w_codes, w_scales, N, st, w_g, out, ldo);
   else
-    gemm_rows_kernel<S, kSkNW, kSkU, false, MT><<<grid, 64 * kSkNW, 0, stream>>>(
-        a_codes, a_scales, a_g, M, K, w_codes, w_scales, N, st, w_g, out, ldo);
+    launch_rows_vw<S, MT, 1>(grid, stream, a_codes, a_scales, a_g, M, K, w_codes, w_scales, N, st, w_g, out, ldo);
 }
 
 // Strips per workgroup of gemm_rows_kernel: every workgroup decodes its S weight
@@ -668,7 +813,7 @@ hipError_t launch_gemm_skinny(const uint8_t* a_codes, const uint8_t* a_scales, c
   const int nstrips = (N + kStrip - 1) / kStrip;
   if (M <= 16) {
 #define NVFP4_SKINNY(S) launch_skinny<S>(nstrips, stream, a_codes, a_scales, a_g, M, K, w_codes, w_scales, N, st, w_g, out, ldo)
-    switch (pick_strips(nstrips)) {
+    switch (skinny_strips(nstrips)) {
       case 1: NVFP4_SKINNY(1); break;
       case 2: NVFP4_SKINNY(2); break;
       default: NVFP4_SKINNY(3);
@@ -708,37 +853,62 @@ hipError_t launch_gemm_skinny(const uint8_t* a_codes, const uint8_t* a_scales, c
 // measured about 0.4 us per launch faster for the 1-row instantiation at
 // K = 5120, N = 12288, slower for 2 to 6 rows and no better for 8 or 16 (or in
 // the skinny GEMM).
-template <int S, int U, int MAXM>
+template <int S, int NW, int U, int MAXM>
 static bool launch_decode(int nstrips, hipStream_t stream, const uint16_t* x, int64_t ldx, const float* amax_in,
                           uint8_t* a_codes, uint8_t* a_scales, float* a_g, int M, int K, const uint8_t* w_codes,
                           const uint8_t* w_scales, int N, const SegTable& st, const float* w_g, float* out,
                           int64_t ldo) {
   const int grid = (nstrips + S - 1) / S;
-  linear_decode_kernel<S, kSkNW, U, MAXM, MAXM == 1><<<grid, 64 * kSkNW, 0, stream>>>(
-      x, ldx, amax_in, a_codes, a_scales, a_g, M, K, w_codes, w_scales, N, st, w_g, out, ldo);
+  if ((K + kTileK - 1) / kTileK == NW * U)           // every wave has U tiles
+    linear_decode_kernel<S, NW, U, MAXM, MAXM == 1 && NW == 8, false><<<grid, 64 * NW, 0, stream>>>(
+        x, ldx, amax_in, a_codes, a_scales, a_g, M, K, w_codes, w_scales, N, st, w_g, out, ldo);
+  else
+    linear_decode_kernel<S, NW, U, MAXM, MAXM == 1 && NW == 8, true><<<grid, 64 * NW, 0, stream>>>(
+        x, ldx, amax_in, a_codes, a_scales, a_g, M, K, w_codes, w_scales, N, st, w_g, out, ldo);
   return true;
 }
 
-// The row-bound instance for M (rows 1, 4, 8, 16; U = 10 stops at 8 rows and
-// U = 20 at 4, as decode_tiles_per_wave allows).  False: no instance.
-template <int S, int U>
+// The row-bound instance for M (rows 1, 4, 8, 16; as decode_max_rows allows,
+// 16 rows while NW * U covers 40 tiles, 8 up to 80 and 4 up to 160).  False: no
+// instance.
+template <int S, int NW, int U>
 static bool launch_decode_rows(int nstrips, hipStream_t stream, const uint16_t* x, int64_t ldx,
                                const float* amax_in, uint8_t* a_codes, uint8_t* a_scales, float* a_g, int M, int K,
                                const uint8_t* w_codes, const uint8_t* w_scales, int N, const SegTable& st,
                                const float* w_g, float* out, int64_t ldo) {
 #define NVFP4_DECODE(MAXM)                                                                                       \
-  launch_decode<S, U, MAXM>(nstrips, stream, x, ldx, amax_in, a_codes, a_scales, a_g, M, K, w_codes, w_scales, N, \
-                            st, w_g, out, ldo)
+  launch_decode<S, NW, U, MAXM>(nstrips, stream, x, ldx, amax_in, a_codes, a_scales, a_g, M, K, w_codes, w_scales, \
+                                N, st, w_g, out, ldo)
   if (M == 1) return NVFP4_DECODE(1);
   if (M <= 4) return NVFP4_DECODE(4);
-  if constexpr (U <= 10) {
+  if constexpr (NW * U <= 80) {
     if (M <= 8) return NVFP4_DECODE(8);
-    if constexpr (U == 5) {
-      if (M <= kDecMaxM) return NVFP4_DECODE(kDecMaxM);
+    if constexpr (NW * U <= 40) {
+      if (M <= 16) return NVFP4_DECODE(16);
     }
   }
 #undef NVFP4_DECODE
   return false;
+}
+
+template <int S, int NW>
+static bool launch_decode_nw(int nstrips, hipStream_t stream, const uint16_t* x, int64_t ldx,
+                             const float* amax_in, uint8_t* a_codes, uint8_t* a_scales, float* a_g, int M, int K,
+                             const uint8_t* w_codes, const uint8_t* w_scales, int N, const SegTable& st,
+                             const float* w_g, float* out, int64_t ldo) {
+  switch (decode_tiles_per_wave(K, NW)) {
+    case 5:
+      return launch_decode_rows<S, NW, 5>(nstrips, stream, x, ldx, amax_in, a_codes, a_scales, a_g, M, K, w_codes,
+                                          w_scales, N, st, w_g, out, ldo);
+    case 10:
+      return launch_decode_rows<S, NW, 10>(nstrips, stream, x, ldx, amax_in, a_codes, a_scales, a_g, M, K, w_codes,
+                                           w_scales, N, st, w_g, out, ldo);
+    default:
+      if constexpr (NW == 8)
+        return launch_decode_rows<S, NW, 20>(nstrips, stream, x, ldx, amax_in, a_codes, a_scales, a_g, M, K,
+                                             w_codes, w_scales, N, st, w_g, out, ldo);
+      return false;                                  // sixteen waves cover K <= 20480 with U <= 10
+  }
 }
 
 template <int S>
@@ -746,19 +916,12 @@ static bool launch_decode_tiles(int nstrips, hipStream_t stream, const uint16_t*
                                 const float* amax_in, uint8_t* a_codes, uint8_t* a_scales, float* a_g, int M, int K,
                                 const uint8_t* w_codes, const uint8_t* w_scales, int N, const SegTable& st,
                                 const float* w_g, float* out, int64_t ldo) {
-  switch (decode_tiles_per_wave(M, K)) {
-    case 5:
-      return launch_decode_rows<S, 5>(nstrips, stream, x, ldx, amax_in, a_codes, a_scales, a_g, M, K, w_codes,
-                                      w_scales, N, st, w_g, out, ldo);
-    case 10:
-      return launch_decode_rows<S, 10>(nstrips, stream, x, ldx, amax_in, a_codes, a_scales, a_g, M, K, w_codes,
-                                       w_scales, N, st, w_g, out, ldo);
-    case 20:
-      return launch_decode_rows<S, 20>(nstrips, stream, x, ldx, amax_in, a_codes, a_scales, a_g, M, K, w_codes,
-                                       w_scales, N, st, w_g, out, ldo);
-    default:
-      return false;
-  }
+  if (M < 1 || M > decode_max_rows(K)) return false;
+  if (stream_waves(K, N) == 16)
+    return launch_decode_nw<S, 16>(nstrips, stream, x, ldx, amax_in, a_codes, a_scales, a_g, M, K, w_codes, w_scales,
+                                   N, st, w_g, out, ldo);
+  return launch_decode_nw<S, 8>(nstrips, stream, x, ldx, amax_in, a_codes, a_scales, a_g, M, K, w_codes, w_scales, N,
+                                st, w_g, out, ldo);
 }
 
 hipError_t launch_linear_decode(const uint16_t* x, int64_t ldx, const float* amax_in, uint8_t* a_codes,
@@ -767,7 +930,7 @@ hipError_t launch_linear_decode(const uint16_t* x, int64_t ldx, const float* ama
                                 int64_t ldo, hipStream_t stream) {
   const int nstrips = (N + kStrip - 1) / kStrip;
   bool ok;
-  switch (pick_strips(nstrips)) {
+  switch (skinny_strips(nstrips)) {
     case 1:
       ok = launch_decode_tiles<1>(nstrips, stream, x, ldx, amax_in, a_codes, a_scales, a_g, M, K, w_codes, w_scales, N,
                                   st, w_g, out, ldo);

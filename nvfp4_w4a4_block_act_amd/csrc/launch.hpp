@@ -27,19 +27,64 @@ constexpr int kCUs = 256;         // compute units of a gfx950 (MI355X) device
 constexpr int kPartials = 1024;             // amax workgroups of the two-pass activation quantizer
 constexpr int64_t kSmallElems = 1 << 17;    // single-launch activation quantizer up to 128K elements
 constexpr int kSegParts = 256;              // amax workgroups per weight segment (packer)
-constexpr int kDecMaxM = 16;                // rows of the one-launch decode layer
 constexpr size_t kScratchBytes = kPartials * sizeof(uint32_t) + 16;   // nvfp4_linear_noalloc's scratch
 constexpr int kMaxDevices = 64;             // GPUs whose scratch address is cached
 
-// k tiles per wave (U) of the one-launch decode layer for an M x K input, 0
-// when it has no instance: the wave-private activation area (MAXM * U tiles of
-// 80 bytes) must fit LDS and the lane's block registers (MAXM * U / 8 steps of
-// two 16-byte chunks) the register file, so longer K takes fewer rows.
-inline int decode_tiles_per_wave(int64_t M, int64_t K) {
-  if (K <= 8 * 5 * kTileK) return 5;               // K <= 5120: every row bound
-  if (K <= 8 * 10 * kTileK && M <= 8) return 10;   // K <= 10240
-  if (K <= 8 * 20 * kTileK && M <= 4) return 20;   // K <= 20480
+// Strips of 16 output columns per workgroup (1..3) of the M <= 16 weight-
+// streaming GEMM: the fewest strips on the busiest CU -- a launch of more than
+// 256 workgroups puts a second one on some CUs -- with ties going to more strips
+// per workgroup (fewer, longer weight streams).  Measured at K = 5120 (us per
+// launch, M = 1, skinny GEMM; S = 1 / 2 / 3): N = 2048 3.9 / 4.7 / 5.7,
+// N = 5120 5.7 / 5.0 / 5.8, N = 8192 6.0 / 5.7 / 6.3, N = 12288 8.5 / 9.0 / 7.8;
+// the one-launch layer follows the same pattern.
+inline int skinny_strips(int64_t nstrips) {
+  int best = 3;
+  int64_t cost = 0;
+  for (int s = 3; s >= 1; --s) {
+    const int64_t wgs = (nstrips + s - 1) / s;
+    const int64_t c = (wgs + kCUs - 1) / kCUs * s;
+    if (s == 3 || c < cost) {
+      best = s;
+      cost = c;
+    }
+  }
+  return best;
+}
+
+// Waves of a weight-streaming workgroup (skinny GEMM, row blocks, one-launch
+// layer) that split its k tiles, wave w taking tiles w, w + W, w + 2W, ...: the
+// count fixes the fp32 summation order, so every weight-streaming form takes it
+// from K and N alone and their results stay bit-identical.  Sixteen waves (four
+// per SIMD) keep more of the weight stream in flight per CU, which pays where
+// the M <= 16 launch leaves CUs idle and each wave has more than five tiles (us
+// per skinny launch at M = 1, 8 / 16 waves: K = 17408, N = 5120 15.9 / 14.9;
+// N = 2048 11.6 / 10.6; K = 6144, N = 5120 9.0 / 8.5); with every CU busy it
+// does not (K = 10240, N = 12288: 15.0 / 15.1), nor at K = 5120 (N = 12288:
+// 9.0 / 11.9).
+inline int stream_waves(int64_t K, int64_t N) {
+  if (K <= 8 * 5 * kTileK) return 8;
+  const int64_t nstrips = (N + kStrip - 1) / kStrip;
+  const int s = skinny_strips(nstrips);
+  return (nstrips + s - 1) / s < kCUs ? 16 : 8;
+}
+
+// Rows of the one-launch decode layer for a K (0: none): each wave keeps its k
+// tiles' activation blocks for every row in registers and in a wave-private LDS
+// area, so longer K takes fewer rows.
+inline int decode_max_rows(int64_t K) {
+  if (K <= 5 * 8 * kTileK) return 16;                // K <= 5120
+  if (K <= 10 * 8 * kTileK) return 8;                // K <= 10240
+  if (K <= 20 * 8 * kTileK) return 4;                // K <= 20480
   return 0;
+}
+
+// Activation k tiles per wave (U: 5, 10 or 20) of the one-launch layer with nw
+// waves; within decode_max_rows the wave-private area (MAXM * U tiles of 80
+// bytes) fits LDS and the lane's block registers (MAXM * U / 8 steps of two
+// 16-byte chunks) fit the register file, 128 VGPRs per lane at sixteen waves.
+inline int decode_tiles_per_wave(int64_t K, int nw) {
+  const int64_t per = ((K + kTileK - 1) / kTileK + nw - 1) / nw;
+  return per <= 5 ? 5 : (per <= 10 ? 10 : 20);
 }
 
 // Rows per weight pass of the row-blocked weight-streaming GEMM: 16 for outputs

@@ -288,13 +288,20 @@ def test_quantizer_down_proj_activations_full_size(calibrated):
 
 
 @pytest.mark.parametrize("M,N,K", [(24, 700, 1040), (32, 200, 5120), (100, 1500, 2064), (70, 100, 1040),
-                                   (300, 2000, 512)])
+                                   (300, 2000, 512), (24, 5120, 10256), (100, 1500, 11664), (70, 100, 6144),
+                                   (128, 5120, 17408), (40, 12300, 10256)])
 def test_gemm_row_blocks_bit_identical_to_16_rows(M, N, K):
     """nvfp4_gemm's weight-streaming form for M > 16 (32-row passes: (24, 700),
-    (32, 200); 64-row: (100, 1500), (300, 2000); 16-row passes for outputs of at
-    most 8 strips: (70, 100)) gives, for every 16-row slice of the quantized
-    activations, exactly the M <= 16 kernel's result on that slice, and the
-    oracle's within tolerance."""
+    (32, 200), (24, 5120); 64-row: (100, 1500), (300, 2000), (128, 5120); 16-row
+    passes for outputs of at most 8 strips: (70, 100)) gives, for every 16-row
+    slice of the quantized activations, exactly the M <= 16 kernel's result on
+    that slice, and the oracle's within tolerance.  For K > 5120 with fewer M <= 16
+    workgroups than CUs the M <= 16 kernel splits the k tiles over sixteen waves,
+    and the row blocks replay that order with two accumulator sets per wave of
+    eight (1, 2 and 3 strips per workgroup at (100, 1500), (24, 5120) and
+    (128, 5120)); the ragged last tile falls to the first set at K = 10256 (tile
+    80, wave 0) and to the second at K = 11664 (tile 91, wave 11).  N = 12300
+    (257 workgroups at M <= 16) keeps eight waves at K = 10256."""
     assert nv.nvfp4_gemm_form(M, K, N) == 0
     rng = np.random.default_rng(M * 7 + N + K)
     segs = [(0, N // 3), (N // 3, N)]

@@ -164,20 +164,22 @@ def test_linear_strips_per_workgroup(M, N):
     assert_within_tol(out.cpu().numpy().astype(np.float64)[:, cols], ref, bnd, f"strips M={M} N={N}")
 
 
-@pytest.mark.parametrize("M,K", [(1, 17408), (4, 20480), (3, 10256), (8, 10240), (6, 5136), (2, 8208),
-                                 (9, 6144), (5, 17408)])
-def test_linear_long_k(M, K):
+@pytest.mark.parametrize("M,K,N", [(1, 17408, 700), (4, 20480, 700), (3, 10256, 700), (8, 10240, 700),
+                                   (6, 5136, 700), (2, 8208, 700), (9, 6144, 700), (5, 17408, 700), (1, 9008, 700),
+                                   (1, 17408, 12300), (3, 10256, 12300), (8, 10240, 12300)])
+def test_linear_long_k(M, K, N):
     """K beyond 5120: one launch while the wave-local activation tiles fit (up to
     10240 for 8 rows, 20480 for 4), two launches otherwise ((9, 6144), (5, 17408));
     either way bit-identical to quantize + GEMM and within the oracle's tolerance
-    on sampled columns."""
-    rng = np.random.default_rng(900 + M + K)
-    N = 700
+    on sampled columns.  N = 700 (15 workgroups) runs sixteen waves per workgroup
+    (row-bound instances 1, 4 and 8 at five tiles per wave, 1 and 4 at ten);
+    N = 12300 (257 workgroups) runs eight (ten and twenty tiles per wave)."""
+    rng = np.random.default_rng(900 + M + K + N)
     segs = [(0, 300), (300, N)]
-    w = np.concatenate([(0.02 * (1 + i) * rng.standard_normal((e - b, K))).astype(np.float32)
+    w = np.concatenate([np.float32(0.02 * (1 + i)) * rng.standard_normal((e - b, K), dtype=np.float32)
                         for i, (b, e) in enumerate(segs)])
     x_bits = W.random_act(1000 + M, M, K, "student_t")
-    say(f"[long K] M={M} K={K}")
+    say(f"[long K] M={M} K={K} N={N}")
     pw = gpu_pack(w, segs)
     x = to_dev_bf16(x_bits)
     out, (c, s, g) = nv.linear(x, pw)
@@ -188,4 +190,4 @@ def test_linear_long_k(M, K):
     assert torch.equal(out, ref_gpu)
     cols = np.sort(np.unique(np.concatenate([rng.choice(N, 120, replace=False), [0, 299, 300, N - 1]])))
     ref, bnd = oracle_linear_rows(x_bits, w, segs, cols=cols)
-    assert_within_tol(out.cpu().numpy().astype(np.float64)[:, cols], ref, bnd, f"long K M={M} K={K}")
+    assert_within_tol(out.cpu().numpy().astype(np.float64)[:, cols], ref, bnd, f"long K M={M} K={K} N={N}")

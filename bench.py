@@ -21,8 +21,9 @@ against the fp16 matrix-core peak and an oracle baseline -- and the standalone
 activation quantizer over the down projection's input (GB/s against HBM).
 
 Prints one JSON line (see the keys below).  ``--config`` selects another
-workload on its own (prefill_gate_up, gdn_in_proj, down_proj,
-down_proj_quantize, tiny, ...); ``--no-prefill`` skips the prefill legs.
+workload on its own (decode_down_proj, prefill_gate_up, gdn_in_proj,
+down_proj, down_proj_quantize, tiny, ...); ``--no-prefill`` skips the prefill
+legs.
 """
 import argparse
 import json
@@ -42,7 +43,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=480)
     ap.add_argument("--warmup", type=int, default=48)
     ap.add_argument("--config", default="decode",
-                    choices=["decode", "prefill_gate_up", "gdn_in_proj", "down_proj", "down_proj_quantize", "tiny",
+                    choices=["decode", "decode_down_proj", "prefill_gate_up", "gdn_in_proj", "down_proj",
+                             "down_proj_quantize", "tiny",
                              "copy_calibration", "gdn_repair_compare", "gate_up_swiglu", "kv_fp8", "static_calibration"])
     ap.add_argument("--copies", type=int, default=16, help="device copies of the packed weight (decode)")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying HIP graphs")
@@ -74,6 +76,8 @@ def main():
 
     if args.config == "decode":
         res = bench_decode(args, torch, nv, W, dev)
+    elif args.config == "decode_down_proj":
+        res = bench_decode(args, torch, nv, W, dev, W.decode_down_proj(M=16))
     elif args.config == "copy_calibration":
         res = bench_copy(args, torch, dev)
     elif args.config == "gdn_repair_compare":
@@ -460,10 +464,22 @@ QUANT_COUNTERS = "quantize_act_kernel_down_proj_activation_m32768_k17408.md"
 QUANT_SOURCES = ("quantize.hip", "quant_device.hpp", "common.hpp", "launch.hpp")
 
 
-def bench_decode(args, torch, nv, W, dev):
+def one_launch_rows(K):
+    """Rows up to which nvfp4_linear runs as one launch for this K (its documented bounds)."""
+    return 16 if K <= 5120 else 8 if K <= 10240 else 4 if K <= 20480 else 0
+
+
+def bench_decode(args, torch, nv, W, dev, d16=None):
+    """The decode linear layer at M = 1, 4, 16 (the default: K = 5120, N = 12288;
+    ``--config decode_down_proj``: K = 17408, N = 5120, where M = 16 runs as the
+    quantizer then the GEMM)."""
     Ms = (1, 4, 16)
-    d16 = W.decode(M=16)
+    headline = d16 is None
+    if headline:
+        d16 = W.decode(M=16)
     K, N = d16.K, d16.N
+    workload = (f"decode_skinny_gemm_m1_m4_m16_k{K}_n{N}" if headline else f"decode_down_proj_m1_m4_m16_k{K}_n{N}")
+    one_launch = {M: M <= one_launch_rows(K) for M in Ms}
     w = torch.from_numpy(d16.w).to(dev)
     pw0 = nv.pack_weight(w, d16.segments)
     del w
@@ -478,8 +494,9 @@ def bench_decode(args, torch, nv, W, dev):
     torch.cuda.synchronize()
 
     def step_eager(r):
-        # one nvfp4_linear call per token count: for these sizes a single launch
-        # (activation quantization + GEMM + epilogue)
+        # one nvfp4_linear call per token count: a single launch (activation
+        # quantization + GEMM + epilogue) where the rows fit the one-launch
+        # layer, else the quantizer then the GEMM
         # every call streams a different weight copy, so no call finds its
         # weights in the 256 MB last-level cache (16 copies = 566 MB)
         for i, M in enumerate(Ms):
@@ -570,8 +587,9 @@ def bench_decode(args, torch, nv, W, dev):
         "vs_baseline": None, "dtype": "f16",
         "dtype_note": "NVFP4 operands decoded exactly to fp16, fp16 MFMA products, fp32 accumulation",
         "data": "synthetic",
-        "config": {"workload": "decode_skinny_gemm_m1_m4_m16_k5120_n12288", "M": list(Ms), "K": K, "N": N,
+        "config": {"workload": workload, "M": list(Ms), "K": K, "N": N,
                    "segments": 1, "weight_copies": len(copies), "graphs": not args.no_graph,
+                   "one_launch": {str(M): one_launch[M] for M in Ms},
                    "step_bytes": step_bytes, "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
                    "linear_kernel": {str(M): {k: round(v, 3) if isinstance(v, float) else v for k, v in kern[M].items()}
                                    for M in Ms},
@@ -579,14 +597,17 @@ def bench_decode(args, torch, nv, W, dev):
                    "device_copy_GBps": round(copy_gbs, 1), "gpu_state_after_run": gpu_state()},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic(DECODE_COUNTERS, DECODE_SOURCES),
+                     "traffic": measured_traffic(DECODE_COUNTERS, DECODE_SOURCES) if headline else None,
                      "traffic_unit": "bytes per launch (mean over the three token counts)",
                      "algorithmic_bytes_per_launch": round(tot_b / len(Ms), 1),
-                     "kernel": "linear_decode_kernel", "per_launch_bytes": {str(M): kern[M]["bytes"] for M in Ms}},
+                     "kernel": "linear_decode_kernel" if all(one_launch.values()) else
+                               "linear_decode_kernel (one-launch rows); quantize_act_small_kernel + gemm_skinny_kernel "
+                               "per call for the others",
+                     "per_launch_bytes": {str(M): kern[M]["bytes"] for M in Ms}},
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline_decode(d16, Ms, args.cpu_seconds, step_bytes)
-    if not args.no_prefill:
+    if headline and not args.no_prefill:
         del copies, pw0, xs, acts, outs, ws
         if not args.no_graph:
             del long_graph, singles
@@ -651,7 +672,7 @@ def cpu_baseline_decode(d16, Ms, target_s, step_bytes):
     per_step = t_all / reps * (N / cols)
     return {"value": round(step_bytes / per_step / 1e9, 4), "unit": "GB/s", "cores": max(threads, oracle_threads()),
             "kind": "oracle", "host": host_info(),
-            "sample": f"{reps} oracle steps over {cols} of {N} output columns (all three token counts), "
+            "sample": f"{reps} oracle steps over {cols} of {N} output columns (token counts {list(Ms)}), "
                       f"scaled by {N / cols:.1f} to the full step; {t_all:.1f} s of CPU time; {cpu_kind(threads)}"}
 
 

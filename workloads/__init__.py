@@ -131,6 +131,19 @@ def swiglu_rows(rng, rows, K):
     return bf16_bits(act.astype(np.float32))
 
 
+def decode_down_proj(seed=0, M=16):
+    """Down projection at decode: M x 17408 SwiGLU activations, 5120 x 17408 weights.
+
+    The M=1 and M=4 cases are the leading rows of the M=16 draw (g then u),
+    then the weights, as in ``down_proj``.
+    """
+    K, N = 17408, 5120
+    rng = np.random.default_rng(seed)
+    x = swiglu_rows(rng, 16, K)
+    w, segs = _weights(rng, [N], K)
+    return Workload(f"decode_down_proj_m{M}_k17408_n5120", x[:M], w, segs)
+
+
 def down_proj(seed=0, M=32768, chunk=2048):
     """Long-context down projection: M x 17408 SwiGLU activations, 5120 x 17408 weights.
 

@@ -710,7 +710,7 @@ def gemm_leg(args, torch, nv, dev, d, steps, warmup, cpu_seconds, x=None):
     mean, med, p10, p90 = kernel_time_pairs(torch, lambda i: nv.gemm(c, s, g, pw, out=out), max(8, steps), 2)
     achieved = flops / mean / 1e12
     leg = {"workload": d.name, "M": M, "K": K, "N": N, "segments": len(d.segments),
-           "gemm_form": "mfma" if nv.nvfp4_gemm_form(M, K, N) == 1 else "weight_streaming",
+           "gemm_form": {0: "weight_streaming", 1: "mfma", 2: "mfma_256x128"}[nv.nvfp4_gemm_form(M, K, N)],
            "steps": steps, "step_ms": round(sec / steps * 1e3, 4),
            "step_TFLOPs": round(flops * steps / sec / 1e12, 2),
            "gemm_kernel_mean_ms": round(mean * 1e3, 4), "gemm_kernel_median_ms": round(med * 1e3, 4),
@@ -718,7 +718,7 @@ def gemm_leg(args, torch, nv, dev, d, steps, warmup, cpu_seconds, x=None):
            "gpu_state_after_run": gpu_state(),
            "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": F16_MFMA_PEAK_TFLOPS,
                         "unit": "TFLOP/s", "frac": round(achieved / F16_MFMA_PEAK_TFLOPS, 4), "traffic": None,
-                        "kernel": "gemm_mfma_kernel" if nv.nvfp4_gemm_form(M, K, N) == 1 else "gemm_rows_kernel"}}
+                        "kernel": "gemm_mfma_kernel" if nv.nvfp4_gemm_form(M, K, N) >= 1 else "gemm_rows_kernel"}}
     if cpu_seconds > 0:
         leg["cpu_baseline"] = cpu_baseline_gemm(d, cpu_seconds, flops)
     del pw, c, s, g, out, ws

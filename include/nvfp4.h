@@ -153,7 +153,9 @@ nvfp4_status nvfp4_weight_to_canonical(const uint8_t* w_codes, const uint8_t* w_
  *   out               fp32 [M][ldo], ldo >= N; must not overlap any input.
  * M <= 16 runs the bandwidth-bound skinny path; larger M the MFMA path, except
  * where too few 256 x 256 tiles would run to fill the chip (e.g. M up to ~256 at
- * K = 5120, N = 12288), which streams the weight once per 32 or 64 rows.  The MFMA
+ * K = 5120, N = 12288), which streams the weight once per 32 or 64 rows.  The
+ * MFMA path uses 256 x 128 tiles where 256 x 256 tiles would leave a partial
+ * last round (nvfp4_gemm_form).  The MFMA
  * path addresses its operands with 32-bit byte offsets: for M > 16 the activation
  * codes (M * K / 2 bytes) and the packed weight codes must each be below 4 GiB,
  * else NVFP4_ESHAPE.
@@ -166,8 +168,11 @@ nvfp4_status nvfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const f
 
 /* Which kernel form nvfp4_gemm (and the GEMM step of nvfp4_linear) runs for an
  * M x K x N product: 0 = the weight-streaming skinny GEMM (32 or 64 rows per
- * weight pass when M > 16), 1 = the MFMA GEMM; -1 for negative sizes.  Informational: the
- * results of both forms meet the same tolerance. */
+ * weight pass when M > 16), 1 = the MFMA GEMM with 256 x 256 output tiles,
+ * 2 = the MFMA GEMM with 256 x 128 tiles (taken where the wide tiles would leave
+ * a partial last round of the chip's CUs); -1 for negative sizes.
+ * Informational: every form meets the same tolerance, and the two MFMA forms
+ * give bit-identical results. */
 int nvfp4_gemm_form(int64_t M, int64_t K, int64_t N);
 
 /* ---------------------------------------------------------------------------
@@ -233,7 +238,7 @@ nvfp4_status nvfp4_linear_noalloc(const void* x_bf16, int64_t M, int64_t K, int6
  * The fused kernel is the MFMA GEMM with this epilogue.  Its result is
  * bit-identical to nvfp4_gemm (unfused packing), nvfp4_swiglu and
  * nvfp4_quantize_act run one after another whenever that nvfp4_gemm takes the
- * MFMA form (nvfp4_gemm_form(M, K, 2I) == 1); where nvfp4_gemm takes the
+ * MFMA form (nvfp4_gemm_form(M, K, 2I) is 1 or 2); where nvfp4_gemm takes the
  * weight-streaming form (small M) the two sum in different fp32 orders, and g
  * and u agree within the GEMM tolerance instead.
  * ------------------------------------------------------------------------- */

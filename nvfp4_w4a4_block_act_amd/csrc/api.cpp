@@ -267,7 +267,8 @@ nvfp4_status nvfp4_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const f
 
 int nvfp4_gemm_form(int64_t M, int64_t K, int64_t N) {
   if (M < 0 || K < 0 || N < 0) return -1;
-  return nvfp4::gemm_prefers_skinny(M, K, N) ? 0 : 1;
+  if (nvfp4::gemm_prefers_skinny(M, K, N)) return 0;
+  return nvfp4::mfma_narrow(M, N) ? 2 : 1;
 }
 
 // ---- nvfp4_linear: the workspace holds the quantizer's amax partials (large inputs only)

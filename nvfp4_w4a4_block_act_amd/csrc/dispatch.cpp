@@ -29,8 +29,7 @@ bool gemm_prefers_skinny(int64_t M, int64_t K, int64_t N) {
   //    17.6 us at M = 64, 64 us at M = 256, 125 us at M = 512 against 110 us for
   //    the MFMA GEMM).
   const double ktiles = (double)((K + kTileK - 1) / kTileK);
-  const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);
-  const double t_mfma = (double)((tiles + 255) / 256) * ktiles * 2.5e-6;
+  const double t_mfma = std::min(mfma_cost(M, N, false), mfma_cost(M, N, true)) * ktiles * 2.5e-6;
   const int rp = rows_per_pass(M, N);
   const double passes = (double)((M + rp - 1) / rp);
   const double t_stream = passes * (double)N * (double)K * 0.5625 / 6e12;

@@ -44,6 +44,9 @@ namespace nvfp4 {
 
 constexpr int kBM = 256, kBN = 256;
 constexpr int kMfWaves = 8, kMfThreads = 64 * kMfWaves;
+// The narrow form: a 256 x 128 tile of four waves (one N-wave), each wave's
+// work exactly as in the 256 x 256 form, two workgroups per CU.
+constexpr int kBNNarrow = 128, kMfThreadsNarrow = 256;
 constexpr int kGroupM = 4;
 constexpr int kHalfRow = 9;                            // uint4 pieces per LDS weight row (8 + 1 pad)
 
@@ -76,20 +79,21 @@ __device__ __forceinline__ uint32_t buf_u8(__amdgpu_buffer_rsrc_t r, uint32_t vo
   return (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(r, voff, soff, 0);
 }
 
-// Per-thread coalesced activation slots: slot q = tid + 512 s covers row q / 4
-// of the tile and its 16-byte piece q % 4.
+// Per-thread coalesced activation slots: slot q = tid + threads * s covers row
+// q / 4 of the tile and its 16-byte piece q % 4 (NS = 1024 / threads slots).
+template <int NS>
 struct ASlots {
-  uint32_t off[2];                                     // byte offset of the piece in tile 0
-  int lds[2];                                          // uint4 index inside an LDS stage
-  int koff[2];                                         // k offset of the piece inside a tile
+  uint32_t off[NS];                                    // byte offset of the piece in tile 0
+  int lds[NS];                                         // uint4 index inside an LDS stage
+  int koff[NS];                                        // k offset of the piece inside a tile
 };
 
-template <bool AL16, bool TAIL>
-__device__ __forceinline__ void load_a_codes(__amdgpu_buffer_rsrc_t ra, const ASlots& as, int t, int full, int K,
-                                             uint4 (&r)[2]) {
+template <bool AL16, bool TAIL, int NS>
+__device__ __forceinline__ void load_a_codes(__amdgpu_buffer_rsrc_t ra, const ASlots<NS>& as, int t, int full, int K,
+                                             uint4 (&r)[NS]) {
   const uint32_t soff = (uint32_t)t * 64u;
 #pragma unroll
-  for (int s = 0; s < 2; ++s) {
+  for (int s = 0; s < NS; ++s) {
     if (TAIL && t == full) {
       const int k0 = t * kTileK + as.koff[s];
       uint4 v = make_uint4(0u, 0u, 0u, 0u);
@@ -238,24 +242,28 @@ constexpr int kHRow = 128 + 8;   // bf16 per LDS row of the SwiGLU tile (16-byte
 // gate/up packing (columns 256 t .. 256 t + 127 are gate rows 128 t .., the next
 // 128 the matching up rows), and the workgroup writes the NVFP4 encoding of
 // h[m][j] = bf16(silu(g) * u) for its 128 j instead of fp32 output.
-template <bool AL16, bool AL4, bool TAIL, int EPI>
-__global__ __launch_bounds__(kMfThreads, 1) void gemm_mfma_kernel(
+// NWN: waves along N (2: the 256 x 256 tile of eight waves; 1: the narrow
+// 256 x 128 tile of four waves, two workgroups per CU).
+template <bool AL16, bool AL4, bool TAIL, int EPI, int NWN>
+__global__ __launch_bounds__(256 * NWN, 3 - NWN) void gemm_mfma_kernel(
     const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales, const float* __restrict__ a_g,
     int M, int K, const uint8_t* __restrict__ w_codes, const uint8_t* __restrict__ w_scales, int N, int n_lo,
     int n_hi, SegTable st, const float* __restrict__ w_g, float* __restrict__ out, int64_t ldo, SwigluOut so) {
   constexpr bool SW = EPI == kEpiSwiglu;
-  __shared__ uint4 sW[2][kBN * kHalfRow];              // decoded weight half-tiles, 2 x 36 KB
+  constexpr int kThreads = 256 * NWN, kTileN = 128 * NWN, NS = 1024 / kThreads;
+  static_assert(!SW || NWN == 2, "the SwiGLU epilogue pairs gate and up columns of a 256-column tile");
+  __shared__ uint4 sW[2][kTileN * kHalfRow];           // decoded weight half-tiles, 2 x 36 KB (2 x 18 KB narrow)
   __shared__ uint4 sA[2][kBM * 4];                     // activation codes, 2 x 16 KB
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / NWN, wn = wave % NWN;
   const int tiles = (K + kTileK - 1) / kTileK, full = K / kTileK;
   const int nstrips = (N + kStrip - 1) / kStrip;
   const int tb = 0, te = tiles;                        // the workgroup's k tiles
 
   // ---- workgroup -> output tile: XCD-major numbering, then grouped row panels
-  const int num_m = (M + kBM - 1) / kBM, num_n = (n_hi - n_lo + kBN - 1) / kBN;
+  const int num_m = (M + kBM - 1) / kBM, num_n = (n_hi - n_lo + kTileN - 1) / kTileN;
   const int nwg = num_m * num_n;
   int pid = blockIdx.x;
   if (nwg % 8 == 0) pid = (pid & 7) * (nwg >> 3) + (pid >> 3);
@@ -264,15 +272,15 @@ __global__ __launch_bounds__(kMfThreads, 1) void gemm_mfma_kernel(
   const int gsz = min(num_m - first_m, kGroupM);
   const int tm = first_m + (pid % per_group) % gsz;
   const int tn = (pid % per_group) / gsz;
-  const int m0 = tm * kBM, n0 = n_lo + tn * kBN;
+  const int m0 = tm * kBM, n0 = n_lo + tn * kTileN;
 
   // ---- activation code slots (coalesced loads) and this lane's scale rows
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(a_codes, (uint32_t)((int64_t)M * (K / 2)));
   const __amdgpu_buffer_rsrc_t ras = make_rsrc(a_scales, (uint32_t)((int64_t)M * (K / kBlock)));
-  ASlots as;
+  ASlots<NS> as;
 #pragma unroll
-  for (int s = 0; s < 2; ++s) {
-    const int q = tid + kMfThreads * s;
+  for (int s = 0; s < NS; ++s) {
+    const int q = tid + kThreads * s;
     const int r = q >> 2, p = q & 3;
     const int rc = min(m0 + r, M - 1);
     as.off[s] = (uint32_t)rc * (uint32_t)(K / 2) + 16u * p;
@@ -316,11 +324,11 @@ __global__ __launch_bounds__(kMfThreads, 1) void gemm_mfma_kernel(
   const int kb = 64 * h;
   const int arow0 = wm * 64 + i;
   const int bbase = (wn * (SW ? 64 : 128) + i) * kHalfRow + 4 * h;
-  uint4 an[2];                                          // activation codes in flight (next tile)
+  uint4 an[NS];                                         // activation codes in flight (next tile)
   uint32_t sc0[2];                                      // activation scales of tile 0
   RawW rw0, rw1;                                        // weights of tiles 0 and 1
   {
-    uint4 a0[2];
+    uint4 a0[NS];
     load_a_codes<AL16, TAIL>(ra, as, tb, full, K, a0);
     load_a_scales<AL4, TAIL>(ras, asp, tb, full, tb * kTileK + kb, K, sc0);
     load_w_tile(rw, rws, ws, tb, rw0);
@@ -328,8 +336,8 @@ __global__ __launch_bounds__(kMfThreads, 1) void gemm_mfma_kernel(
     load_w_tile(rw, rws, ws, min(tb + 1, last), rw1);
 #pragma unroll
     for (int d = 0; d < 4; ++d) store_w_piece(ws, rw0, 0, d, sW[0]);
-    sA[0][as.lds[0]] = a0[0];
-    sA[0][as.lds[1]] = a0[1];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) sA[0][as.lds[s]] = a0[s];
   }
   __syncthreads();
 
@@ -350,8 +358,8 @@ __global__ __launch_bounds__(kMfThreads, 1) void gemm_mfma_kernel(
     uint32_t scn[2];
     load_a_scales<AL4, TAIL>(ras, asp, min(t + 1, last), full, min(t + 1, last) * kTileK + kb, K, scn);
     mfma_half<0, SW>(sa, sW[0], scc, amask, arow0, bbase, h, ws, rwc, 1, sW[1], acc);
-    sa_next[as.lds[0]] = an[0];
-    sa_next[as.lds[1]] = an[1];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) sa_next[as.lds[s]] = an[s];
     load_a_codes<AL16, TAIL>(ra, as, min(t + 2, last), full, K, an);
     __syncthreads();
     mfma_half<1, SW>(sa, sW[1], scc, amask, arow0, bbase, h, ws, rwn, 0, sW[0], acc);
@@ -441,14 +449,15 @@ hipError_t launch_swiglu(const float* gu, int64_t M, int64_t I, int64_t ldgu, ui
   return hipGetLastError();
 }
 
-// Number of waves of 256 workgroups a launch of `tiles` workgroups takes.
-static int rounds(int64_t tiles) { return (int)((tiles + 255) / 256); }
-
-hipError_t launch_gemm_mfma(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_g, int M, int K,
-                            const uint8_t* w_codes, const uint8_t* w_scales, int N, const SegTable& st,
-                            const float* w_g, float* out, int64_t ldo, hipStream_t stream) {
+// One form of the MFMA GEMM over all N columns (NWN = 2: 256 x 256 tiles; 1: the
+// narrow 256 x 128 tiles).
+template <int NWN>
+static hipError_t launch_mfma_form(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_g, int M, int K,
+                                   const uint8_t* w_codes, const uint8_t* w_scales, int N, const SegTable& st,
+                                   const float* w_g, float* out, int64_t ldo, hipStream_t stream) {
+  constexpr int kTileN = 128 * NWN, kThreads = 256 * NWN;
   const int num_m = (M + kBM - 1) / kBM;
-  const int n_full = N / kBN * kBN;                    // columns covered by whole tiles
+  const int n_full = N / kTileN * kTileN;              // columns covered by whole tiles
   const int tiles = (K + kTileK - 1) / kTileK;
   // A ragged last tile column costs a whole extra round of workgroups when the
   // whole tiles fill their last round (e.g. 16 x 48 = 768 = 3 x 256).  Then the
@@ -459,14 +468,13 @@ hipError_t launch_gemm_mfma(const uint8_t* a_codes, const uint8_t* a_scales, con
   // per workgroup) that takes 11-13 us, where a K-split of the 256 x 256 tile
   // with fp32 atomics into a zeroed output took 29 us; the result is
   // deterministic.
-  const bool ragged = n_full > 0 && n_full < N &&
-                      rounds((int64_t)num_m * (n_full / kBN)) < rounds((int64_t)num_m * (N / kBN + 1));
-  const int n_main = ragged ? n_full : N;
-  const int grid = num_m * ((n_main + kBN - 1) / kBN);
+  const int n_main = (int)mfma_main_columns(M, N, NWN == 1);
+  const bool ragged = n_main < N;
+  const int grid = num_m * ((n_main + kTileN - 1) / kTileN);
 #define NVFP4_MFMA_LAUNCH(A16, A4, T, EPI, GRID, NLO, NHI)                                                      \
-  gemm_mfma_kernel<A16, A4, T, EPI><<<GRID, kMfThreads, 0, stream>>>(a_codes, a_scales, a_g, M, K, w_codes,     \
-                                                                     w_scales, N, NLO, NHI, st, w_g, out, ldo,  \
-                                                                     SwigluOut{})
+  gemm_mfma_kernel<A16, A4, T, EPI, NWN><<<GRID, kThreads, 0, stream>>>(a_codes, a_scales, a_g, M, K, w_codes,  \
+                                                                        w_scales, N, NLO, NHI, st, w_g, out,    \
+                                                                        ldo, SwigluOut{})
 #define NVFP4_MFMA_DISPATCH(EPI, GRID, NLO, NHI)                                                                 \
   if (K % kTileK == 0) NVFP4_MFMA_LAUNCH(true, true, false, EPI, GRID, NLO, NHI);                               \
   else if (K % 64 == 0) NVFP4_MFMA_LAUNCH(true, true, true, EPI, GRID, NLO, NHI);                               \
@@ -491,6 +499,14 @@ hipError_t launch_gemm_mfma(const uint8_t* a_codes, const uint8_t* a_scales, con
   return hipGetLastError();
 }
 
+hipError_t launch_gemm_mfma(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_g, int M, int K,
+                            const uint8_t* w_codes, const uint8_t* w_scales, int N, const SegTable& st,
+                            const float* w_g, float* out, int64_t ldo, hipStream_t stream) {
+  if (mfma_narrow(M, N))
+    return launch_mfma_form<1>(a_codes, a_scales, a_g, M, K, w_codes, w_scales, N, st, w_g, out, ldo, stream);
+  return launch_mfma_form<2>(a_codes, a_scales, a_g, M, K, w_codes, w_scales, N, st, w_g, out, ldo, stream);
+}
+
 hipError_t launch_gemm_swiglu_quantize(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_g, int M,
                                        int K, const uint8_t* w_codes, const uint8_t* w_scales, int I,
                                        const float* w_g, const float* amax_h, uint8_t* h_codes,
@@ -503,7 +519,7 @@ hipError_t launch_gemm_swiglu_quantize(const uint8_t* a_codes, const uint8_t* a_
   st.end[1] = N;
   const SwigluOut so{amax_h, h_codes, h_scales, h_g_dec, I};
 #define NVFP4_SWIGLU_LAUNCH(A16, A4, T)                                                                          \
-  gemm_mfma_kernel<A16, A4, T, kEpiSwiglu><<<grid, kMfThreads, 0, stream>>>(a_codes, a_scales, a_g, M, K,        \
+  gemm_mfma_kernel<A16, A4, T, kEpiSwiglu, 2><<<grid, kMfThreads, 0, stream>>>(a_codes, a_scales, a_g, M, K,        \
                                                                             w_codes, w_scales, N, 0, N, st, w_g, \
                                                                             nullptr, 0, so)
   if (K % kTileK == 0) NVFP4_SWIGLU_LAUNCH(true, true, false);

@@ -87,6 +87,37 @@ inline int decode_tiles_per_wave(int64_t K, int nw) {
   return per <= 5 ? 5 : (per <= 10 ? 10 : 20);
 }
 
+// The MFMA GEMM's two tile forms: 256 x 256 (eight waves, one workgroup per
+// CU) and the narrow 256 x 128 (four waves doing the same per-wave work, two
+// workgroups per CU).  Their duration in rounds of the wide form (one 256 x 256
+// tile per CU): the wide form takes ceil(tiles / 256); the narrow form runs 512
+// workgroups per round, and a last round of at most 256 workgroups puts one on
+// each of as many CUs (half the work per CU at a lower rate per wave), which
+// costs kNarrowLoneRound of a round: measured 0.76-0.79 at K = 5120, N = 12288
+// (M = 256 / 512: 96 / 192 narrow workgroups, 79 / 82 us, against 103 us for a
+// round of 96 wide ones).
+constexpr double kNarrowLoneRound = 0.78;
+inline double mfma_rounds(int64_t M, int64_t N, bool narrow) {
+  const int64_t num_m = (M + 255) / 256;
+  if (!narrow) return (double)((num_m * ((N + 255) / 256) + kCUs - 1) / kCUs);
+  const int64_t t = num_m * ((N + 127) / 128), rem = t % (2 * kCUs);
+  return (double)(t / (2 * kCUs)) + (rem == 0 ? 0.0 : (rem <= kCUs ? kNarrowLoneRound : 1.0));
+}
+// Columns a form covers with whole tiles where its last, ragged tile column
+// would cost an extra round (that column then runs as the row-blocked
+// weight-streaming GEMM); N otherwise.
+inline int64_t mfma_main_columns(int64_t M, int64_t N, bool narrow) {
+  const int64_t tn = narrow ? 128 : 256, n_full = N / tn * tn;
+  return (n_full > 0 && n_full < N && mfma_rounds(M, n_full, narrow) < mfma_rounds(M, n_full + tn, narrow)) ? n_full
+                                                                                                          : N;
+}
+inline double mfma_cost(int64_t M, int64_t N, bool narrow) {
+  return mfma_rounds(M, mfma_main_columns(M, N, narrow), narrow);
+}
+// The narrow form where it takes fewer rounds (a partial last round of wide
+// tiles); the wide form on ties.
+inline bool mfma_narrow(int64_t M, int64_t N) { return mfma_cost(M, N, true) < mfma_cost(M, N, false); }
+
 // Rows per weight pass of the row-blocked weight-streaming GEMM: 16 for outputs
 // of at most 8 strips (there the activation work dominates: the 64 ragged
 // columns of the GDN in-projection take 12.9 us in 16-row passes with 2 strips

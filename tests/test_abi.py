@@ -269,11 +269,14 @@ def test_convenience_layer_stream_must_be_a_torch_stream():
 
 def test_gemm_form_query():
     """nvfp4_gemm_form: the skinny GEMM for M <= 16 and wherever too few
-    256 x 256 tiles would fill the chip, the MFMA GEMM for the prefill shapes."""
+    256 x 256 tiles would fill the chip, the MFMA GEMM for the prefill shapes
+    (2: its 256 x 128 tiles where 256 x 256 tiles leave a partial last round)."""
     assert nv.nvfp4_gemm_form(-1, 16, 16) == -1
     assert nv.nvfp4_gemm_form(16, 5120, 12288) == 0
     assert nv.nvfp4_gemm_form(17, 5120, 12288) == 0
-    assert nv.nvfp4_gemm_form(512, 5120, 12288) == 1
+    assert nv.nvfp4_gemm_form(512, 5120, 12288) == 2         # 192 narrow tiles instead of 96 wide
+    assert nv.nvfp4_gemm_form(1024, 5120, 12288) == 1        # 192 wide tiles: one round either way
+    assert nv.nvfp4_gemm_form(4096, 5120, 5120) == 2         # 320 wide tiles: a partial second round
     assert nv.nvfp4_gemm_form(8192, 5120, 34816) == 1
     assert nv.nvfp4_gemm_form(4096, 5120, 12352) == 1
     assert nv.nvfp4_gemm_form(32768, 17408, 5120) == 1

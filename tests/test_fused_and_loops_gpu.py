@@ -141,9 +141,12 @@ def test_fused_swiglu_full_prefill_shape():
     assert float(fg.cpu()[0]) == float(og)
 
 
-def test_fused_equals_unfused_mid_size_mfma_form():
-    M, K, I = 2048, 512, 1024
-    assert nv.nvfp4_gemm_form(M, K, 2 * I) == 1
+@pytest.mark.parametrize("M,K,I,form", [(2048, 512, 1024, 2), (2048, 512, 4096, 1)])
+def test_fused_equals_unfused_mid_size_mfma_form(M, K, I, form):
+    """Fused == unfused bit for bit where nvfp4_gemm takes an MFMA form: the fused
+    kernel runs 256 x 256 tiles; the unfused GEMM runs 256 x 128 tiles at I = 1024
+    (128 of them instead of 64) and 256 x 256 at I = 4096 (one full round)."""
+    assert nv.nvfp4_gemm_form(M, K, 2 * I) == form
     rng = np.random.default_rng(46)
     w = (0.02 * rng.standard_normal((2 * I, K))).astype(np.float32)
     w[I:] *= 3.0

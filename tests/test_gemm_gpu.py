@@ -174,6 +174,41 @@ def test_gemm_ragged_column_split_along_k(M, N, K):
     check_linear(x, w, segs, f"ragged column split M={M} N={N} K={K}", rows, cols)
 
 
+@pytest.mark.parametrize("M,N,K", [(1536, 12300, 512), (512, 12288, 1040), (4096, 5120, 256)])
+def test_gemm_narrow_mfma_tiles(M, N, K):
+    """Shapes whose 256 x 256 tiles would leave a partial last round run the MFMA
+    GEMM with 256 x 128 tiles (nvfp4_gemm_form 2): 6 x 97 tiles with the last
+    128-column tile holding 12 columns (1536, 12300); a k tail with rows not
+    16-byte aligned (512, 12288, 1040); 16 x 40 tiles (4096, 5120).  Sampled
+    rows and columns within the oracle's tolerance."""
+    assert nv.nvfp4_gemm_form(M, K, N) == 2
+    rng = np.random.default_rng(3 * M + N + K)
+    segs = [(0, 700), (700, N - 12), (N - 12, N)]
+    w = np.concatenate([(0.02 * (1 + 2 * i) * rng.standard_normal((e - b, K), dtype=np.float32))
+                        for i, (b, e) in enumerate(segs)])
+    x = W.random_act(M + 2 * K, M, K, "student_t")
+    rows = _sample(M, 16, rng, [0, 255, 256, M - 1])
+    cols = _sample(N, 300, rng, [0, 127, 128, N - N % 128 - 1 if N % 128 else N - 129] + list(range(N - 12, N)))
+    check_linear(x, w, segs, f"narrow MFMA tiles M={M} N={N} K={K}", rows, cols)
+
+
+def test_gemm_narrow_and_wide_mfma_tiles_bit_identical():
+    """The two MFMA forms run the same per-wave MFMA sequence on each output: the
+    first module's columns of a 2048 x 8192 product (256 x 256 tiles, one full
+    round) equal, bit for bit, the 2048 x 2048 product of that module alone
+    (256 x 128 tiles), with a k tail (K = 1040)."""
+    M, K, N, n1 = 2048, 1040, 8192, 2048
+    assert nv.nvfp4_gemm_form(M, K, N) == 1 and nv.nvfp4_gemm_form(M, K, n1) == 2
+    rng = np.random.default_rng(77)
+    w = np.float32(0.02) * rng.standard_normal((N, K), dtype=np.float32)
+    w[n1:] *= np.float32(3.0)
+    x = W.random_act(78, M, K, "student_t")
+    say(f"[gemm] narrow vs wide M={M} K={K} N={N}/{n1}")
+    wide = gpu_linear(x, gpu_pack(w, [(0, n1), (n1, N)]))
+    narrow = gpu_linear(x, gpu_pack(w[:n1], [(0, n1)]))
+    assert torch.equal(wide[:, :n1], narrow), "256 x 128 tiles differ from 256 x 256 tiles"
+
+
 def test_gemm_k_zero_and_m_zero():
     w = np.zeros((16, 0), np.float32)
     pw = gpu_pack(w, [(0, 16)])

@@ -19,11 +19,12 @@ pytestmark = pytest.mark.gpu
 
 
 def _sweep_case(seed, form):
-    """A seeded random shape for which nvfp4_gemm takes `form` (1: MFMA GEMM,
-    0: weight-streaming GEMM over row blocks), with 1-5 modules and a ragged k tile."""
+    """A seeded random shape for which nvfp4_gemm takes `form` (1: MFMA GEMM with
+    256 x 256 tiles, 2: with 256 x 128 tiles, 0: weight-streaming GEMM over row
+    blocks), with 1-5 modules and a ragged k tile."""
     rng = np.random.default_rng(7000 + seed)
     while True:
-        if form == 1:
+        if form >= 1:
             M, N = int(rng.integers(300, 1200)), int(rng.integers(2000, 9000))
         else:
             M, N = int(rng.integers(17, 400)), int(rng.integers(1, 1500))
@@ -32,7 +33,7 @@ def _sweep_case(seed, form):
             return rng, M, K, N
 
 
-@pytest.mark.parametrize("form", [1, 0])
+@pytest.mark.parametrize("form", [1, 2, 0])
 @pytest.mark.parametrize("seed", range(12))
 def test_gemm_rows_sweep(seed, form):
     rng, M, K, N = _sweep_case(seed, form)

@@ -34,7 +34,11 @@
 //    reads are bank-conflict free without padding;
 //  * workgroups are numbered XCD-major, then in groups of four row panels, so
 //    the 32 workgroups resident on an XCD share one activation slab in its L2
-//    while they stream weight column panels.
+//    while they stream weight column panels;
+//  * a narrow form (NWN = 1) runs the same per-wave work on a 256 x 128 tile
+//    of four waves, two workgroups per CU, where 256 x 256 tiles would leave a
+//    partial last round (mfma_narrow); each output sees the same MFMA
+//    sequence, so the two forms give bit-identical results.
 #include <algorithm>
 
 #include "common.hpp"

@@ -348,6 +348,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_rows_kernel(
   constexpr int kDepth = 2;
   constexpr int kPer = (16 * MT * S * kStrip + 64 * NW - 1) / (64 * NW);
   static_assert(U >= kDepth, "pipeline depth");
+  static_assert(VW == 1 || VW == 2, "one or two accumulator sets (eight or sixteen waves)");
   static_assert(U % VW == 0, "tile u of an outer iteration belongs to accumulator set u % VW");
   static_assert(S * kStrip <= 64, "one lane of wave 0 per column");
   __shared__ float red[NW][S][MT][4][64];
@@ -486,7 +487,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_rows_kernel(
       w[s] = *reinterpret_cast<const uint4*>(wc[s] + (int64_t)t * kChunkCodes);
       wsv[s] = *reinterpret_cast<const uint16_t*>(ws[s] + (int64_t)t * kChunkScales);
     }
-    if (VW == 1 || (t / NW) % VW == 0)
+    if ((t / NW) % VW == 0)                          // the set of tile t
       batch(acc[0], av, asc, true, w, wsv);
     else
       batch(acc[VW - 1], av, asc, true, w, wsv);
@@ -560,6 +561,7 @@ __global__ __launch_bounds__(64 * NW) void linear_decode_kernel(
   constexpr int kSlots = MAXM * U * (kTileK / kBlock);   // block slots of one wave
   constexpr int kQ = (kSlots + 63) / 64;
   static_assert(U >= 2, "two weight batches in flight");
+  static_assert(kQ <= 32, "one bit of `live` per encode step");
   __shared__ float red[NW][S][4][64];
   // wave-private activation tiles, row-major over (row, tile): slot group
   // v = row * U + u holds the 8 blocks of row `row` in the wave's tile u

@@ -174,13 +174,14 @@ def test_gemm_ragged_column_split_along_k(M, N, K):
     check_linear(x, w, segs, f"ragged column split M={M} N={N} K={K}", rows, cols)
 
 
-@pytest.mark.parametrize("M,N,K", [(1536, 12300, 512), (512, 12288, 1040), (4096, 5120, 256)])
+@pytest.mark.parametrize("M,N,K", [(1536, 12300, 512), (512, 12288, 1040), (4096, 5120, 256), (4096, 5120, 48)])
 def test_gemm_narrow_mfma_tiles(M, N, K):
     """Shapes whose 256 x 256 tiles would leave a partial last round run the MFMA
     GEMM with 256 x 128 tiles (nvfp4_gemm_form 2): 6 x 97 tiles with the last
     128-column tile holding 12 columns (1536, 12300); a k tail with rows not
-    16-byte aligned (512, 12288, 1040); 16 x 40 tiles (4096, 5120).  Sampled
-    rows and columns within the oracle's tolerance."""
+    16-byte aligned (512, 12288, 1040); 16 x 40 tiles (4096, 5120), also with
+    K = 48, below one k tile.  Sampled rows and columns within the oracle's
+    tolerance."""
     assert nv.nvfp4_gemm_form(M, K, N) == 2
     rng = np.random.default_rng(3 * M + N + K)
     segs = [(0, 700), (700, N - 12), (N - 12, N)]

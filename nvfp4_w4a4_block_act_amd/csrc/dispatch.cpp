@@ -21,7 +21,8 @@ bool gemm_prefers_skinny(int64_t M, int64_t K, int64_t N) {
   // Cost models measured at K = 5120 (N = 5120, 12288, 34816):
   //  * the MFMA GEMM needs about 256 tiles of 256 x 256 to fill the chip; a
   //    round of them costs ~2.5 us per 128-k tile however few run (94-128 us
-  //    for M = 17..256);
+  //    for M = 17..256), a partial round of its 256 x 128 tiles 0.78 of that
+  //    (mfma_cost takes the cheaper tiling);
   //  * the row-blocked weight-streaming GEMM streams the packed weight once per
   //    32 or 64 rows at ~6 TB/s (later passes find it in the 256 MB last-level
   //    cache) and decodes both operands for every MFMA, ~4.6e-15 s per

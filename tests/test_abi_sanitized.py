@@ -34,3 +34,21 @@ def test_c_abi_under_sanitizers(tmp_path):
     assert r.returncode == 0, (r.stdout[-4000:], r.stderr[-4000:])
     assert r.stdout.strip().splitlines()[-1].startswith("ok "), r.stdout
     assert "runtime error" not in r.stderr and "AddressSanitizer" not in r.stderr, r.stderr[-4000:]
+
+
+def test_launch_rules_host(tmp_path):
+    """The launch rules of launch.hpp (wave count of the weight-streaming kernels,
+    one-launch row bounds and tiles per wave, MFMA tiling choice): documented
+    values, and a kernel instance for every (M, K) the one-launch layer accepts
+    over a sweep of K and N (tests/abi_host/check_policy.cpp)."""
+    gxx = shutil.which("g++")
+    if gxx is None or not os.path.isdir(ROCM_INCLUDE):
+        pytest.skip("g++ or the HIP runtime headers are not available")
+    exe = str(tmp_path / "check_policy")
+    cmd = [gxx, "-std=c++17", "-O1", "-Wall", "-fsanitize=undefined", "-fno-sanitize-recover=undefined",
+           "-D__HIP_PLATFORM_AMD__", "-I", ROCM_INCLUDE, os.path.join(HOST, "check_policy.cpp"), "-o", exe]
+    b = subprocess.run(cmd, capture_output=True, text=True, timeout=300)
+    assert b.returncode == 0, b.stderr[-4000:]
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stdout[-4000:]
+    assert r.stdout.strip().splitlines()[-1].startswith("ok "), r.stdout

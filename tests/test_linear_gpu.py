@@ -171,7 +171,7 @@ def test_linear_long_k(M, K, N):
     """K beyond 5120: one launch while the wave-local activation tiles fit (up to
     10240 for 8 rows, 20480 for 4), two launches otherwise ((9, 6144), (5, 17408));
     either way bit-identical to quantize + GEMM and within the oracle's tolerance
-    on sampled columns.  N = 700 (15 workgroups) runs sixteen waves per workgroup
+    on sampled columns.  N = 700 (44 workgroups) runs sixteen waves per workgroup
     (row-bound instances 1, 4 and 8 at five tiles per wave, 1 and 4 at ten);
     N = 12300 (257 workgroups) runs eight (ten and twenty tiles per wave)."""
     rng = np.random.default_rng(900 + M + K + N)

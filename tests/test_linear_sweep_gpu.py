@@ -1,10 +1,13 @@
-"""Seeded randomized parity sweep of the one-launch decode-form linear layer
-(nvfp4_linear with 1 <= M <= 16, K <= 5120): random token counts, K (multiples
-of 16, most of them not multiples of the 128-k tile), output widths, module
-splits, activation distributions and dynamic or calibrated activation scales.
-Each case must be bit-identical to nvfp4_quantize_act followed by nvfp4_gemm and
-within the GEMM tolerance of the oracle (every output of small cases, a sample of
-columns of larger ones); the activation codes and scales must equal the oracle's.
+"""Seeded randomized parity sweep of the decode-form linear layer (nvfp4_linear
+with 1 <= M <= 16): random token counts, K (multiples of 16, most of them not
+multiples of the 128-k tile), output widths, module splits, activation
+distributions and dynamic or calibrated activation scales -- 40 cases with
+K <= 5120 (one launch, eight waves) and 16 with 5120 < K <= 20496 (one launch
+where the rows fit, else quantizer + GEMM; sixteen waves per workgroup on
+narrow outputs, eight on outputs of at least 256 workgroups).  Each case must be
+bit-identical to nvfp4_quantize_act followed by nvfp4_gemm and within the GEMM
+tolerance of the oracle (every output of small cases, a sample of columns of
+larger ones); the activation codes and scales must equal the oracle's.
 """
 import numpy as np
 import pytest
@@ -18,18 +21,23 @@ from oracle import nvfp4 as Q
 pytestmark = pytest.mark.gpu
 
 CASES = 40
+LONG_CASES = 16
 
 
-def case(seed):
-    rng = np.random.default_rng(9000 + seed)
+def case(seed, long_k=False):
+    rng = np.random.default_rng((9500 if long_k else 9000) + seed)
     M = int(rng.integers(1, 17))
-    K = 16 * int(rng.integers(1, 321))
-    N = int(rng.integers(1, 2049))
+    if long_k:
+        K = 16 * int(rng.integers(321, 1282))                  # 5136 .. 20496
+        N = int(rng.integers(12256, 13000)) if seed % 4 == 0 else int(rng.integers(1, 3000))
+    else:
+        K = 16 * int(rng.integers(1, 321))
+        N = int(rng.integers(1, 2049))
     nseg = int(rng.integers(1, min(N, 5) + 1))
     cuts = sorted(rng.choice(np.arange(1, N), nseg - 1, replace=False).tolist()) if nseg > 1 else []
     bounds = [0] + cuts + [N]
     segs = list(zip(bounds[:-1], bounds[1:]))
-    w = np.concatenate([(0.03 * (1 + 2 * i) * rng.standard_normal((e - b, K))).astype(np.float32)
+    w = np.concatenate([np.float32(0.03 * (1 + 2 * i)) * rng.standard_normal((e - b, K), dtype=np.float32)
                         for i, (b, e) in enumerate(segs)])
     dist = ("normal", "student_t", "uniform")[seed % 3]
     x = W.random_act(31 * seed + 7, M, K, dist)
@@ -45,7 +53,15 @@ def case(seed):
 
 @pytest.mark.parametrize("seed", range(CASES))
 def test_linear_decode_sweep(seed):
-    M, K, N, segs, w, x_bits, amax = case(seed)
+    _check(seed, *case(seed))
+
+
+@pytest.mark.parametrize("seed", range(LONG_CASES))
+def test_linear_long_k_sweep(seed):
+    _check(seed, *case(seed, long_k=True))
+
+
+def _check(seed, M, K, N, segs, w, x_bits, amax):
     say(f"[sweep] seed={seed} M={M} K={K} N={N} nseg={len(segs)} static={amax is not None}")
     pw = gpu_pack(w, segs)
     x = to_dev_bf16(x_bits)

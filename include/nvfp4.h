@@ -49,7 +49,8 @@
 extern "C" {
 #endif
 
-#define NVFP4_ABI_VERSION 1
+/* 2: nvfp4_gemm_form may return 2 (the MFMA GEMM with 256 x 128 tiles). */
+#define NVFP4_ABI_VERSION 2
 #define NVFP4_MAX_SEGMENTS 16
 
 typedef enum {

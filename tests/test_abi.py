@@ -28,7 +28,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert nv.nvfp4_abi_version() == 1
+    assert nv.nvfp4_abi_version() == 2
     for s in range(7):
         assert nv.nvfp4_status_str(s)
     assert nv.nvfp4_status_str(99) == "unknown status"

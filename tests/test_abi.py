@@ -28,7 +28,10 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert nv.nvfp4_abi_version() == 2
+    """The library reports the header's ABI version (the check build() makes)."""
+    with open(os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "nvfp4.h")) as f:
+        want = int(re.search(r"#define NVFP4_ABI_VERSION (\d+)", f.read()).group(1))
+    assert want == 2 and nv.nvfp4_abi_version() == want
     for s in range(7):
         assert nv.nvfp4_status_str(s)
     assert nv.nvfp4_status_str(99) == "unknown status"

@@ -44,18 +44,37 @@ constexpr int kAmaxLoads = 4;                // amax pass: 16-byte loads in flig
 constexpr int64_t kMaxEncodeGrid = 1 << 20;  // encoder workgroups (blocks beyond loop)
 constexpr int kFuseParts = 64;               // partial maxima an encode workgroup reduces itself
 
+// Tensors whose bf16 bytes exceed the 256 MB last-level cache are streamed with
+// non-temporal loads and stores (ST): nothing of them survives in a cache for
+// the next pass or launch, and the hint keeps them from evicting what would.
+// Smaller tensors keep plain accesses, so the encode pass finds the data the
+// maximum pass has just read.
+constexpr int64_t kStreamBytes = int64_t(256) << 20;
+
 // Encode the bf16 block (m, b) of x.
+template <bool ST>
 __device__ __forceinline__ void encode_block_at(const uint16_t* __restrict__ x, int64_t ldx, int K, int64_t m,
                                                 int b, const EncCtx& cx, uint8_t* __restrict__ codes,
                                                 uint8_t* __restrict__ scales) {
-  const uint4* p = reinterpret_cast<const uint4*>(x + m * ldx + (int64_t)b * kBlock);
-  encode_bf16_chunks(p[0], p[1], cx, codes + m * (K / 2) + (int64_t)b * 8, scales + m * (K / kBlock) + b);
+  const uint16_t* p = x + m * ldx + (int64_t)b * kBlock;
+  uint8_t* cdst = codes + m * (K / 2) + (int64_t)b * 8;
+  uint8_t* sdst = scales + m * (K / kBlock) + b;
+  if constexpr (ST) {
+    uint2 c;
+    const uint32_t sc = encode_bf16_block(ld_stream16(p), ld_stream16(p + 8), cx, c);
+    st_stream8(cdst, c);
+    st_stream1(sdst, sc);
+  } else {
+    const uint4* q = reinterpret_cast<const uint4*>(p);
+    encode_bf16_chunks(q[0], q[1], cx, cdst, sdst);
+  }
 }
 
 // ---- whole-tensor |x| maximum on bf16 bit patterns ------------------------------
 // For finite bf16, |x| orders exactly like (bits & 0x7FFF) as an unsigned integer.
 // 8-element (16-byte) chunks of the M x K tensor, row-major over the valid
 // region; each trip issues kAmaxLoads chunk loads before reducing any.
+template <bool ST>
 __device__ __forceinline__ uint32_t chunk_absmax(const uint16_t* __restrict__ x, int64_t ldx, int K,
                                                  int64_t M, int64_t first, int64_t stride) {
   const int64_t cpr = K / 8;
@@ -70,7 +89,7 @@ __device__ __forceinline__ uint32_t chunk_absmax(const uint16_t* __restrict__ x,
       if (c < total) {
         const int64_t r = c / cpr;
         const int64_t k = (c - r * cpr) * 8;
-        v[u] = *reinterpret_cast<const uint4*>(x + r * ldx + k);
+        v[u] = ST ? ld_stream16(x + r * ldx + k) : *reinterpret_cast<const uint4*>(x + r * ldx + k);
       }
     }
 #pragma unroll
@@ -79,12 +98,13 @@ __device__ __forceinline__ uint32_t chunk_absmax(const uint16_t* __restrict__ x,
   return m;
 }
 
+template <bool ST>
 __global__ __launch_bounds__(kQThreads) void amax_partial_kernel(const uint16_t* __restrict__ x, int64_t M,
                                                                  int K, int64_t ldx,
                                                                  uint32_t* __restrict__ partial) {
   __shared__ uint32_t red[kQThreads / 64];
-  const uint32_t m = chunk_absmax(x, ldx, K, M, (int64_t)blockIdx.x * blockDim.x + threadIdx.x,
-                                  (int64_t)gridDim.x * blockDim.x);
+  const uint32_t m = chunk_absmax<ST>(x, ldx, K, M, (int64_t)blockIdx.x * blockDim.x + threadIdx.x,
+                                      (int64_t)gridDim.x * blockDim.x);
   const uint32_t r = block_reduce_max(m, red);
   if (threadIdx.x == 0) partial[blockIdx.x] = r;
 }
@@ -102,6 +122,7 @@ __global__ __launch_bounds__(kQThreads) void amax_finalize_kernel(const uint32_t
 // Encode with the tensor maximum: *amax (calibrated, or the dynamic one the two
 // kernels above left in the workspace), or, with `partial`, the largest of the
 // nparts partial maxima (bf16 bit patterns), reduced by every workgroup.
+template <bool ST>
 __global__ __launch_bounds__(kQThreads) void quantize_act_kernel(
     const uint16_t* __restrict__ x, int64_t M, int K, int64_t ldx, const float* __restrict__ amax_in,
     const uint32_t* __restrict__ partial, int nparts, uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
@@ -127,7 +148,7 @@ __global__ __launch_bounds__(kQThreads) void quantize_act_kernel(
        i += (int64_t)gridDim.x * blockDim.x) {
     const int64_t m = i / nb;
     const int b = (int)(i - m * nb);
-    encode_block_at(x, ldx, K, m, b, cx, codes, scales);
+    encode_block_at<ST>(x, ldx, K, m, b, cx, codes, scales);
   }
 }
 
@@ -202,9 +223,17 @@ hipError_t launch_quantize_act(const uint16_t* x, int64_t M, int64_t K, int64_t 
   }
   // One block per thread (grid-stride beyond kMaxEncodeGrid workgroups).
   const int grid = (int)std::min<int64_t>((blocks + kQThreads - 1) / kQThreads, kMaxEncodeGrid);
+  const bool st = M * K * 2 > kStreamBytes;
+  auto encode = [&](const float* amax, const uint32_t* partial, int nparts) {
+    if (st)
+      quantize_act_kernel<true><<<grid, kQThreads, 0, stream>>>(x, M, (int)K, ldx, amax, partial, nparts, codes,
+                                                                scales, g_dec_out);
+    else
+      quantize_act_kernel<false><<<grid, kQThreads, 0, stream>>>(x, M, (int)K, ldx, amax, partial, nparts, codes,
+                                                                 scales, g_dec_out);
+  };
   if (amax_in) {
-    quantize_act_kernel<<<grid, kQThreads, 0, stream>>>(x, M, (int)K, ldx, amax_in, nullptr, 0, codes, scales,
-                                                        g_dec_out);
+    encode(amax_in, nullptr, 0);
   } else if (M * K <= kSmallElems) {
     const int grid = (int)((blocks + kSmallThreads - 1) / kSmallThreads);
     quantize_act_small_kernel<<<grid, kSmallThreads, 0, stream>>>(x, (int)M, (int)K, ldx, 1.0f / (float)(K / 8),
@@ -216,14 +245,15 @@ hipError_t launch_quantize_act(const uint16_t* x, int64_t M, int64_t K, int64_t 
     // mid-size tensors: at most kFuseParts partials, each workgroup two chunks per thread
     if (pgrid <= kFuseParts) pgrid = (int)std::max<int64_t>(1, std::min<int64_t>(kFuseParts, chunks / (kQThreads * 2)));
     float* amax = reinterpret_cast<float*>(partial + kPartials);
-    amax_partial_kernel<<<pgrid, kQThreads, 0, stream>>>(x, M, (int)K, ldx, partial);
+    if (st)
+      amax_partial_kernel<true><<<pgrid, kQThreads, 0, stream>>>(x, M, (int)K, ldx, partial);
+    else
+      amax_partial_kernel<false><<<pgrid, kQThreads, 0, stream>>>(x, M, (int)K, ldx, partial);
     if (pgrid <= kFuseParts) {
-      quantize_act_kernel<<<grid, kQThreads, 0, stream>>>(x, M, (int)K, ldx, nullptr, partial, pgrid, codes, scales,
-                                                          g_dec_out);
+      encode(nullptr, partial, pgrid);
     } else {
       amax_finalize_kernel<<<1, kQThreads, 0, stream>>>(partial, pgrid, amax);
-      quantize_act_kernel<<<grid, kQThreads, 0, stream>>>(x, M, (int)K, ldx, amax, nullptr, 0, codes, scales,
-                                                          g_dec_out);
+      encode(amax, nullptr, 0);
     }
   }
   return hipGetLastError();
@@ -246,7 +276,7 @@ hipError_t launch_amax_observe(const uint16_t* x, int64_t M, int64_t K, int64_t 
   uint32_t* partial = static_cast<uint32_t*>(workspace);
   const int64_t chunks = M * (K / 8);
   const int pgrid = (int)std::max<int64_t>(1, std::min<int64_t>(kPartials, chunks / (kQThreads * 16)));
-  amax_partial_kernel<<<pgrid, kQThreads, 0, stream>>>(x, M, (int)K, ldx, partial);
+  amax_partial_kernel<false><<<pgrid, kQThreads, 0, stream>>>(x, M, (int)K, ldx, partial);
   amax_observe_finalize_kernel<<<1, kQThreads, 0, stream>>>(partial, pgrid, running);
   return hipGetLastError();
 }

@@ -88,14 +88,12 @@ __device__ __forceinline__ half8_t decode8(uint32_t w, half2_t s2) {
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
-// ---- streaming accesses ---------------------------------------------------------
-// Loads and stores with the non-temporal hint, for bytes a launch touches once
-// and no later launch finds in a cache anyway: the weight stream of the
-// decode-form GEMMs, and activation tensors larger than the last-level cache.
-// The data and the instructions are the same as plain accesses (only the
-// cache policy bit differs), so results do not depend on the choice.
+// ---- streaming loads ------------------------------------------------------------
+// Loads with the non-temporal hint, for bytes a launch reads once and no later
+// launch finds in a cache anyway: the weight stream of the decode-form GEMMs,
+// and the maximum pass over activation tensors larger than the last-level
+// cache.  Only the cache policy bit differs from a plain load.
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ uint4 ld_stream16(const void* p) {
   const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
@@ -104,13 +102,6 @@ __device__ __forceinline__ uint4 ld_stream16(const void* p) {
 __device__ __forceinline__ uint32_t ld_stream2(const void* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(p));
 }
-__device__ __forceinline__ void st_stream8(void* p, uint2 v) {
-  u32x2_t w;
-  w.x = v.x;
-  w.y = v.y;
-  __builtin_nontemporal_store(w, reinterpret_cast<u32x2_t*>(p));
-}
-__device__ __forceinline__ void st_stream1(uint8_t* p, uint32_t v) { __builtin_nontemporal_store((uint8_t)v, p); }
 
 __device__ __forceinline__ uint32_t u4_dword_sel(uint4 v, int d) {
   return d == 0 ? v.x : d == 1 ? v.y : d == 2 ? v.z : v.w;

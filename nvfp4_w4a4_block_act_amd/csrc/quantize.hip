@@ -44,20 +44,38 @@ constexpr int kAmaxLoads = 4;                // amax pass: 16-byte loads in flig
 constexpr int64_t kMaxEncodeGrid = 1 << 20;  // encoder workgroups (blocks beyond loop)
 constexpr int kFuseParts = 64;               // partial maxima an encode workgroup reduces itself
 
-// The maximum pass over tensors whose bf16 bytes exceed the 256 MB last-level
-// cache uses non-temporal loads (ST): none of those bytes survive in a cache
-// until the encode pass anyway (32768 x 17408: 212 -> 193 us).  Smaller tensors
-// keep plain loads, so the encode pass finds what the maximum pass has just
-// read (the hint made 4096 x 5120 9% slower).  Non-temporal loads and stores in
-// the encode pass gave nothing measurable and wrote 1.5% more bytes.
+// Tensors whose bf16 bytes exceed the 256 MB last-level cache are streamed (ST):
+// the maximum pass and the encode pass read x, and the encode pass writes the
+// codes and scales, with the non-temporal hint, since none of those bytes
+// survive in a cache until they are used again (32768 x 17408: maximum pass
+// 212 -> 187 us; calibrated-scale call 260 -> 246 us, where the hint on the
+// stores is what counts).  Smaller tensors keep plain accesses, so the encode
+// pass finds what the maximum pass has just read (the hint made 4096 x 5120
+// 9% slower).
 constexpr int64_t kStreamBytes = int64_t(256) << 20;
 
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+
 // Encode the bf16 block (m, b) of x.
+template <bool ST>
 __device__ __forceinline__ void encode_block_at(const uint16_t* __restrict__ x, int64_t ldx, int K, int64_t m,
                                                 int b, const EncCtx& cx, uint8_t* __restrict__ codes,
                                                 uint8_t* __restrict__ scales) {
-  const uint4* p = reinterpret_cast<const uint4*>(x + m * ldx + (int64_t)b * kBlock);
-  encode_bf16_chunks(p[0], p[1], cx, codes + m * (K / 2) + (int64_t)b * 8, scales + m * (K / kBlock) + b);
+  const uint16_t* p = x + m * ldx + (int64_t)b * kBlock;
+  uint8_t* cdst = codes + m * (K / 2) + (int64_t)b * 8;
+  uint8_t* sdst = scales + m * (K / kBlock) + b;
+  if constexpr (ST) {
+    uint2 c;
+    const uint32_t sc = encode_bf16_block(ld_stream16(p), ld_stream16(p + 8), cx, c);
+    u32x2_t w;
+    w.x = c.x;
+    w.y = c.y;
+    __builtin_nontemporal_store(w, reinterpret_cast<u32x2_t*>(cdst));
+    __builtin_nontemporal_store((uint8_t)sc, sdst);
+  } else {
+    const uint4* q = reinterpret_cast<const uint4*>(p);
+    encode_bf16_chunks(q[0], q[1], cx, cdst, sdst);
+  }
 }
 
 // ---- whole-tensor |x| maximum on bf16 bit patterns ------------------------------
@@ -112,6 +130,7 @@ __global__ __launch_bounds__(kQThreads) void amax_finalize_kernel(const uint32_t
 // Encode with the tensor maximum: *amax (calibrated, or the dynamic one the two
 // kernels above left in the workspace), or, with `partial`, the largest of the
 // nparts partial maxima (bf16 bit patterns), reduced by every workgroup.
+template <bool ST>
 __global__ __launch_bounds__(kQThreads) void quantize_act_kernel(
     const uint16_t* __restrict__ x, int64_t M, int K, int64_t ldx, const float* __restrict__ amax_in,
     const uint32_t* __restrict__ partial, int nparts, uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
@@ -137,7 +156,7 @@ __global__ __launch_bounds__(kQThreads) void quantize_act_kernel(
        i += (int64_t)gridDim.x * blockDim.x) {
     const int64_t m = i / nb;
     const int b = (int)(i - m * nb);
-    encode_block_at(x, ldx, K, m, b, cx, codes, scales);
+    encode_block_at<ST>(x, ldx, K, m, b, cx, codes, scales);
   }
 }
 
@@ -212,9 +231,17 @@ hipError_t launch_quantize_act(const uint16_t* x, int64_t M, int64_t K, int64_t 
   }
   // One block per thread (grid-stride beyond kMaxEncodeGrid workgroups).
   const int grid = (int)std::min<int64_t>((blocks + kQThreads - 1) / kQThreads, kMaxEncodeGrid);
+  const bool st = M * K * 2 > kStreamBytes;
+  auto encode = [&](const float* amax, const uint32_t* partial, int nparts) {
+    if (st)
+      quantize_act_kernel<true><<<grid, kQThreads, 0, stream>>>(x, M, (int)K, ldx, amax, partial, nparts, codes,
+                                                                scales, g_dec_out);
+    else
+      quantize_act_kernel<false><<<grid, kQThreads, 0, stream>>>(x, M, (int)K, ldx, amax, partial, nparts, codes,
+                                                                 scales, g_dec_out);
+  };
   if (amax_in) {
-    quantize_act_kernel<<<grid, kQThreads, 0, stream>>>(x, M, (int)K, ldx, amax_in, nullptr, 0, codes, scales,
-                                                        g_dec_out);
+    encode(amax_in, nullptr, 0);
   } else if (M * K <= kSmallElems) {
     const int grid = (int)((blocks + kSmallThreads - 1) / kSmallThreads);
     quantize_act_small_kernel<<<grid, kSmallThreads, 0, stream>>>(x, (int)M, (int)K, ldx, 1.0f / (float)(K / 8),
@@ -226,17 +253,15 @@ hipError_t launch_quantize_act(const uint16_t* x, int64_t M, int64_t K, int64_t 
     // mid-size tensors: at most kFuseParts partials, each workgroup two chunks per thread
     if (pgrid <= kFuseParts) pgrid = (int)std::max<int64_t>(1, std::min<int64_t>(kFuseParts, chunks / (kQThreads * 2)));
     float* amax = reinterpret_cast<float*>(partial + kPartials);
-    if (M * K * 2 > kStreamBytes)
+    if (st)
       amax_partial_kernel<true><<<pgrid, kQThreads, 0, stream>>>(x, M, (int)K, ldx, partial);
     else
       amax_partial_kernel<false><<<pgrid, kQThreads, 0, stream>>>(x, M, (int)K, ldx, partial);
     if (pgrid <= kFuseParts) {
-      quantize_act_kernel<<<grid, kQThreads, 0, stream>>>(x, M, (int)K, ldx, nullptr, partial, pgrid, codes, scales,
-                                                          g_dec_out);
+      encode(nullptr, partial, pgrid);
     } else {
       amax_finalize_kernel<<<1, kQThreads, 0, stream>>>(partial, pgrid, amax);
-      quantize_act_kernel<<<grid, kQThreads, 0, stream>>>(x, M, (int)K, ldx, amax, nullptr, 0, codes, scales,
-                                                          g_dec_out);
+      encode(amax, nullptr, 0);
     }
   }
   return hipGetLastError();

@@ -153,3 +153,41 @@ def test_leading_dimension_two_pass(static):
 
 def test_all_zero_two_pass():
     check(np.zeros((300, 1024), np.uint16), None, "all zero, two-pass")
+
+
+@pytest.mark.parametrize("static", [False, True])
+def test_streamed_tensor_strided(static):
+    """A strided view whose bf16 bytes exceed 256 MB (4099 x 32784 inside rows of
+    32832; K % 128 != 0), so the maximum and encode passes take their
+    non-temporal instances: g_dec exact, and the codes and scales of 48 sampled
+    rows (the first, the last and the one holding the maximum among them)
+    bit-exact against the oracle with the same tensor maximum (half of it when
+    calibrated, which saturates blocks)."""
+    import torch
+    import nvfp4_w4a4_block_act_amd as nv
+    from gpu_util import to_dev_bf16
+    M, K, ldx = 4099, 32784, 32832
+    assert M * K * 2 > 256 << 20
+    bits = random_act(21, M, ldx, "normal")
+    view_bits = bits[:, 16:16 + K]
+    mag = view_bits & 0x7FFF
+    at = int(np.argmax(mag))
+    amax = float(bf16_to_f32(np.array([mag.flat[at]], np.uint16))[0])
+    del mag
+    if static:
+        amax = float(np.float32(amax) * np.float32(0.5))
+    say(f"[quant streamed] static={static} amax={amax}")
+    full = to_dev_bf16(bits)
+    am = torch.tensor([amax], dtype=torch.float32, device="cuda:0") if static else None
+    c, s, g = nv.quantize_act(full[:, 16:16 + K], am)
+    torch.cuda.synchronize()
+    del full
+    rng = np.random.default_rng(22 + static)
+    rows = np.unique(np.concatenate([rng.choice(M, 45, replace=False), [0, M - 1, at // K]]))
+    oc, os_, og, _ = Q.quantize(bf16_to_f32(np.ascontiguousarray(view_bits[rows])), np.float32(amax))
+    if static:
+        assert (os_ == 0x7E).any()
+    assert np.float32(g.cpu().numpy()[0]) == og
+    rows_t = torch.from_numpy(rows).to("cuda:0")
+    assert np.array_equal(c.index_select(0, rows_t).cpu().numpy(), oc)
+    assert np.array_equal(s.index_select(0, rows_t).cpu().numpy(), os_)

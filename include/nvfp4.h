@@ -27,7 +27,7 @@
  *    status except NVFP4_EHIP means nothing was enqueued.  NVFP4_EHIP means the
  *    HIP runtime rejected a launch (hipGetLastError); a call that enqueues
  *    several kernels (the two-pass quantizer, nvfp4_linear outside its
- *    one-launch range, a GEMM with a ragged last tile column) may already have
+ *    one-launch range, some GEMMs with a ragged last tile column) may already have
  *    enqueued the kernels before the rejected one, and all of its outputs are
  *    then unspecified.  The library never prints and never aborts.
  *  - Element codes are packed two per byte, the even k in the low nibble:

@@ -43,6 +43,7 @@
 
 #include "common.hpp"
 #include "quant_device.hpp"
+#include "rows_body.hpp"
 
 namespace nvfp4 {
 
@@ -241,19 +242,43 @@ __device__ __forceinline__ float swiglu_f32(float g, float u) { return g / (1.0f
 
 constexpr int kHRow = 128 + 8;   // bf16 per LDS row of the SwiGLU tile (16-byte pad)
 
+// The ragged last tile column of a launch whose whole tiles fill their last
+// round, run by workgroups nmain.. of the same launch as the row-blocked
+// weight-streaming GEMM (rows_block over 16-row blocks of RS strips): they start
+// as the whole tiles' workgroups finish, with no second launch.
+struct RaggedCols {
+  const uint8_t* w_codes;   // the strips of columns n_full..
+  const uint8_t* w_scales;
+  const float* w_g;         // module scales from the first module with such columns
+  float* out;               // output column n_full
+  SegTable st;              // segment table shifted to column n_full
+  int N;                    // ragged columns
+  int nmain;                // workgroups of the whole tiles
+};
+
 // One launch covers output columns [n_lo, n_hi) (n_lo a multiple of 256).  With
 // kEpiSwiglu the weight is the interleaved
 // gate/up packing (columns 256 t .. 256 t + 127 are gate rows 128 t .., the next
 // 128 the matching up rows), and the workgroup writes the NVFP4 encoding of
 // h[m][j] = bf16(silu(g) * u) for its 128 j instead of fp32 output.
 // NWN: waves along N (2: the 256 x 256 tile of eight waves; 1: the narrow
-// 256 x 128 tile of four waves, two workgroups per CU).
-template <bool AL16, bool AL4, bool TAIL, int EPI, int NWN>
+// 256 x 128 tile of four waves, two workgroups per CU).  RS > 0: workgroups
+// from rg.nmain on run the ragged column (RaggedCols) with RS strips each.
+template <bool AL16, bool AL4, bool TAIL, int EPI, int NWN, int RS>
 __global__ __launch_bounds__(256 * NWN, 3 - NWN) void gemm_mfma_kernel(
     const uint8_t* __restrict__ a_codes, const uint8_t* __restrict__ a_scales, const float* __restrict__ a_g,
     int M, int K, const uint8_t* __restrict__ w_codes, const uint8_t* __restrict__ w_scales, int N, int n_lo,
-    int n_hi, SegTable st, const float* __restrict__ w_g, float* __restrict__ out, int64_t ldo, SwigluOut so) {
+    int n_hi, SegTable st, const float* __restrict__ w_g, float* __restrict__ out, int64_t ldo, SwigluOut so,
+    RaggedCols rg) {
   constexpr bool SW = EPI == kEpiSwiglu;
+  if constexpr (RS > 0) {
+    static_assert(NWN == 2 && AL16 && !TAIL && !SW, "ragged workgroups: 512 threads, whole k tiles");
+    if ((int)blockIdx.x >= rg.nmain) {             // uniform per workgroup
+      rows_block<RS, 8, 1, kSkU, true, 1>((int)blockIdx.x - rg.nmain, a_codes, a_scales, a_g, M, K, rg.w_codes,
+                                          rg.w_scales, rg.N, rg.st, rg.w_g, rg.out, ldo);
+      return;
+    }
+  }
   constexpr int kThreads = 256 * NWN, kTileN = 128 * NWN, NS = 1024 / kThreads;
   static_assert(!SW || NWN == 2, "the SwiGLU epilogue pairs gate and up columns of a 256-column tile");
   __shared__ uint4 sW[2][kTileN * kHalfRow];           // decoded weight half-tiles, 2 x 36 KB (2 x 18 KB narrow)
@@ -475,10 +500,50 @@ static hipError_t launch_mfma_form(const uint8_t* a_codes, const uint8_t* a_scal
   const int n_main = (int)mfma_main_columns(M, N, NWN == 1);
   const bool ragged = n_main < N;
   const int grid = num_m * ((n_main + kTileN - 1) / kTileN);
+  // The ragged strips as the row-blocked GEMM: its segment table shifted to them.
+  SegTable sr{};
+  int first = 0;                                       // first module with columns at or past n_full
+  int64_t rstrip = 0;
+  if (ragged) {
+    while (st.end[first] <= n_full) ++first;
+    sr.nseg = st.nseg - first;
+    for (int i = 0; i < sr.nseg; ++i) sr.end[i] = st.end[first + i] - n_full;
+    rstrip = n_full / kStrip;
+  }
+  const int nr = N - n_full;
+  // Merged into this launch where the ragged part takes 16-row blocks in the
+  // eight-wave order and every k tile is whole (the GDN in-projection: 64
+  // columns, 256 workgroups of 4 strips after the 768 whole tiles); otherwise a
+  // second launch of the same kernel (gemm_rows_kernel) follows.
+  if constexpr (NWN == 2) {
+    if (ragged && K % kTileK == 0 && rows_per_pass(M, nr) == 16 && stream_waves(K, nr) == 8) {
+      const int rstrips = (nr + kStrip - 1) / kStrip;
+      const int64_t blocks = (M + 15) / 16;
+      const int rs = pick_strips_rows(rstrips, blocks, 1);
+      const int64_t rwgs = (int64_t)(rstrips + rs - 1) / rs * blocks;
+      if (grid + rwgs <= INT32_MAX) {
+        const RaggedCols rg{w_codes + rstrip * tiles * kChunkCodes, w_scales + rstrip * tiles * kChunkScales,
+                            w_g + first, out + n_full, sr, nr, grid};
+        const int g2 = (int)(grid + rwgs);
+#define NVFP4_MFMA_RAGGED(RS)                                                                                   \
+  gemm_mfma_kernel<true, true, false, kEpiStore, 2, RS><<<g2, kThreads, 0, stream>>>(                          \
+      a_codes, a_scales, a_g, M, K, w_codes, w_scales, N, 0, n_main, st, w_g, out, ldo, SwigluOut{}, rg)
+        switch (rs) {
+          case 1: NVFP4_MFMA_RAGGED(1); break;
+          case 2: NVFP4_MFMA_RAGGED(2); break;
+          case 3: NVFP4_MFMA_RAGGED(3); break;
+          default: NVFP4_MFMA_RAGGED(4);
+        }
+#undef NVFP4_MFMA_RAGGED
+        return hipGetLastError();
+      }
+    }
+  }
 #define NVFP4_MFMA_LAUNCH(A16, A4, T, EPI, GRID, NLO, NHI)                                                      \
-  gemm_mfma_kernel<A16, A4, T, EPI, NWN><<<GRID, kThreads, 0, stream>>>(a_codes, a_scales, a_g, M, K, w_codes,  \
-                                                                        w_scales, N, NLO, NHI, st, w_g, out,    \
-                                                                        ldo, SwigluOut{})
+  gemm_mfma_kernel<A16, A4, T, EPI, NWN, 0><<<GRID, kThreads, 0, stream>>>(a_codes, a_scales, a_g, M, K,        \
+                                                                           w_codes, w_scales, N, NLO, NHI, st,  \
+                                                                           w_g, out, ldo, SwigluOut{},          \
+                                                                           RaggedCols{})
 #define NVFP4_MFMA_DISPATCH(EPI, GRID, NLO, NHI)                                                                 \
   if (K % kTileK == 0) NVFP4_MFMA_LAUNCH(true, true, false, EPI, GRID, NLO, NHI);                               \
   else if (K % 64 == 0) NVFP4_MFMA_LAUNCH(true, true, true, EPI, GRID, NLO, NHI);                               \
@@ -488,15 +553,9 @@ static hipError_t launch_mfma_form(const uint8_t* a_codes, const uint8_t* a_scal
   if (ragged) {
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    SegTable sr{};
-    int first = 0;                                     // first module with columns at or past n_full
-    while (st.end[first] <= n_full) ++first;
-    sr.nseg = st.nseg - first;
-    for (int i = 0; i < sr.nseg; ++i) sr.end[i] = st.end[first + i] - n_full;
-    const int64_t strip = n_full / kStrip;
-    return launch_gemm_skinny(a_codes, a_scales, a_g, M, K, w_codes + strip * tiles * kChunkCodes,
-                              w_scales + strip * tiles * kChunkScales, N - n_full, sr, w_g + first, out + n_full,
-                              ldo, stream);
+    return launch_gemm_skinny(a_codes, a_scales, a_g, M, K, w_codes + rstrip * tiles * kChunkCodes,
+                              w_scales + rstrip * tiles * kChunkScales, nr, sr, w_g + first, out + n_full, ldo,
+                              stream);
   }
 #undef NVFP4_MFMA_DISPATCH
 #undef NVFP4_MFMA_LAUNCH
@@ -523,9 +582,8 @@ hipError_t launch_gemm_swiglu_quantize(const uint8_t* a_codes, const uint8_t* a_
   st.end[1] = N;
   const SwigluOut so{amax_h, h_codes, h_scales, h_g_dec, I};
 #define NVFP4_SWIGLU_LAUNCH(A16, A4, T)                                                                          \
-  gemm_mfma_kernel<A16, A4, T, kEpiSwiglu, 2><<<grid, kMfThreads, 0, stream>>>(a_codes, a_scales, a_g, M, K,        \
-                                                                            w_codes, w_scales, N, 0, N, st, w_g, \
-                                                                            nullptr, 0, so)
+  gemm_mfma_kernel<A16, A4, T, kEpiSwiglu, 2, 0><<<grid, kMfThreads, 0, stream>>>(                               \
+      a_codes, a_scales, a_g, M, K, w_codes, w_scales, N, 0, N, st, w_g, nullptr, 0, so, RaggedCols{})
   if (K % kTileK == 0) NVFP4_SWIGLU_LAUNCH(true, true, false);
   else if (K % 64 == 0) NVFP4_SWIGLU_LAUNCH(true, true, true);
   else if (K % 32 == 0) NVFP4_SWIGLU_LAUNCH(true, false, true);

@@ -159,10 +159,12 @@ def test_gemm_subnormal_block_scales(M):
 @pytest.mark.parametrize("M,N,K", [(300, 32808, 1040), (520, 65584, 512)])
 def test_gemm_ragged_column_split_along_k(M, N, K):
     """Shapes whose whole 256x256 tiles exactly fill their last round of 256
-    workgroups (2 x 128 and 3 x 256 tiles): the ragged last column then runs as a
-    separate launch of the weight-streaming GEMM over row blocks, with the segment
-    table shifted to its columns.  (300, 32808, 1040) also has ragged rows and a
-    k tail (K % 128 == 16)."""
+    workgroups (2 x 128 and 3 x 256 tiles): the ragged last column then runs as
+    the weight-streaming GEMM over row blocks, with the segment table shifted to
+    its columns -- as extra workgroups of the MFMA launch at (520, 65584, 512), as
+    a second launch at (300, 32808, 1040), which also has ragged rows and a k
+    tail (K % 128 == 16).  The GDN in-projection test covers the merged form with
+    four strips per workgroup."""
     assert nv.nvfp4_gemm_form(M, K, N) == 1
     rng = np.random.default_rng(M + N + K)
     segs = [(0, 1000), (1000, N - 20), (N - 20, N)]
@@ -325,11 +327,13 @@ def test_quantizer_down_proj_activations_full_size(calibrated):
 
 @pytest.mark.parametrize("M,N,K", [(24, 700, 1040), (32, 200, 5120), (100, 1500, 2064), (70, 100, 1040),
                                    (300, 2000, 512), (24, 5120, 10256), (100, 1500, 11664), (70, 100, 6144),
-                                   (128, 5120, 17408), (40, 12300, 10256)])
+                                   (128, 5120, 17408), (40, 12300, 10256), (2100, 64, 1040), (2100, 60, 10256)])
 def test_gemm_row_blocks_bit_identical_to_16_rows(M, N, K):
     """nvfp4_gemm's weight-streaming form for M > 16 (32-row passes: (24, 700),
     (32, 200), (24, 5120); 64-row: (100, 1500), (300, 2000), (128, 5120); 16-row
-    passes for outputs of at most 8 strips: (70, 100)) gives, for every 16-row
+    passes for outputs of at most 8 strips: (70, 100), and with all four strips
+    in one workgroup over 132 row blocks: (2100, 64), (2100, 60), the latter in
+    the sixteen-wave order with a ragged last strip) gives, for every 16-row
     slice of the quantized activations, exactly the M <= 16 kernel's result on
     that slice, and the oracle's within tolerance.  For K > 5120 with fewer M <= 16
     workgroups than CUs the M <= 16 kernel splits the k tiles over sixteen waves,

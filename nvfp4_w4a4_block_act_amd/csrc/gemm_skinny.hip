@@ -284,6 +284,15 @@ __global__ __launch_bounds__(64 * NW) void linear_decode_kernel(
   constexpr int kQ = (kSlots + 63) / 64;
   static_assert(U >= 2, "two weight batches in flight");
   static_assert(kQ <= 32, "one bit of `live` per encode step");
+  // PSC: the wave's S x U weight scale chunks (128 bytes each) are fetched by two
+  // 16-byte loads per lane at kernel start (eight chunks per load) and handed to
+  // the MFMA lanes through a wave-private LDS area, instead of one 2-byte load
+  // per lane, strip and tile in each batch.  Measured at K = 5120, N = 12288
+  // (three alternating runs on one box, us per launch): M = 1 8.27 -> 7.95,
+  // M = 4 8.61 -> 8.54, M = 16 12.79 -> 12.89, so the 8- and 16-row instances
+  // keep the per-batch loads.
+  constexpr bool PSC = S * U <= 16 && NW == 8 && MAXM <= 4;
+  __shared__ __align__(16) uint8_t lwsc[NW][PSC ? 16 : 1][kChunkScales];
   __shared__ float red[NW][S][4][64];
   // wave-private activation tiles, row-major over (row, tile): slot group
   // v = row * U + u holds the 8 blocks of row `row` in the wave's tile u
@@ -327,12 +336,23 @@ __global__ __launch_bounds__(64 * NW) void linear_decode_kernel(
   strip_pointers<S>(w_codes, w_scales, strip0, nstrips, tiles, lane, wc, ws);
   uint4 wv[U][S];
   uint32_t wsc[U][S];
+  uint4 scp[2];                                      // PSC: chunk c = s U + u of the wave (c = 8 j + lane / 8)
+  if constexpr (PSC) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int c = min(8 * j + (lane >> 3), S * U - 1);
+      const int sc = c / U, u = c - sc * U;
+      const int64_t strip = min(strip0 + sc, nstrips - 1);
+      const int t = min(wave + NW * u, tiles - 1);
+      scp[j] = ld_stream16(w_scales + (strip * tiles + t) * kChunkScales + (lane & 7) * 16);
+    }
+  }
   auto request = [&](int u) {
     const int t = min(wave + NW * u, tiles - 1);
 #pragma unroll
     for (int s = 0; s < S; ++s) {
       wv[u][s] = ld_stream16(wc[s] + (int64_t)t * kChunkCodes);
-      wsc[u][s] = ld_stream2(ws[s] + (int64_t)t * kChunkScales);
+      if constexpr (!PSC) wsc[u][s] = ld_stream2(ws[s] + (int64_t)t * kChunkScales);
     }
   };
   request(0);
@@ -390,6 +410,11 @@ __global__ __launch_bounds__(64 * NW) void linear_decode_kernel(
     }
     if (q == 0) request(1);
   }
+  if constexpr (PSC) {                               // lane l of load j held bytes 16 l of chunks 8 j ..
+    uint4* const dst = reinterpret_cast<uint4*>(&lwsc[wave][0][0]);
+    dst[lane] = scp[0];
+    dst[64 + lane] = scp[1];
+  }
   if constexpr (BAL) set_issue_priority(3);
   // the lanes of this wave read each other's LDS writes
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -416,7 +441,9 @@ __global__ __launch_bounds__(64 * NW) void linear_decode_kernel(
       half8_t A[4];
       decode_a(cv, sc, 0xFFFFu, A);
 #pragma unroll
-      for (int s = 0; s < S; ++s) tile_mfma(A, wv[u][s], wsc[u][s], acc[s]);
+      for (int s = 0; s < S; ++s)
+        tile_mfma(A, wv[u][s], PSC ? (uint32_t)*reinterpret_cast<const uint16_t*>(&lwsc[wave][s * U + u][2 * lane])
+                                   : wsc[u][s], acc[s]);
     } else if (wave + NW * u < tiles) {              // uniform: tiles past the end only complete their loads
       const int t = wave + NW * u;
       const int k0 = t * kTileK + 32 * g;
@@ -428,7 +455,9 @@ __global__ __launch_bounds__(64 * NW) void linear_decode_kernel(
       half8_t A[4];
       decode_a(cv, sc, 0xFFFFu, A);
 #pragma unroll
-      for (int s = 0; s < S; ++s) tile_mfma(A, wv[u][s], wsc[u][s], acc[s]);
+      for (int s = 0; s < S; ++s)
+        tile_mfma(A, wv[u][s], PSC ? (uint32_t)*reinterpret_cast<const uint16_t*>(&lwsc[wave][s * U + u][2 * lane])
+                                   : wsc[u][s], acc[s]);
     }
     __builtin_amdgcn_sched_barrier(0);
     if (u + 2 < U) request(u + 2);             // two batches in flight

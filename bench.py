@@ -459,7 +459,7 @@ def gpu_state():
 
 # ---------------------------------------------------------------------------------------
 DECODE_COUNTERS = "linear_decode_kernel_decode_k5120_n12288_counters.md"
-DECODE_SOURCES = ("gemm_skinny.hip", "quant_device.hpp", "common.hpp", "launch.hpp")
+DECODE_SOURCES = ("gemm_skinny.hip", "rows_body.hpp", "quant_device.hpp", "common.hpp", "launch.hpp")
 QUANT_COUNTERS = "quantize_act_kernel_down_proj_activation_m32768_k17408.md"
 QUANT_SOURCES = ("quantize.hip", "quant_device.hpp", "common.hpp", "launch.hpp")
 

@@ -120,36 +120,12 @@ inline bool mfma_narrow(int64_t M, int64_t N) { return mfma_cost(M, N, true) < m
 
 // Rows per weight pass of the row-blocked weight-streaming GEMM: 16 for outputs
 // of at most 8 strips (there the activation work dominates: the 64 ragged
-// columns of the GDN in-projection took 12.9 us in 16-row passes with 2 strips
-// per workgroup and 15.3 us in 64-row passes with 1; 16-row passes with all 4
-// strips in one workgroup are faster still), else 32 up to 32 rows and 64
-// beyond.
+// columns of the GDN in-projection take 12.9 us in 16-row passes with 2 strips
+// per workgroup and 15.3 us in 64-row passes with 1), else 32 up to 32 rows and
+// 64 beyond.
 inline int rows_per_pass(int64_t M, int64_t N) {
   if ((N + kStrip - 1) / kStrip <= 8) return 16;
   return M <= 32 ? 32 : 64;
-}
-
-// Strips per workgroup of gemm_rows_kernel: every workgroup decodes its S weight
-// fragments and its MT activation tiles per k tile, so the busiest CU's work is
-// ceil(workgroups / 256) * (S + MT); the fewest, ties to larger S (fewer
-// activation re-decodes).  E.g. N = 34816, M = 128: S = 3 (1452 workgroups).
-// 16-row passes (MT = 1) may take four strips: the 64 ragged columns of the GDN
-// in-projection (M = 4096) then run as 256 workgroups that each decode their
-// activation rows once, 1.6 us faster than 512 workgroups of two strips (four
-// alternating runs on one box, bit-identical).
-inline int pick_strips_rows(int nstrips, int64_t blocks, int mt) {
-  const int smax = mt == 1 ? 4 : 3;
-  int best = smax;
-  int64_t cost = 0;
-  for (int s = smax; s >= 1; --s) {
-    const int64_t wgs = (int64_t)(nstrips + s - 1) / s * blocks;
-    const int64_t c = (wgs + kCUs - 1) / kCUs * (s + mt);
-    if (s == smax || c < cost) {
-      best = s;
-      cost = c;
-    }
-  }
-  return best;
 }
 
 // Segment table passed by value to the GEMM kernels: column -> module index.

@@ -129,6 +129,30 @@ __device__ __forceinline__ void reduce_rows_set(const float4_t (&acc)[S][MT], fl
   }
 }
 
+// Strips per workgroup of gemm_rows_kernel: every workgroup decodes its S weight
+// fragments and its MT activation tiles per k tile, so the busiest CU's work is
+// ceil(workgroups / 256) * (S + MT); the fewest, ties to larger S (fewer
+// activation re-decodes).  E.g. N = 34816, M = 128: S = 3 (1452 workgroups).
+// 16-row passes (MT = 1, outputs of at most 8 strips: rows_per_pass) may take
+// four strips: the 64 ragged columns of the GDN in-projection (M = 4096) then
+// run as 256 workgroups that each decode their activation rows once, 1.6 us
+// faster than 512 workgroups of two strips (four alternating runs on one box,
+// bit-identical).  Host code, used by the launchers of both GEMM sources.
+inline int pick_strips_rows(int nstrips, int64_t blocks, int mt) {
+  const int smax = mt == 1 ? 4 : 3;
+  int best = smax;
+  int64_t cost = 0;
+  for (int s = smax; s >= 1; --s) {
+    const int64_t wgs = (int64_t)(nstrips + s - 1) / s * blocks;
+    const int64_t c = (wgs + kCUs - 1) / kCUs * (s + mt);
+    if (s == smax || c < cost) {
+      best = s;
+      cost = c;
+    }
+  }
+  return best;
+}
+
 // The workgroup body of gemm_rows_kernel for workgroup index `bid`: a kernel of
 // its own (gemm_skinny.hip) or the extra workgroups of an MFMA GEMM launch that
 // take its ragged last tile column (gemm_mfma.hip).  64 NW threads.

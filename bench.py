@@ -67,6 +67,9 @@ def main():
         print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(how the layer would shard is a design, not code); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
+    if args.steps < 1 or args.warmup < 0:
+        print("bench.py needs --steps >= 1 and --warmup >= 0", file=sys.stderr)
+        sys.exit(2)
     import torch
     import nvfp4_w4a4_block_act_amd as nv
     import workloads as W
@@ -506,8 +509,9 @@ def bench_decode(args, torch, nv, W, dev, d16=None):
     if args.no_graph:
         sec, wall = time_region(torch, step_eager, args.steps, args.warmup)
     else:
-        # one graph per weight copy (a single step) and one graph of all copies in
-        # order (nc consecutive steps), so the host submits one replay per nc steps
+        # one graph of exactly the timed steps and one of the warmup steps (weight
+        # copies in rotation), so the timed region is a single replay: the host's
+        # submission of separate replays does not show up as idle GPU time
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
@@ -515,26 +519,19 @@ def bench_decode(args, torch, nv, W, dev, d16=None):
                 step_eager(r)
         torch.cuda.current_stream().wait_stream(side)
         torch.cuda.synchronize()
-        long_graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(long_graph):
-            for r in range(nc):
-                step_eager(r)
-        singles = []
-        for r in range(nc):
+
+        def capture(n):
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
-                step_eager(r)
-            singles.append(g)
+                for r in range(n):
+                    step_eager(r)
+            return g
+
+        timed_graph = capture(args.steps)
+        warm_graph = capture(args.warmup) if args.warmup > 0 else None
         torch.cuda.synchronize()
-
-        def run_steps(n):
-            for _ in range(n // nc):
-                long_graph.replay()
-            for r in range(n % nc):
-                singles[r].replay()
-
-        sec, wall = time_region(torch, lambda i: run_steps(args.steps) if i == 0 else run_steps(args.warmup),
-                                1, 1)
+        sec, wall = time_region(torch, lambda i: (timed_graph if i == 0 else warm_graph).replay(), 1,
+                                1 if warm_graph is not None else 0)
     # algorithmic bytes of one step: packed weight + bf16 activations + fp32 outputs, per call
     wbytes = pw0.nbytes()
     step_bytes = sum(wbytes + 2 * M * K + 4 * M * N for M in Ms)
@@ -610,7 +607,7 @@ def bench_decode(args, torch, nv, W, dev, d16=None):
     if headline and not args.no_prefill:
         del copies, pw0, xs, acts, outs, ws
         if not args.no_graph:
-            del long_graph, singles
+            del timed_graph, warm_graph
         torch.cuda.synchronize()
         torch.cuda.empty_cache()
         res["config"]["prefill"] = prefill_legs(args, torch, nv, W, dev)

@@ -255,7 +255,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_rows_kernel(
 // another wave's encode, so its weight decode and MFMAs overlap the rest of the
 // weight stream.  Every workgroup encodes the tensor's blocks (redundantly;
 // the bf16 input is L2-resident after the first reads) and workgroup 0 also
-// writes the canonical codes, scales and g_dec.  Steps:
+// writes g_dec and, after its outputs, the canonical codes and scales.  Steps:
 //  1. each lane loads its bf16 blocks: slot i = lane + 64 q is row i / (8 U),
 //     tile u = (i / 8) % U, block j = i % 8 of that tile, i.e. block column
 //     (w + NW u) * 8 + j; groups of eight lanes read 256 contiguous bytes;
@@ -387,9 +387,9 @@ __global__ __launch_bounds__(64 * NW) void linear_decode_kernel(
   const bool writer = blockIdx.x == 0;
   if (writer && tid == 0) *a_g = g_dec;
 
-  // 4. encode this wave's blocks into its LDS area (workgroup 0 also writes the
-  //    canonical codes and scales); the second weight batch goes out after the
-  //    first encode step
+  // 4. encode this wave's blocks into its LDS area (workgroup 0 stores them as
+  //    the canonical codes and scales at the end); the second weight batch goes
+  //    out after the first encode step
   uint8_t* const lc = &lcodes[wave][lane >> 3][(lane & 7) * 8];   // slot group (lane >> 3) + 8 q
   uint8_t* const ls = &lscales[wave][lane >> 3][lane & 7];
 #pragma unroll
@@ -400,12 +400,6 @@ __global__ __launch_bounds__(64 * NW) void linear_decode_kernel(
         const uint32_t sc = encode_bf16_block_max(xv[q][0], xv[q][1], bm[q], cx, cd);
         *reinterpret_cast<uint2*>(lc + q * 8 * kDecRowBytes) = cd;
         ls[q * 8 * (kTileK / kBlock)] = (uint8_t)sc;
-        if (writer) {
-          const int i = lane + 64 * q;
-          const int row = i / (8 * U), c = (wave + NW * ((i >> 3) % U)) * 8 + (i & 7);
-          *reinterpret_cast<uint2*>(a_codes + (int64_t)row * (K / 2) + c * 8) = cd;
-          a_scales[(int64_t)row * nb + c] = (uint8_t)sc;
-        }
       }
     }
     if (q == 0) request(1);
@@ -466,6 +460,22 @@ __global__ __launch_bounds__(64 * NW) void linear_decode_kernel(
   }
   if constexpr (BAL) __builtin_amdgcn_s_setprio(0);
   reduce_store<S, NW>(acc, red, scol, wgv, strip0, M, N, st, g_dec, out, ldo);
+  // workgroup 0 stores the canonical codes and scales last, from each lane's own
+  // slots in its wave's LDS area: a store counts against the same in-order
+  // counter as the weight loads, so stores issued during the encode would make
+  // the weight batches behind them wait for their round trips
+  if (writer) {
+#pragma unroll
+    for (int q = 0; q < kQ; ++q) {
+      if (64 * q < nslot && ((live >> q) & 1u)) {
+        const int i = lane + 64 * q;
+        const int row = i / (8 * U), c = (wave + NW * ((i >> 3) % U)) * 8 + (i & 7);
+        *reinterpret_cast<uint2*>(a_codes + (int64_t)row * (K / 2) + c * 8) =
+            *reinterpret_cast<const uint2*>(lc + q * 8 * kDecRowBytes);
+        a_scales[(int64_t)row * nb + c] = ls[q * 8 * (kTileK / kBlock)];
+      }
+    }
+  }
 }
 
 __global__ void fill_zero_kernel(float* __restrict__ out, int M, int N, int64_t ldo) {

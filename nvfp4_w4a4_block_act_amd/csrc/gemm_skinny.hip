@@ -385,7 +385,6 @@ __global__ __launch_bounds__(64 * NW) void linear_decode_kernel(
   const EncCtx cx = make_ctx(amax, rtab);
   const float g_dec = amax / kGMax;
   const bool writer = blockIdx.x == 0;
-  if (writer && tid == 0) *a_g = g_dec;
 
   // 4. encode this wave's blocks into its LDS area (workgroup 0 stores them as
   //    the canonical codes and scales at the end); the second weight batch goes
@@ -460,11 +459,12 @@ __global__ __launch_bounds__(64 * NW) void linear_decode_kernel(
   }
   if constexpr (BAL) __builtin_amdgcn_s_setprio(0);
   reduce_store<S, NW>(acc, red, scol, wgv, strip0, M, N, st, g_dec, out, ldo);
-  // workgroup 0 stores the canonical codes and scales last, from each lane's own
-  // slots in its wave's LDS area: a store counts against the same in-order
-  // counter as the weight loads, so stores issued during the encode would make
-  // the weight batches behind them wait for their round trips
+  // workgroup 0 stores g_dec and the canonical codes and scales last, the codes
+  // from each lane's own slots in its wave's LDS area: a store counts against
+  // the same in-order counter as the weight loads, so stores issued during the
+  // encode would make the weight batches behind them wait for their round trips
   if (writer) {
+    if (tid == 0) *a_g = g_dec;
 #pragma unroll
     for (int q = 0; q < kQ; ++q) {
       if (64 * q < nslot && ((live >> q) & 1u)) {

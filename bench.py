@@ -45,7 +45,8 @@ def parse():
     ap.add_argument("--config", default="decode",
                     choices=["decode", "decode_down_proj", "prefill_gate_up", "gdn_in_proj", "down_proj",
                              "down_proj_quantize", "tiny",
-                             "copy_calibration", "gdn_repair_compare", "gate_up_swiglu", "kv_fp8", "static_calibration"])
+                             "copy_calibration", "gdn_repair_compare", "gate_up_swiglu", "kv_fp8", "static_calibration",
+                             "read_probe"])
     ap.add_argument("--copies", type=int, default=16, help="device copies of the packed weight (decode)")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying HIP graphs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -83,6 +84,8 @@ def main():
         res = bench_decode(args, torch, nv, W, dev, W.decode_down_proj(M=16))
     elif args.config == "copy_calibration":
         res = bench_copy(args, torch, dev)
+    elif args.config == "read_probe":
+        res = bench_read_probe(args, torch, nv, dev)
     elif args.config == "gdn_repair_compare":
         res = bench_repair(args, torch, nv, W, dev)
     elif args.config == "gate_up_swiglu":
@@ -145,6 +148,46 @@ def bench_copy(args, torch, dev):
             "ms_per_step": round(sec / args.steps * 1e3, 5), "higher_is_better": True, "scaling": "weak",
             "vs_baseline": None, "dtype": "u8", "data": "synthetic",
             "config": {"workload": "copy_512MiB", "bytes_read_per_launch": n, "bytes_written_per_launch": n}}
+
+
+def bench_read_probe(args, torch, nv, dev):
+    """The read rate of a bare stream (nvfp4_read_probe: non-temporal 16-byte loads,
+    one contiguous share per workgroup) for the sizes the HBM-bound kernels stream:
+    the decode GEMMs' packed weights (K = 5120, N = 12288 and K = 17408, N = 5120;
+    16 rotating copies, so no launch finds its bytes in the 256 MB last-level cache)
+    and the bf16 input of the 32768 x 17408 activation quantizer (larger than that
+    cache, one buffer), each over 256 / 512 / 1024 workgroups.  Per-launch time from
+    HIP event pairs around graphs of back-to-back launches on the launch stream."""
+    sizes = [("decode_weight_k5120_n12288", 12288 * 5120 * 9 // 16, 16),
+             ("decode_weight_k17408_n5120", 5120 * 17408 * 9 // 16, 16),
+             ("activation_bf16_m32768_k17408", 32768 * 17408 * 2, 1)]
+    grids = (256, 512, 1024)
+    sink = torch.zeros(max(grids), dtype=torch.int32, device=dev)
+    rows = []
+    for name, nbytes, copies in sizes:
+        bufs = [torch.randint(-2 ** 31, 2 ** 31 - 1, (nbytes // 4,), dtype=torch.int32, device=dev)
+                for _ in range(copies)]
+        per_graph = 16
+        for wg in grids:
+            g = torch.cuda.CUDAGraph()
+            torch.cuda.synchronize()
+            with torch.cuda.graph(g):
+                for r in range(per_graph):
+                    nv.nvfp4_read_probe(bufs[r % copies], nbytes, wg, sink)
+            mean, med, p10, p90 = kernel_time_pairs(torch, lambda i: g.replay(), max(8, args.steps // per_graph))
+            mean, med = mean / per_graph, med / per_graph
+            rows.append({"stream": name, "bytes": nbytes, "workgroups": wg, "mean_us": round(mean * 1e6, 3),
+                         "median_us": round(med * 1e6, 3), "GBps": round(nbytes / mean / 1e9, 1),
+                         "frac_of_hbm_peak": round(nbytes / mean / 1e9 / HBM_PEAK_GBS, 4)})
+            del g
+        del bufs
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+    head = rows[0]
+    return {"metric": "HBM read rate of a bare stream (read-rate probe), GB/s", "value": head["GBps"], "unit": "GB/s",
+            "n_gpus": 1, "steps": args.steps, "warmup": 0, "ms_per_step": round(head["mean_us"] / 1e3, 6),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "u8", "data": "synthetic",
+            "config": {"workload": "read_probe_decode_weight_k5120_n12288_256wg", "probes": rows}}
 
 
 def bench_repair(args, torch, nv, W, dev):

@@ -50,7 +50,8 @@ extern "C" {
 #endif
 
 /* 2: nvfp4_gemm_form may return 2 (the MFMA GEMM with 256 x 128 tiles). */
-#define NVFP4_ABI_VERSION 2
+/* 3: nvfp4_read_probe. */
+#define NVFP4_ABI_VERSION 3
 #define NVFP4_MAX_SEGMENTS 16
 
 typedef enum {
@@ -332,6 +333,21 @@ nvfp4_status nvfp4_kv_fp8_decode(const uint8_t* codes, int64_t n, const float* a
  * (NVFP4_ESHAPE otherwise); op outside 0..2 is NVFP4_EINVAL.
  * ------------------------------------------------------------------------- */
 nvfp4_status nvfp4_convert_sweep(int32_t op, uint32_t first_bits, int64_t n, uint8_t* out, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Diagnostic: the HBM read rate a stream of `bytes` reaches with the access
+ * pattern of the decode-form GEMMs' weight stream -- the ceiling those GEMMs
+ * are measured against.  `workgroups` workgroups of 512 lanes each read one
+ * contiguous share of buf with non-temporal 16-byte loads (four in flight per
+ * lane); workgroup b stores the XOR of every 32-bit word of its share to
+ * sink[b], so that nothing is skipped and tests can check the coverage.
+ *   buf   device, `bytes` bytes (a multiple of 16, below 2^40), read only.
+ *   sink  device, `workgroups` uint32 words (1 <= workgroups <= 65536),
+ *         disjoint from buf.
+ * Pointers 16-byte aligned.  Errors as for every call (nothing enqueued unless
+ * NVFP4_OK or NVFP4_EHIP).
+ * ------------------------------------------------------------------------- */
+nvfp4_status nvfp4_read_probe(const void* buf, int64_t bytes, int32_t workgroups, uint32_t* sink, void* stream);
 
 #ifdef __cplusplus
 }

@@ -97,6 +97,8 @@ def _lib():
         lib.nvfp4_swiglu.argtypes = [_vp, _i64, _i64, _i64, _vp, _i64, _vp]
         lib.nvfp4_convert_sweep.restype = ctypes.c_int
         lib.nvfp4_convert_sweep.argtypes = [ctypes.c_int32, ctypes.c_uint32, _i64, _vp, _vp]
+        lib.nvfp4_read_probe.restype = ctypes.c_int
+        lib.nvfp4_read_probe.argtypes = [_vp, _i64, ctypes.c_int32, _vp, _vp]
         _LIB = lib
     return _LIB
 
@@ -244,6 +246,11 @@ def nvfp4_swiglu(gu, M, I, ldgu, h, ldh, stream=None):
 def nvfp4_convert_sweep(op, first_bits, n, out, stream=None):
     _check(_lib().nvfp4_convert_sweep(int(op), int(first_bits), int(n), _ptr(out), _stream(stream)),
            "nvfp4_convert_sweep")
+
+
+def nvfp4_read_probe(buf, nbytes, workgroups, sink, stream=None):
+    _check(_lib().nvfp4_read_probe(_ptr(buf), int(nbytes), int(workgroups), _ptr(sink), _stream(stream)),
+           "nvfp4_read_probe")
 
 
 # ---- convenience layer: allocate with torch, call the C ABI --------------------------

@@ -16,7 +16,7 @@ CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libnvfp4_w4a4.so")
 ARCH = "gfx950"
 
-HIP_SOURCES = ["quantize.hip", "gemm_skinny.hip", "gemm_mfma.hip", "kv_fp8.hip"]
+HIP_SOURCES = ["quantize.hip", "gemm_skinny.hip", "gemm_mfma.hip", "kv_fp8.hip", "stream_probe.hip"]
 HOST_SOURCES = ["api.cpp", "dispatch.cpp"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function"]

@@ -169,6 +169,10 @@ nvfp4_status check_linear(const void* x, int64_t M, int64_t K, int64_t ldx, cons
 
 }  // namespace
 
+namespace nvfp4 {
+hipError_t launch_read_probe(const void* buf, int64_t bytes, int workgroups, uint32_t* sink, hipStream_t stream);
+}  // namespace nvfp4
+
 extern "C" {
 
 int nvfp4_abi_version(void) { return NVFP4_ABI_VERSION; }
@@ -461,6 +465,18 @@ nvfp4_status nvfp4_convert_sweep(int32_t op, uint32_t first_bits, int64_t n, uin
   if (!out) return NVFP4_EINVAL;
   if (!aligned16(out)) return NVFP4_EALIGN;
   return launched(nvfp4::launch_convert_sweep(op, first_bits, n, out, static_cast<hipStream_t>(stream)));
+}
+
+// ---- diagnostic: the read rate of a bare stream (stream_probe.hip)
+nvfp4_status nvfp4_read_probe(const void* buf, int64_t bytes, int32_t workgroups, uint32_t* sink, void* stream) {
+  if (bytes < 0 || workgroups < 1 || workgroups > 65536) return NVFP4_EINVAL;
+  if (bytes % 16 != 0 || bytes >= ((int64_t)1 << 40)) return NVFP4_ESHAPE;
+  if (!buf || !sink) return NVFP4_EINVAL;
+  if (!all_aligned({buf, sink})) return NVFP4_EALIGN;
+  const Buf outs[] = {{sink, (size_t)workgroups * 4}};
+  const Buf ins[] = {{buf, (size_t)bytes}};
+  if (!disjoint(outs, ins)) return NVFP4_EINVAL;
+  return launched(nvfp4::launch_read_probe(buf, bytes, workgroups, sink, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -68,4 +68,5 @@ hipError_t scratch_for_stream(hipStream_t, void** out) {
 }
 hipError_t launch_kv_fp8_encode(const uint16_t*, int64_t, const float*, uint8_t*, hipStream_t) { return record(); }
 hipError_t launch_kv_fp8_decode(const uint8_t*, int64_t, const float*, uint16_t*, hipStream_t) { return record(); }
+hipError_t launch_read_probe(const void*, int64_t, int, uint32_t*, hipStream_t) { return record(); }
 }  // namespace nvfp4

@@ -31,7 +31,7 @@ def test_version_and_status_strings():
     """The library reports the header's ABI version (the check build() makes)."""
     with open(os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "nvfp4.h")) as f:
         want = int(re.search(r"#define NVFP4_ABI_VERSION (\d+)", f.read()).group(1))
-    assert want == 2 and nv.nvfp4_abi_version() == want
+    assert want == 3 and nv.nvfp4_abi_version() == want
     for s in range(7):
         assert nv.nvfp4_status_str(s)
     assert nv.nvfp4_status_str(99) == "unknown status"
@@ -283,3 +283,19 @@ def test_gemm_form_query():
     assert nv.nvfp4_gemm_form(8192, 5120, 34816) == 1
     assert nv.nvfp4_gemm_form(4096, 5120, 12352) == 1
     assert nv.nvfp4_gemm_form(32768, 17408, 5120) == 1
+
+
+def test_read_probe_validation():
+    """The read-rate probe: size a multiple of 16 below 2^40, 1..65536 workgroups,
+    aligned and disjoint buffers; checked before any launch."""
+    f = nv.lib().nvfp4_read_probe
+    assert f(A, -16, 256, A + (2 << 20), None) == 1
+    assert f(A, 1 << 20, 0, A + (2 << 20), None) == 1
+    assert f(A, 1 << 20, 65537, A + (2 << 20), None) == 1
+    assert f(A, (1 << 20) + 8, 256, A + (2 << 20), None) == 2
+    assert f(A, 1 << 40, 256, A + (2 << 20), None) == 2
+    assert f(None, 1 << 20, 256, A + (2 << 20), None) == 1
+    assert f(A, 1 << 20, 256, None, None) == 1
+    assert f(A + 4, 1 << 20, 256, A + (2 << 20), None) == 3
+    assert f(A, 1 << 20, 256, A + (2 << 20) + 4, None) == 3
+    assert f(A, 1 << 20, 256, A + 64, None) == 1                   # sink inside the buffer

@@ -176,6 +176,31 @@ def test_gemm_ragged_column_split_along_k(M, N, K):
     check_linear(x, w, segs, f"ragged column split M={M} N={N} K={K}", rows, cols)
 
 
+@pytest.mark.parametrize("M,N,K", [(4096, 12304, 512), (4096, 12320, 512)])
+def test_gemm_ragged_columns_inside_the_mfma_launch(M, N, K):
+    """768 whole 256 x 256 tiles fill three rounds, so the 16 / 32 ragged columns run
+    as extra workgroups of the MFMA launch (the row-blocked body with one / two strips
+    per workgroup).  With the ragged columns as a module of their own, they equal the
+    GEMM of that module alone (which runs the same row-blocked body as its own launch)
+    bit for bit, and the oracle on sampled rows within tolerance."""
+    assert nv.nvfp4_gemm_form(M, K, N) == 1 and nv.nvfp4_gemm_form(M, K, N - 12288) == 0
+    rng = np.random.default_rng(N + K)
+    segs = [(0, 12288), (12288, N)]
+    w = np.concatenate([(0.02 * rng.standard_normal((12288, K))).astype(np.float32),
+                        (0.3 * rng.standard_normal((N - 12288, K))).astype(np.float32)])
+    x = W.random_act(M + N, M, K, "student_t")
+    say(f"[ragged in launch] M={M} N={N} K={K}")
+    c, s_, g = nv.quantize_act(to_dev_bf16(x))
+    out = nv.gemm(c, s_, g, gpu_pack(w, segs))
+    part = nv.gemm(c, s_, g, gpu_pack(np.ascontiguousarray(w[12288:]), [(0, N - 12288)]))
+    torch.cuda.synchronize()
+    assert torch.equal(out[:, 12288:], part)
+    rows = _sample(M, 16, rng, [0, M - 1])
+    cols = np.concatenate([np.arange(12288, N), _sample(12288, 40, rng, [0, 12287])])
+    ref, bnd = oracle_linear_rows(x, w, segs, rows, cols)
+    assert_within_tol(out.cpu().numpy().astype(np.float64)[rows][:, cols], ref, bnd, f"ragged in launch N={N}")
+
+
 @pytest.mark.parametrize("M,N,K", [(1536, 12300, 512), (512, 12288, 1040), (4096, 5120, 256), (4096, 5120, 48)])
 def test_gemm_narrow_mfma_tiles(M, N, K):
     """Shapes whose 256 x 256 tiles would leave a partial last round run the MFMA

@@ -106,13 +106,36 @@ __device__ __forceinline__ uint32_t chunk_absmax(const uint16_t* __restrict__ x,
   return m;
 }
 
+// The same over a contiguous tensor (ldx == K) seen as one flat run of chunks:
+// workgroup b takes the contiguous share [b * per, min((b + 1) * per, total)),
+// its lanes consecutive chunks, kAmaxLoads loads in flight per lane, with no
+// row / column arithmetic per chunk.
+template <bool ST>
+__device__ __forceinline__ uint32_t flat_absmax(const uint16_t* __restrict__ x, int64_t total) {
+  const int64_t per = (total + gridDim.x - 1) / gridDim.x;
+  const int64_t lo = (int64_t)blockIdx.x * per, hi = min(lo + per, total);
+  const uint4* p = reinterpret_cast<const uint4*>(x);
+  uint32_t m = 0;
+  int64_t c = lo + threadIdx.x;
+  for (; c + (kAmaxLoads - 1) * kQThreads < hi; c += kAmaxLoads * kQThreads) {
+    uint4 v[kAmaxLoads];
+#pragma unroll
+    for (int u = 0; u < kAmaxLoads; ++u) v[u] = ST ? ld_stream16(p + c + u * kQThreads) : p[c + u * kQThreads];
+#pragma unroll
+    for (int u = 0; u < kAmaxLoads; ++u) m = absmax_bits(v[u], m);
+  }
+  for (; c < hi; c += kQThreads) m = absmax_bits(ST ? ld_stream16(p + c) : p[c], m);
+  return m;
+}
+
 template <bool ST>
 __global__ __launch_bounds__(kQThreads) void amax_partial_kernel(const uint16_t* __restrict__ x, int64_t M,
                                                                  int K, int64_t ldx,
                                                                  uint32_t* __restrict__ partial) {
   __shared__ uint32_t red[kQThreads / 64];
-  const uint32_t m = chunk_absmax<ST>(x, ldx, K, M, (int64_t)blockIdx.x * blockDim.x + threadIdx.x,
-                                      (int64_t)gridDim.x * blockDim.x);
+  const uint32_t m = (ldx == K) ? flat_absmax<ST>(x, M * (K / 8))   // uniform
+                                : chunk_absmax<ST>(x, ldx, K, M, (int64_t)blockIdx.x * blockDim.x + threadIdx.x,
+                                                   (int64_t)gridDim.x * blockDim.x);
   const uint32_t r = block_reduce_max(m, red);
   if (threadIdx.x == 0) partial[blockIdx.x] = r;
 }

@@ -56,14 +56,10 @@ constexpr int64_t kStreamBytes = int64_t(256) << 20;
 
 typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 
-// Encode the bf16 block (m, b) of x.
+// Encode the bf16 block at p into its 8 code bytes at cdst and its scale byte at sdst.
 template <bool ST>
-__device__ __forceinline__ void encode_block_at(const uint16_t* __restrict__ x, int64_t ldx, int K, int64_t m,
-                                                int b, const EncCtx& cx, uint8_t* __restrict__ codes,
-                                                uint8_t* __restrict__ scales) {
-  const uint16_t* p = x + m * ldx + (int64_t)b * kBlock;
-  uint8_t* cdst = codes + m * (K / 2) + (int64_t)b * 8;
-  uint8_t* sdst = scales + m * (K / kBlock) + b;
+__device__ __forceinline__ void encode_block_to(const uint16_t* __restrict__ p, uint8_t* __restrict__ cdst,
+                                                uint8_t* __restrict__ sdst, const EncCtx& cx) {
   if constexpr (ST) {
     uint2 c;
     const uint32_t sc = encode_bf16_block(ld_stream16(p), ld_stream16(p + 8), cx, c);
@@ -76,6 +72,15 @@ __device__ __forceinline__ void encode_block_at(const uint16_t* __restrict__ x, 
     const uint4* q = reinterpret_cast<const uint4*>(p);
     encode_bf16_chunks(q[0], q[1], cx, cdst, sdst);
   }
+}
+
+// Encode the bf16 block (m, b) of x.
+template <bool ST>
+__device__ __forceinline__ void encode_block_at(const uint16_t* __restrict__ x, int64_t ldx, int K, int64_t m,
+                                                int b, const EncCtx& cx, uint8_t* __restrict__ codes,
+                                                uint8_t* __restrict__ scales) {
+  encode_block_to<ST>(x + m * ldx + (int64_t)b * kBlock, codes + m * (K / 2) + (int64_t)b * 8,
+                      scales + m * (K / kBlock) + b, cx);
 }
 
 // ---- whole-tensor |x| maximum on bf16 bit patterns ------------------------------
@@ -175,11 +180,17 @@ __global__ __launch_bounds__(kQThreads) void quantize_act_kernel(
 
   const int nb = K / kBlock;
   const int64_t total = M * nb;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
-       i += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t m = i / nb;
-    const int b = (int)(i - m * nb);
-    encode_block_at<ST>(x, ldx, K, m, b, cx, codes, scales);
+  const int64_t first = (int64_t)blockIdx.x * blockDim.x + threadIdx.x, stride = (int64_t)gridDim.x * blockDim.x;
+  if (ldx == K) {
+    // contiguous: block i of the flat tensor is row i / nb, block i % nb, and its
+    // codes and scales sit at i * 8 and i in the canonical layout
+    for (int64_t i = first; i < total; i += stride) encode_block_to<ST>(x + i * kBlock, codes + i * 8, scales + i, cx);
+  } else {
+    for (int64_t i = first; i < total; i += stride) {
+      const int64_t m = i / nb;
+      const int b = (int)(i - m * nb);
+      encode_block_at<ST>(x, ldx, K, m, b, cx, codes, scales);
+    }
   }
 }
 

@@ -508,6 +508,11 @@ DECODE_COUNTERS = "linear_decode_kernel_decode_k5120_n12288_counters.md"
 DECODE_SOURCES = ("gemm_skinny.hip", "rows_body.hpp", "quant_device.hpp", "common.hpp", "launch.hpp")
 QUANT_COUNTERS = "quantize_act_kernel_down_proj_activation_m32768_k17408.md"
 QUANT_SOURCES = ("quantize.hip", "quant_device.hpp", "common.hpp", "launch.hpp")
+# the MFMA GEMM's counter summaries (FETCH_SIZE / WRITE_SIZE per launch), by prefill workload
+MFMA_COUNTERS = {"prefill_gate_up": "gemm_mfma_kernel_prefill_gate_up_m8192_k5120_n34816.md",
+                 "gdn_in_proj": "gemm_mfma_kernel_gdn_in_proj_m4096_k5120_n12352.md",
+                 "down_proj": "gemm_mfma_kernel_down_proj_m32768_k17408_n5120.md"}
+MFMA_SOURCES = ("gemm_mfma.hip", "rows_body.hpp", "quant_device.hpp", "common.hpp", "launch.hpp")
 
 
 def one_launch_rows(K):
@@ -726,10 +731,13 @@ GEMM_CONFIGS = {
 GEMM_METRIC = "NVFP4 W4A4 prefill GEMM TFLOP/s (quantize + GEMM + epilogue), % of MI355X fp16 MFMA roofline"
 
 
-def gemm_leg(args, torch, nv, dev, d, steps, warmup, cpu_seconds, x=None):
+def gemm_leg(args, torch, nv, dev, d, steps, warmup, cpu_seconds, x=None, counters=None):
     """One prefill workload: quantize (dynamic scale) + GEMM + per-module epilogue per
     step, timed over `steps` steps; the GEMM call alone timed with an event pair around
-    each launch on its stream.  TFLOP/s counts 2 M N K."""
+    each launch on its stream.  TFLOP/s counts 2 M N K.  `traffic` is the GEMM launch's
+    HBM bytes from the counter summary `counters` in profiles/ (null when absent or
+    taken on other sources); its algorithmic bytes are the activation and weight codes
+    and scales read once and the fp32 output written once."""
     M, K, N = d.M, d.K, d.N
     pw = nv.pack_weight(torch.from_numpy(d.w).to(dev), d.segments)
     if x is None:
@@ -757,7 +765,10 @@ def gemm_leg(args, torch, nv, dev, d, steps, warmup, cpu_seconds, x=None):
            "gemm_kernel_p10_ms": round(p10 * 1e3, 4), "gemm_kernel_p90_ms": round(p90 * 1e3, 4),
            "gpu_state_after_run": gpu_state(),
            "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": F16_MFMA_PEAK_TFLOPS,
-                        "unit": "TFLOP/s", "frac": round(achieved / F16_MFMA_PEAK_TFLOPS, 4), "traffic": None,
+                        "unit": "TFLOP/s", "frac": round(achieved / F16_MFMA_PEAK_TFLOPS, 4),
+                        "traffic": measured_traffic(counters, MFMA_SOURCES) if counters else None,
+                        "traffic_unit": "HBM bytes per GEMM launch",
+                        "algorithmic_bytes_per_launch": (M + N) * K * 9 // 16 + 4 * M * N,
                         "kernel": "gemm_mfma_kernel" if nv.nvfp4_gemm_form(M, K, N) >= 1 else "gemm_rows_kernel"}}
     if cpu_seconds > 0:
         leg["cpu_baseline"] = cpu_baseline_gemm(d, cpu_seconds, flops)
@@ -769,7 +780,7 @@ def bench_gemm(args, torch, nv, W, dev):
     d = GEMM_CONFIGS[args.config](W)
     steps = max(1, args.steps)
     leg = gemm_leg(args, torch, nv, dev, d, steps, min(args.warmup, 5),
-                   0 if args.no_cpu_baseline else args.cpu_seconds)
+                   0 if args.no_cpu_baseline else args.cpu_seconds, counters=MFMA_COUNTERS.get(args.config))
     res = {"metric": GEMM_METRIC, "value": leg["step_TFLOPs"], "unit": "TFLOP/s", "n_gpus": 1, "steps": steps,
            "warmup": min(args.warmup, 5), "ms_per_step": leg["step_ms"], "higher_is_better": True,
            "scaling": "weak", "vs_baseline": None, "dtype": "f16",
@@ -895,7 +906,8 @@ def prefill_legs(args, torch, nv, W, dev):
         print(f"[bench] prefill leg {name}", file=sys.stderr, flush=True)
         d = GEMM_CONFIGS[name](W)
         x = to_dev_bf16(torch, d.x_bits, dev)
-        legs[name] = gemm_leg(args, torch, nv, dev, d, args.prefill_steps, 3, cpu_s, x=x)
+        legs[name] = gemm_leg(args, torch, nv, dev, d, args.prefill_steps, 3, cpu_s, x=x,
+                              counters=MFMA_COUNTERS[name])
         if name == "down_proj":
             print("[bench] prefill leg down_proj_quantize", file=sys.stderr, flush=True)
             legs["down_proj_quantize"] = quantize_leg(args, torch, nv, dev, x, d.x_bits, args.prefill_steps, cpu_s)
